@@ -1,0 +1,527 @@
+// C ABI of the indexer library: argument checks, workspace layout, and the
+// four pipelines (route; MISA score + top-k; MISA-dagger; HISA), each a short
+// sequence of asynchronous launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/misa.h"
+#include "launch.h"
+
+namespace misa {
+
+// ---------------------------------------------------------------- errors
+
+static thread_local std::string g_last_error;
+
+static misa_status fail(misa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+static misa_status hip_fail(hipError_t e, const char* where) {
+  return fail(MISA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- profiling
+
+struct ProfRec {
+  std::string name;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+static std::mutex g_prof_mu;
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof;
+
+void prof_begin(const char* name, hipStream_t stream) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r;
+  r.name = name;
+  if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
+  (void)hipEventRecord(r.start, stream);
+  g_prof.push_back(r);
+}
+
+void prof_end(hipStream_t stream) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof.empty()) (void)hipEventRecord(g_prof.back().stop, stream);
+}
+
+// ---------------------------------------------------------------- workspace
+
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~size_t(255);
+    return at;
+  }
+};
+
+struct Plan {
+  size_t ksum = 0, tsum = 0, pmax = 0, heads = 0, beta = 0;
+  size_t S = 0;
+  size_t ghist = 0, rkeys = 0, ridx = 0, rcnt = 0, gkeys = 0, gidx = 0;
+  size_t cand = 0, ncand = 0, S2 = 0, blocks = 0, nblocks = 0;
+  long long cand_ld = 0;
+  int Mmax = 0, mm = 0;
+  size_t total = 0;
+};
+
+static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Long-row selection scratch for `rows` rows of up to `max_n` items.
+static void plan_long(Bump& bp, Plan& pl, int rows, int max_n) {
+  if (max_n <= topk_lds_cap()) return;
+  const size_t nch = (size_t)topk_long_chunks(max_n);
+  const size_t rld = nch * (size_t)topk_long_chunk();
+  const size_t need_hist = (size_t)rows * topk_coarse_bins() * 4;
+  // one set of scratch serves every selection of a call (they run in order)
+  pl.ghist = bp.take(need_hist);
+  pl.rkeys = bp.take((size_t)rows * rld * 4);
+  pl.ridx = bp.take((size_t)rows * rld * 4);
+  pl.rcnt = bp.take((size_t)rows * nch * 4);
+  pl.gkeys = bp.take((size_t)rows * rld * 4);
+  pl.gidx = bp.take((size_t)rows * rld * 4);
+}
+
+static void plan_route(Bump& bp, Plan& pl, const misa_problem* p) {
+  const int M = ceil_div(p->L, p->B);
+  pl.ksum = bp.take((size_t)M * 128 * 8);
+  pl.tsum = bp.take((size_t)p->T * 128 * 8);
+  pl.pmax = bp.take((size_t)p->T * route_chunks(p->L, p->B) * 64 * 8);
+}
+
+static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, int m) {
+  Bump bp;
+  Plan pl;
+  const int T = p->T, L = p->L;
+  bp.take(256);  // keep offset 0 unused so 0 can mean "absent"
+  switch (op) {
+    case MISA_OP_BLOCK_MEANS:
+      pl.ksum = bp.take((size_t)ceil_div(L, p->B) * 128 * 8);
+      break;
+    case MISA_OP_ROUTE:
+      plan_route(bp, pl, p);
+      break;
+    case MISA_OP_SCORE_TOPK:
+      plan_route(bp, pl, p);
+      pl.heads = bp.take((size_t)T * A * 4);
+      pl.S = bp.take((size_t)T * L * 4);
+      plan_long(bp, pl, T, L);
+      break;
+    case MISA_OP_HIER_TOPK: {
+      plan_route(bp, pl, p);
+      pl.heads = bp.take((size_t)T * A * 4);
+      pl.S = bp.take((size_t)T * L * 4);
+      pl.cand_ld = kprime < L ? kprime : L;
+      pl.cand = bp.take((size_t)T * pl.cand_ld * 4);
+      pl.ncand = bp.take((size_t)T * 4);
+      pl.S2 = bp.take((size_t)T * pl.cand_ld * 4);
+      plan_long(bp, pl, T, L);  // covers the k' stage and the final stage (cand_ld <= L)
+      break;
+    }
+    case MISA_OP_HISA_TOPK: {
+      plan_route(bp, pl, p);
+      pl.Mmax = ceil_div(L, p->B);
+      pl.mm = m < pl.Mmax ? m : pl.Mmax;
+      pl.beta = bp.take((size_t)T * pl.Mmax * 4);
+      pl.blocks = bp.take((size_t)T * pl.mm * 4);
+      pl.nblocks = bp.take((size_t)T * 4);
+      const long long mb = (long long)pl.mm * p->B;
+      pl.cand_ld = mb < L ? mb : L;
+      pl.cand = bp.take((size_t)T * pl.cand_ld * 4);
+      pl.ncand = bp.take((size_t)T * 4);
+      pl.S2 = bp.take((size_t)T * pl.cand_ld * 4);
+      const int mx = pl.Mmax > (int)pl.cand_ld ? pl.Mmax : (int)pl.cand_ld;
+      plan_long(bp, pl, T, mx);
+      break;
+    }
+    default:
+      break;
+  }
+  pl.total = bp.off;
+  return pl;
+}
+
+template <typename Tp>
+static Tp* at(void* ws, size_t off) {
+  return off ? reinterpret_cast<Tp*>(static_cast<char*>(ws) + off) : nullptr;
+}
+
+// ---------------------------------------------------------------- validation
+
+static bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+static misa_status check_problem(const misa_problem* p, bool need_queries) {
+  if (!p) return fail(MISA_ERR_INVALID_ARG, "problem is NULL");
+  if (p->T < 0) return fail(MISA_ERR_INVALID_ARG, "T = %d is negative", p->T);
+  if (p->d < 1 || p->H < 1) return fail(MISA_ERR_INVALID_ARG, "H = %d and d = %d must be >= 1", p->H, p->d);
+  if (p->L < 1) return fail(MISA_ERR_INVALID_ARG, "L = %d must be >= 1", p->L);
+  if (p->B < 1) return fail(MISA_ERR_INVALID_ARG, "B = %d must be >= 1", p->B);
+  if (p->k_dtype != MISA_K_BF16 && p->k_dtype != MISA_K_FP8_E4M3FN)
+    return fail(MISA_ERR_INVALID_ARG, "k_dtype = %d is not a misa_kdtype", p->k_dtype);
+  if (p->d != kHeadDimHost) return fail(MISA_ERR_UNSUPPORTED, "d = %d (only d = 128 is supported)", p->d);
+  if (p->H > 64) return fail(MISA_ERR_UNSUPPORTED, "H = %d (at most 64 heads are supported)", p->H);
+  if (p->L > (1 << 28)) return fail(MISA_ERR_UNSUPPORTED, "L = %d exceeds 2^28 keys", p->L);
+  if (p->T > (1 << 24)) return fail(MISA_ERR_UNSUPPORTED, "T = %d exceeds 2^24 queries", p->T);
+  if (!p->K) return fail(MISA_ERR_INVALID_ARG, "K is NULL");
+  if (!aligned(p->K, 16)) return fail(MISA_ERR_INVALID_ARG, "K must be 16-byte aligned");
+  const bool fp8 = p->k_dtype == MISA_K_FP8_E4M3FN;
+  if (fp8 && !p->k_scale) return fail(MISA_ERR_INVALID_ARG, "k_scale is required for fp8 keys");
+  if (!fp8 && p->k_scale) return fail(MISA_ERR_INVALID_ARG, "k_scale must be NULL for bf16 keys");
+  if (p->k_scale && !aligned(p->k_scale, 4)) return fail(MISA_ERR_INVALID_ARG, "k_scale must be 4-byte aligned");
+  if (need_queries && p->T > 0) {
+    if (!p->q || !p->w || !p->pos) return fail(MISA_ERR_INVALID_ARG, "q, w and pos must be non-NULL");
+    if (!aligned(p->q, 16)) return fail(MISA_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if (!aligned(p->w, 4) || !aligned(p->pos, 4)) return fail(MISA_ERR_INVALID_ARG, "w and pos must be 4-byte aligned");
+  }
+  return MISA_OK;
+}
+
+static misa_status check_ws(const Plan& pl, void* ws, size_t ws_bytes) {
+  if (ws_bytes < pl.total)
+    return fail(MISA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, pl.total);
+  if (!ws) return fail(MISA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(MISA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return MISA_OK;
+}
+
+static misa_status check_out(const void* ptr, const char* name) {
+  if (!ptr) return fail(MISA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(ptr, 4)) return fail(MISA_ERR_INVALID_ARG, "%s must be 4-byte aligned", name);
+  return MISA_OK;
+}
+
+#define MISA_TRY(expr)                   \
+  do {                                   \
+    misa_status _st = (expr);            \
+    if (_st != MISA_OK) return _st;      \
+  } while (0)
+
+#define HIP_TRY(expr, where)                     \
+  do {                                           \
+    hipError_t _e = (expr);                      \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// ---------------------------------------------------------------- pipelines
+
+static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws,
+                             int A, int32_t* heads, float* r, float* beta, int beta_ld) {
+  const bool fp8 = p->k_dtype == MISA_K_FP8_E4M3FN;
+  double* ksum = at<double>(ws, pl.ksum);
+  double* tsum = at<double>(ws, pl.tsum);
+  double* pmax = at<double>(ws, pl.pmax);
+  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr), "block sums");
+  HIP_TRY(launch_tail_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, p->T, p->pos, tsum), "tail sums");
+  HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, tsum, pmax, heads, r,
+                       beta, beta_ld),
+          "router");
+  return MISA_OK;
+}
+
+static TopkLongWs long_ws(const Plan& pl, void* ws) {
+  TopkLongWs lw;
+  lw.ghist = at<uint32_t>(ws, pl.ghist);
+  lw.rkeys = at<uint32_t>(ws, pl.rkeys);
+  lw.ridx = at<int32_t>(ws, pl.ridx);
+  lw.rcnt = at<int32_t>(ws, pl.rcnt);
+  lw.gkeys = at<uint32_t>(ws, pl.gkeys);
+  lw.gidx = at<int32_t>(ws, pl.gidx);
+  return lw;
+}
+
+static misa_status run_topk(const LaunchCtx& cx, const TopkArgs& a, const Plan& pl, void* ws, int max_n) {
+  if (max_n <= topk_lds_cap()) {
+    HIP_TRY(launch_topk_rows(cx, a, max_n), "top-k");
+  } else {
+    HIP_TRY(launch_topk_long(cx, a, long_ws(pl, ws), max_n), "top-k (long rows)");
+  }
+  return MISA_OK;
+}
+
+static ScoreArgs score_args(const misa_problem* p) {
+  ScoreArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = p->q;
+  a.w = p->w;
+  a.H = p->H;
+  a.T = p->T;
+  a.K = p->K;
+  a.kscale = p->k_scale;
+  a.L = p->L;
+  a.pos = p->pos;
+  return a;
+}
+
+static TopkArgs topk_args(const misa_problem* p) {
+  TopkArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.pos = p->pos;
+  a.L = p->L;
+  a.n_div = 1;
+  a.rows = p->T;
+  return a;
+}
+
+// Routed scores of every visible key into S[T, L].
+static misa_status run_routed_scores(const LaunchCtx& cx, const misa_problem* p, const Plan& pl,
+                                     void* ws, int A, const int32_t* heads_in) {
+  const int32_t* heads = heads_in;
+  if (!heads) {
+    int32_t* hw = at<int32_t>(ws, pl.heads);
+    if (A == p->H) {
+      heads = nullptr;  // dense: slot j is head j, no routing needed
+    } else {
+      MISA_TRY(run_route(cx, p, pl, ws, A, hw, nullptr, nullptr, 0));
+      heads = hw;
+    }
+  }
+  ScoreArgs sa = score_args(p);
+  sa.heads = heads;
+  sa.A = A;
+  sa.S = at<float>(ws, pl.S);
+  sa.S_ld = p->L;
+  HIP_TRY(launch_score_keys(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "routed scoring");
+  return MISA_OK;
+}
+
+}  // namespace misa
+
+using namespace misa;
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" {
+
+size_t misa_workspace_bytes(const misa_problem* p, int32_t op, int32_t A, int32_t kprime, int32_t k,
+                            int32_t m) {
+  if (check_problem(p, false) != MISA_OK) return 0;
+  switch (op) {
+    case MISA_OP_ROUTE:
+    case MISA_OP_SCORE_TOPK:
+      if (A < 1 || A > p->H) return 0;
+      if (op == MISA_OP_SCORE_TOPK && k < 1) return 0;
+      break;
+    case MISA_OP_HIER_TOPK:
+      if (A < 1 || A > p->H || k < 1 || kprime < k) return 0;
+      break;
+    case MISA_OP_HISA_TOPK:
+      if (m < 1 || k < 1) return 0;
+      break;
+    case MISA_OP_BLOCK_MEANS:
+      break;
+    default:
+      return 0;
+  }
+  return make_plan(p, op, A, kprime, k, m).total;
+}
+
+misa_status misa_block_means(const misa_problem* p, float* kbar, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, false));
+  MISA_TRY(check_out(kbar, "kbar"));
+  const Plan pl = make_plan(p, MISA_OP_BLOCK_MEANS, 1, 1, 1, 1);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, p->k_dtype == MISA_K_FP8_E4M3FN, p->L, p->B,
+                            at<double>(ws, pl.ksum), kbar),
+          "block means");
+  return MISA_OK;
+}
+
+misa_status misa_route(const misa_problem* p, int32_t A, int32_t* heads, float* r, void* ws,
+                       size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, true));
+  if (A < 1 || A > p->H) return fail(MISA_ERR_INVALID_ARG, "A = %d must lie in [1, H = %d]", A, p->H);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(heads, "heads"));
+  if (r && !aligned(r, 4)) return fail(MISA_ERR_INVALID_ARG, "r must be 4-byte aligned");
+  const Plan pl = make_plan(p, MISA_OP_ROUTE, A, 1, 1, 1);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  return run_route(cx, p, pl, ws, A, heads, r, nullptr, 0);
+}
+
+misa_status misa_score_topk(const misa_problem* p, int32_t A, const int32_t* heads, int32_t k,
+                            int32_t* idx, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, true));
+  if (A < 1 || A > p->H) return fail(MISA_ERR_INVALID_ARG, "A = %d must lie in [1, H = %d]", A, p->H);
+  if (k < 1) return fail(MISA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(idx, "idx"));
+  MISA_TRY(check_out(scores, "scores"));
+  if (heads && !aligned(heads, 4)) return fail(MISA_ERR_INVALID_ARG, "heads must be 4-byte aligned");
+  const Plan pl = make_plan(p, MISA_OP_SCORE_TOPK, A, 1, k, 1);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads));
+  TopkArgs ta = topk_args(p);
+  ta.S = at<float>(ws, pl.S);
+  ta.S_ld = p->L;
+  ta.k = k;
+  ta.out_idx = idx;
+  ta.out_score = scores;
+  ta.out_ld = k;
+  return run_topk(cx, ta, pl, ws, p->L);
+}
+
+misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* heads, int32_t kprime,
+                           int32_t k, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
+                           void* stream) {
+  MISA_TRY(check_problem(p, true));
+  if (A < 1 || A > p->H) return fail(MISA_ERR_INVALID_ARG, "A = %d must lie in [1, H = %d]", A, p->H);
+  if (k < 1) return fail(MISA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (kprime < k) return fail(MISA_ERR_INVALID_ARG, "kprime = %d must be >= k = %d", kprime, k);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(idx, "idx"));
+  MISA_TRY(check_out(scores, "scores"));
+  if (heads && !aligned(heads, 4)) return fail(MISA_ERR_INVALID_ARG, "heads must be 4-byte aligned");
+  const Plan pl = make_plan(p, MISA_OP_HIER_TOPK, A, kprime, k, 1);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads));
+  int32_t* cand = at<int32_t>(ws, pl.cand);
+  int32_t* ncand = at<int32_t>(ws, pl.ncand);
+  // coarse stage: top-k' of the routed scores (indices only)
+  TopkArgs ta = topk_args(p);
+  ta.S = at<float>(ws, pl.S);
+  ta.S_ld = p->L;
+  ta.k = (int)pl.cand_ld;
+  ta.out_idx = cand;
+  ta.out_ld = pl.cand_ld;
+  ta.out_count = ncand;
+  MISA_TRY(run_topk(cx, ta, pl, ws, p->L));
+  // fine stage: all H heads rescore the candidates, then top-k
+  ScoreArgs sa = score_args(p);
+  sa.cand = cand;
+  sa.cand_ld = pl.cand_ld;
+  sa.ncand = ncand;
+  sa.S = at<float>(ws, pl.S2);
+  sa.S_ld = pl.cand_ld;
+  HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "rerank scoring");
+  TopkArgs tb = topk_args(p);
+  tb.S = at<float>(ws, pl.S2);
+  tb.S_ld = pl.cand_ld;
+  tb.row_n = ncand;
+  tb.row_idx = cand;
+  tb.idx_ld = pl.cand_ld;
+  tb.k = k;
+  tb.out_idx = idx;
+  tb.out_score = scores;
+  tb.out_ld = k;
+  return run_topk(cx, tb, pl, ws, (int)pl.cand_ld);
+}
+
+misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,
+                      void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, true));
+  if (m < 1) return fail(MISA_ERR_INVALID_ARG, "m = %d must be >= 1", m);
+  if (k < 1) return fail(MISA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(idx, "idx"));
+  MISA_TRY(check_out(scores, "scores"));
+  const Plan pl = make_plan(p, MISA_OP_HISA_TOPK, 1, 1, k, m);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  float* beta = at<float>(ws, pl.beta);
+  // Stage 1: block scores of every visible block, then the top-m blocks
+  MISA_TRY(run_route(cx, p, pl, ws, 1, nullptr, nullptr, beta, pl.Mmax));
+  int32_t* blocks = at<int32_t>(ws, pl.blocks);
+  int32_t* nblocks = at<int32_t>(ws, pl.nblocks);
+  TopkArgs tb = topk_args(p);
+  tb.S = beta;
+  tb.S_ld = pl.Mmax;
+  tb.n_div = p->B;
+  tb.k = pl.mm;
+  tb.out_idx = blocks;
+  tb.out_ld = pl.mm;
+  tb.out_count = nblocks;
+  MISA_TRY(run_topk(cx, tb, pl, ws, pl.Mmax));
+  // Stage 2: the full indexer on the tokens of the chosen blocks, then top-k
+  int32_t* cand = at<int32_t>(ws, pl.cand);
+  int32_t* ncand = at<int32_t>(ws, pl.ncand);
+  HIP_TRY(launch_expand_blocks(cx, blocks, nblocks, pl.mm, p->pos, p->L, p->B, p->T, cand,
+                               pl.cand_ld, ncand),
+          "block expansion");
+  ScoreArgs sa = score_args(p);
+  sa.cand = cand;
+  sa.cand_ld = pl.cand_ld;
+  sa.ncand = ncand;
+  sa.S = at<float>(ws, pl.S2);
+  sa.S_ld = pl.cand_ld;
+  HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "refine scoring");
+  TopkArgs tf = topk_args(p);
+  tf.S = at<float>(ws, pl.S2);
+  tf.S_ld = pl.cand_ld;
+  tf.row_n = ncand;
+  tf.row_idx = cand;
+  tf.idx_ld = pl.cand_ld;
+  tf.k = k;
+  tf.out_idx = idx;
+  tf.out_score = scores;
+  tf.out_ld = k;
+  return run_topk(cx, tf, pl, ws, (int)pl.cand_ld);
+}
+
+const char* misa_status_str(int32_t status) {
+  switch (status) {
+    case MISA_OK: return "MISA_OK";
+    case MISA_ERR_INVALID_ARG: return "MISA_ERR_INVALID_ARG";
+    case MISA_ERR_UNSUPPORTED: return "MISA_ERR_UNSUPPORTED";
+    case MISA_ERR_WORKSPACE: return "MISA_ERR_WORKSPACE";
+    case MISA_ERR_HIP: return "MISA_ERR_HIP";
+    default: return "unknown misa_status";
+  }
+}
+
+const char* misa_last_error(void) { return g_last_error.c_str(); }
+
+misa_status misa_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return MISA_OK;
+}
+
+misa_status misa_profile_read(const char* name_substr, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(MISA_ERR_INVALID_ARG, "total_ms and launches must be non-NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double sum = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_prof) {
+    if (name_substr && !strstr(r.name.c_str(), name_substr)) continue;
+    if (hipEventSynchronize(r.stop) != hipSuccess) return fail(MISA_ERR_HIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return fail(MISA_ERR_HIP, "event elapsed failed");
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return MISA_OK;
+}
+
+misa_status misa_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof) {
+    if (r.start) (void)hipEventDestroy(r.start);
+    if (r.stop) (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  return MISA_OK;
+}
+
+}  // extern "C"

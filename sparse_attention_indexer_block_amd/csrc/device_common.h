@@ -1,0 +1,97 @@
+// Device-side helpers shared by the indexer kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace misa {
+
+constexpr int kHeadDim = 128;   // d supported by the kernels
+constexpr int kMaxHeads = 64;   // H supported by the kernels
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Visible prefix length of a query at position `pos` among L keys (clamped).
+__device__ __forceinline__ int visible_len(int pos, int L) {
+  int n = pos + 1;
+  return n < 0 ? 0 : (n > L ? L : n);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Two OCP E4M3FN bytes (byte 0/1 or 2/3 of `packed`) -> two bf16 packed in a
+// dword (HIGH_WORD selects bytes 2/3). The conversion is exact: E4M3 values have 4 significant bits and an
+// exponent range inside bf16's. Scale 1.0 (exponent 127) leaves values as is.
+template <bool HIGH_WORD>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t packed) {
+  bf16x2 v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)packed, 1.0f, HIGH_WORD);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two E4M3FN bytes -> two fp32 values (exact).
+template <bool HIGH_WORD>
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t packed, float& a, float& b) {
+  uint32_t bb = fp8x2_to_bf16x2<HIGH_WORD>(packed);
+  a = __uint_as_float(bb << 16);
+  b = __uint_as_float(bb & 0xffff0000u);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key); -0.0 is
+// folded onto +0.0 so the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t b = __float_as_uint(x);
+  b = (b == 0x80000000u) ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t u) {
+  uint32_t b = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
+  return __uint_as_float(b);
+}
+
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+template <typename Tv>
+__device__ __forceinline__ Tv wave_sum(Tv v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+template <typename Tv>
+__device__ __forceinline__ Tv wave_max(Tv v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    Tv o = __shfl_xor(v, off, kWave);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Inclusive prefix sum across one wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+}  // namespace misa

@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library against the CPU oracle on seeded inputs.
+
+Small sweeps cover several key tiles, query groups and ragged tails (T, L and B
+not multiples of the tile sizes), rows shorter than k, A = H (dense), A = 1,
+fp8 keys with negative scales, and explicit head lists.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from parity import (RTOL, check_heads, check_row, kdtype, oracle_problem, pool_bands, to_gpu,
+                    tolerance)
+
+pytestmark = pytest.mark.gpu
+
+S = pytest.importorskip("sparse_attention_indexer_block_amd")
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _case(seed, T, L, H, kdt, positions="random", w_scale=0.125, neg_scales=False):
+    inp = synth.random_small(seed, T=T, L=L, H=H, k_dtype=kdt, positions=positions, w_scale=w_scale)
+    if positions == "random" and T >= 3:
+        inp["pos"][0] = 0            # one visible key
+        inp["pos"][1] = L - 1        # the whole key array
+        inp["pos"][2] = min(L - 1, 127)
+    if neg_scales and inp["k_scale"] is not None:
+        inp["k_scale"][::3] *= np.float32(-1.0)
+    return inp
+
+
+# ----------------------------------------------------------------- block means
+
+@pytest.mark.parametrize("kdt", [O.KDT_BF16, O.KDT_FP8])
+def test_block_means(kdt):
+    rng = np.random.default_rng(5)
+    L, B = 1000, 128
+    if kdt == O.KDT_FP8:
+        # every finite E4M3FN code appears, with positive and negative scales
+        codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+        K = rng.choice(codes, size=(L, 128)).astype(np.uint8)
+        K[:2, :] = np.resize(codes, (2, 128))
+        ks = (rng.random(L).astype(np.float32) + np.float32(0.01)) * np.where(rng.random(L) < 0.3, -1, 1).astype(np.float32)
+        inp = {"K": K, "k_scale": ks.astype(np.float32)}
+        Kt = torch.from_numpy(K).cuda()
+        kst = torch.from_numpy(inp["k_scale"]).cuda()
+        vals = O.dequant_keys(K, O.KDT_FP8, inp["k_scale"])
+    else:
+        K = synth.encode_bf16(rng.standard_normal((L, 128), dtype=np.float32))
+        Kt = torch.from_numpy(K.view(np.int16)).cuda()
+        kst = None
+        vals = O.dequant_keys(K, O.KDT_BF16)
+    for Bv in [B, 7, 1000, 2048]:
+        got = _np(S.block_means(Kt, Bv, kst))
+        ref = O.full_block_means(vals, Bv).astype(np.float32)
+        np.testing.assert_allclose(got, ref, rtol=2.5e-7, atol=1e-38)
+
+
+# ----------------------------------------------------------------- router
+
+ROUTE_CASES = [
+    # seed, T, L, H, A, B, kdt
+    (1, 5, 300, 64, 8, 128, O.KDT_BF16),
+    (2, 17, 1000, 32, 8, 128, O.KDT_FP8),
+    (3, 9, 777, 48, 5, 37, O.KDT_BF16),
+    (4, 40, 2100, 64, 64, 128, O.KDT_BF16),
+    (5, 6, 257, 7, 1, 1, O.KDT_FP8),
+    (6, 8, 4096, 64, 8, 4096, O.KDT_BF16),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}A{c[4]}B{c[5]}k{c[6]}")
+def test_route(case):
+    seed, T, L, H, A, B, kdt = case
+    inp = _case(seed, T, L, H, kdt, neg_scales=True)
+    q, w, K, ks, pos = to_gpu(inp)
+    heads, r = S.route(q, w, K, pos, B, A, ks, with_r=True)
+    P = oracle_problem(inp, B)
+    _, ill = check_heads(P, A, _np(heads), _np(r))
+    assert ill == 0
+
+
+# ----------------------------------------------------------------- MISA
+
+MISA_CASES = [
+    # seed, T, L, H, A, B, k, kdt, positions
+    (11, 7, 500, 64, 8, 128, 64, O.KDT_BF16, "random"),
+    (12, 33, 1500, 64, 8, 128, 100, O.KDT_FP8, "random"),
+    (13, 16, 4096, 64, 8, 128, 512, O.KDT_BF16, "decode"),
+    (14, 70, 70, 32, 4, 16, 9, O.KDT_BF16, "prefill"),
+    (15, 12, 900, 64, 64, 128, 50, O.KDT_BF16, "random"),
+    (16, 10, 600, 16, 1, 64, 33, O.KDT_FP8, "random"),
+    (17, 9, 1200, 40, 13, 100, 1200, O.KDT_BF16, "random"),
+    (18, 300, 300, 64, 8, 128, 20, O.KDT_FP8, "prefill"),
+    (19, 5, 20000, 32, 8, 128, 700, O.KDT_BF16, "decode"),
+]
+
+
+def _check_misa(inp, B, A, k, idx, sc, heads_used=None, label=""):
+    P = oracle_problem(inp, B)
+    rtol = RTOL[kdtype(inp)]
+    if heads_used is None:
+        heads_used, _ = O.route(P, A)
+    worst = 0.0
+    for t in range(P.T):
+        n = P.n(t)
+        keys = np.arange(n)
+        sel, _ = O.first_k(O.routed_scores(P, t, heads_used[t], keys), keys, k)
+        hs = heads_used[t]
+        worst = max(worst, check_row(
+            idx[t], sc[t], k, n, "ascending", sel,
+            lambda s, t=t, hs=hs: O.routed_scores(P, t, hs, s),
+            lambda s, t=t, hs=hs: tolerance(P, t, hs, s, rtol), label=f"{label} row {t}"))
+    return worst
+
+
+@pytest.mark.parametrize("case", MISA_CASES, ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}A{c[4]}B{c[5]}k{c[6]}kd{c[7]}{c[8]}")
+def test_misa_score_topk(case):
+    seed, T, L, H, A, B, k, kdt, positions = case
+    inp = _case(seed, T, L, H, kdt, positions=positions, neg_scales=True)
+    q, w, K, ks, pos = to_gpu(inp)
+    heads = S.route(q, w, K, pos, B, A, ks)
+    idx, sc = S.score_topk(q, w, K, pos, B, A, k, ks)
+    torch.cuda.synchronize()
+    P = oracle_problem(inp, B)
+    heads_o, ill = check_heads(P, A, _np(heads))
+    assert ill == 0
+    worst = _check_misa(inp, B, A, k, _np(idx), _np(sc), heads_o, label="misa")
+    print(f"worst error / tolerance = {worst:.3e}")
+
+
+def test_misa_explicit_heads():
+    inp = _case(21, 11, 800, 64, O.KDT_BF16)
+    rng = np.random.default_rng(0)
+    A = 6
+    hs = np.stack([np.sort(rng.choice(64, A, replace=False)) for _ in range(11)]).astype(np.int32)
+    q, w, K, ks, pos = to_gpu(inp)
+    idx, sc = S.score_topk(q, w, K, pos, 128, A, 40, ks, heads=torch.from_numpy(hs).cuda())
+    _check_misa(inp, 128, A, 40, _np(idx), _np(sc), hs, label="explicit heads")
+
+
+# ----------------------------------------------------------------- MISA-dagger
+
+HIER_CASES = [
+    # seed, T, L, H, A, B, kprime, k, kdt
+    (31, 6, 900, 64, 8, 128, 200, 50, O.KDT_BF16),
+    (32, 9, 3000, 32, 8, 128, 1024, 256, O.KDT_FP8),
+    (33, 5, 400, 64, 4, 64, 400, 30, O.KDT_BF16),      # k' >= n: dense
+    (34, 8, 20000, 64, 8, 128, 4096, 512, O.KDT_FP8),  # long rows
+]
+
+
+def check_hier(inp, B, A, kprime, k, idx, sc, label="hier"):
+    P = oracle_problem(inp, B)
+    rtol = RTOL[kdtype(inp)]
+    heads, _ = O.route(P, A)
+    res, _, cands = O.misa_hier_topk(P, A, kprime, k, heads=heads)
+    for t in range(P.T):
+        n = P.n(t)
+        keys = np.arange(n)
+        rs = O.routed_scores(P, t, heads[t], keys)
+        sure, maybe = pool_bands(rs, cands[t], tolerance(P, t, heads[t], keys, rtol))
+        allh = list(range(P.H))
+        check_row(idx[t], sc[t], k, n, "ascending", res[t][0],
+                  lambda s, t=t: O.dense_scores(P, t, s),
+                  lambda s, t=t: tolerance(P, t, allh, s, rtol),
+                  sure_pool=sure, maybe_pool=maybe, label=f"{label} row {t}")
+
+
+@pytest.mark.parametrize("case", HIER_CASES, ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}kp{c[6]}k{c[7]}kd{c[8]}")
+def test_misa_hier_topk(case):
+    seed, T, L, H, A, B, kprime, k, kdt = case
+    inp = _case(seed, T, L, H, kdt, positions="random" if L < 10000 else "decode")
+    q, w, K, ks, pos = to_gpu(inp)
+    idx, sc = S.hier_topk(q, w, K, pos, B, A, kprime, k, ks)
+    check_hier(inp, B, A, kprime, k, _np(idx), _np(sc))
+
+
+# ----------------------------------------------------------------- HISA
+
+HISA_CASES = [
+    # seed, T, L, H, B, m, k, kdt
+    (41, 7, 1000, 64, 128, 3, 100, O.KDT_BF16),
+    (42, 12, 5000, 32, 128, 16, 512, O.KDT_FP8),
+    (43, 5, 600, 64, 64, 20, 40, O.KDT_BF16),     # m*B >= n: dense
+    (44, 6, 300, 16, 1, 50, 30, O.KDT_BF16),      # token blocks
+    (45, 4, 40000, 32, 128, 64, 2048, O.KDT_FP8),  # long rows
+]
+
+
+def check_hisa(inp, B, m, k, idx, sc, label="hisa"):
+    P = oracle_problem(inp, B)
+    rtol = RTOL[kdtype(inp)]
+    res, blocks = O.hisa_topk(P, m, k)
+    allh = list(range(P.H))
+    for t in range(P.T):
+        n = P.n(t)
+        beta = O.hisa_block_scores(P, t)
+        rho = O.block_logits(P, t)
+        # the GPU forms beta in float64 and compares it in float32
+        btol = 1e-6 * (np.abs(P.w[t])[:, None] * np.maximum(rho, 0)).sum(axis=0) + 1e-30
+        sure_b, maybe_b = pool_bands(beta, blocks[t], btol)
+        rng = O.block_ranges(n, B)
+        tok = lambda bs: set(s for b in bs for s in range(*rng[b]))
+        check_row(idx[t], sc[t], k, n, "ascending", res[t][0],
+                  lambda s, t=t: O.dense_scores(P, t, s),
+                  lambda s, t=t: tolerance(P, t, allh, s, rtol),
+                  sure_pool=tok(sure_b), maybe_pool=tok(maybe_b), label=f"{label} row {t}")
+
+
+@pytest.mark.parametrize("case", HISA_CASES, ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}B{c[4]}m{c[5]}k{c[6]}kd{c[7]}")
+def test_hisa_topk(case):
+    seed, T, L, H, B, m, k, kdt = case
+    inp = _case(seed, T, L, H, kdt, positions="random" if L < 10000 else "decode")
+    q, w, K, ks, pos = to_gpu(inp)
+    idx, sc = S.hisa_topk(q, w, K, pos, B, m, k, ks)
+    check_hisa(inp, B, m, k, _np(idx), _np(sc))
+
+
+# ----------------------------------------------------------------- properties
+
+def test_dense_equals_misa_with_all_heads():
+    inp = _case(51, 9, 1100, 32, O.KDT_FP8)
+    q, w, K, ks, pos = to_gpu(inp)
+    a = S.score_topk(q, w, K, pos, 128, 32, 77, ks)
+    hs = torch.arange(32, dtype=torch.int32, device="cuda").repeat(9, 1).contiguous()
+    b = S.score_topk(q, w, K, pos, 128, 32, 77, ks, heads=hs)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_determinism_and_poisoned_outputs():
+    inp = _case(52, 20, 3000, 64, O.KDT_BF16)
+    q, w, K, ks, pos = to_gpu(inp)
+    outs = []
+    for fill in (0x7F, 0x00):
+        idx = torch.full((20, 300), 0, dtype=torch.int32, device="cuda")
+        sc = torch.zeros((20, 300), dtype=torch.float32, device="cuda")
+        idx.view(torch.uint8).fill_(fill)
+        sc.view(torch.uint8).fill_(fill)
+        S.score_topk(q, w, K, pos, 128, 8, 300, ks, out=(idx, sc))
+        outs.append((idx.clone(), sc.clone()))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
+    _check_misa(inp, 128, 8, 300, _np(outs[0][0]), _np(outs[0][1]), label="poisoned")
+
+
+def test_causality_on_gpu():
+    inp = _case(53, 6, 2000, 64, O.KDT_BF16)
+    q, w, K, ks, pos = to_gpu(inp)
+    a = [x.clone() for x in S.score_topk(q, w, K, pos, 128, 8, 100, ks)]
+    h = [x.clone() for x in S.hisa_topk(q, w, K, pos, 128, 4, 100, ks)]
+    K2 = K.clone()
+    t = 3
+    K2[int(inp["pos"][t]) + 1:] = 0x40E0  # 7.0 in bf16
+    b = S.score_topk(q, w, K2, pos, 128, 8, 100, ks)
+    h2 = S.hisa_topk(q, w, K2, pos, 128, 4, 100, ks)
+    assert torch.equal(a[0][t], b[0][t]) and torch.equal(a[1][t], b[1][t])
+    assert torch.equal(h[0][t], h2[0][t]) and torch.equal(h[1][t], h2[1][t])
+
+
+def test_weight_doubling_is_exact():
+    inp = _case(54, 8, 1500, 64, O.KDT_FP8)
+    q, w, K, ks, pos = to_gpu(inp)
+    a = S.score_topk(q, w, K, pos, 128, 8, 90, ks)
+    b = S.score_topk(q, w * 2, K, pos, 128, 8, 90, ks)
+    assert torch.equal(a[0], b[0])
+    assert torch.equal(a[1] * 2, b[1])
+
+
+def test_rows_without_keys():
+    inp = _case(55, 4, 500, 64, O.KDT_BF16)
+    inp["pos"][:] = np.array([-1, -5, 0, 499], dtype=np.int32)
+    q, w, K, ks, pos = to_gpu(inp)
+    for idx, sc in (S.score_topk(q, w, K, pos, 128, 8, 16, ks),
+                    S.hier_topk(q, w, K, pos, 128, 8, 32, 16, ks),
+                    S.hisa_topk(q, w, K, pos, 128, 2, 16, ks)):
+        idx, sc = _np(idx), _np(sc)
+        assert (idx[:2] == -1).all() and np.isneginf(sc[:2]).all()
+        assert idx[2, 0] == 0 and (idx[2, 1:] == -1).all()
+        assert (idx[3] >= 0).all()
