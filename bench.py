@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X lightning-indexer hot path.
+
+Metric: indexed query-key pairs per second including routing and top-k
+(pairs = sum over queries of the visible prefix length pos[t] + 1), plus the
+roofline fraction of the dominant kernel.
+
+Headline workload (one GPU): MISA-dagger decode at a 128K context, DeepSeek-V3.2
+shape - T = 8 queries at positions L-8..L-1 over L = 131072 keys, H = 64
+indexer heads routed to A = 8, d = 128, fp8 E4M3 keys with a per-token fp32
+scale, bf16 queries, k' = 8192 candidates reranked by all 64 heads to k = 2048.
+One step = one misa_hier_topk call = block pooling, routing, routed scoring,
+top-k', full-head rerank and top-k.
+
+Protocol: inputs live in HBM before timing; the step reads one of R copies of
+the inputs in rotation (R * input bytes > 512 MiB, so the 256 MiB Infinity
+Cache cannot serve a step from the previous one). Each step is captured in a
+HIP graph (one graph per input copy) and replayed; a graph replay is checked
+against the eager call first. Dominant-kernel durations come from HIP events
+that the library records around each launch, in a second timed pass.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def _fail_multi_gpu(n):
+    print(f"bench.py measures one GPU only (asked for --gpus {n}); multi-GPU runs are not part "
+          "of this build. Run with --gpus 1.", file=sys.stderr)
+    sys.exit(2)
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def load_inputs(name, seed=0):
+    log(f"generating {name}")
+    import torch
+    import synth
+    wl = synth.CONFIGS[name]
+    inp = synth.make_inputs(wl, seed=seed)
+    dev = "cuda"
+    q = torch.from_numpy(inp["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(inp["w"]).to(dev)
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    if inp["k_scale"] is not None:
+        K = torch.from_numpy(inp["K"]).to(dev)
+        ks = torch.from_numpy(inp["k_scale"]).to(dev)
+    else:
+        K = torch.from_numpy(inp["K"].view(np.int16)).to(dev)
+        ks = None
+    return wl, inp, (q, w, K, ks, pos)
+
+
+def rotation_sets(tensors, min_bytes=600 << 20):
+    """Copies of the inputs at distinct addresses, enough to exceed the caches."""
+    per = sum(t.numel() * t.element_size() for t in tensors if t is not None)
+    r = max(2, -(-min_bytes // per))
+    sets = [tensors]
+    for _ in range(r - 1):
+        sets.append(tuple(None if t is None else t.clone() for t in tensors))
+    return sets, per
+
+
+class Step:
+    """One call of an entry point with preallocated workspace and outputs."""
+
+    def __init__(self, S, path, wl, tensors, A=None):
+        import torch
+        self.S, self.path, self.wl = S, path, wl
+        self.A = wl.A if A is None else A
+        q, w, K, ks, pos = tensors
+        p = S.make_problem(q, w, K, pos, wl.B, ks)
+        op = {"hier": S.OP_HIER_TOPK, "misa": S.OP_SCORE_TOPK, "hisa": S.OP_HISA_TOPK}[path]
+        nbytes = S.workspace_bytes(p, op, A=self.A, kprime=wl.kprime, k=wl.k, m=wl.m)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.out = (torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda"),
+                    torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda"))
+
+    def __call__(self, tensors):
+        q, w, K, ks, pos = tensors
+        wl, S = self.wl, self.S
+        if self.path == "hier":
+            return S.hier_topk(q, w, K, pos, wl.B, self.A, wl.kprime, wl.k, ks, ws=self.ws, out=self.out)
+        if self.path == "misa":
+            return S.score_topk(q, w, K, pos, wl.B, self.A, wl.k, ks, ws=self.ws, out=self.out)
+        return S.hisa_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out)
+
+
+def time_path(S, path, wl, tensors, steps, warmup, use_graphs=True, A=None, kernel=None):
+    """Returns (ms per step, per-kernel avg ms dict or None)."""
+    import torch
+    log(f"timing {path} on {wl.name} (A={A or wl.A}, {steps} steps)")
+    sets, _ = rotation_sets(tensors)
+    step = Step(S, path, wl, tensors, A=A)
+    eager = [x.clone() for x in step(sets[0])]
+    torch.cuda.synchronize()
+    graphs = []
+    if use_graphs:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(sets[0])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for st in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(st)
+            graphs.append(g)
+        # a replay must reproduce the eager result (also after other work)
+        for _ in range(2):
+            graphs[0].replay()
+            torch.cuda.synchronize()
+            if not (torch.equal(step.out[0], eager[0]) and torch.equal(step.out[1], eager[1])):
+                raise RuntimeError(f"{path}: graph replay differs from the eager call")
+            step(sets[1])
+            torch.cuda.synchronize()
+    run = (lambda i: graphs[i % len(graphs)].replay()) if use_graphs else (lambda i: step(sets[i % len(sets)]))
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        run(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    kms = None
+    if kernel is not None:
+        # second timed pass, eager, with per-launch HIP events on the launch stream
+        S.profile_reset()
+        S.profile_enable(True)
+        for i in range(steps):
+            step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        S.profile_enable(False)
+        kms = {}
+        for name in kernel:
+            tot, n = S.profile_read(name)
+            kms[name] = (tot / n if n else None, n)
+        S.profile_reset()
+    del graphs
+    return ms, kms
+
+
+def pairs_of(inp):
+    return int(np.sum(np.minimum(np.maximum(inp["pos"].astype(np.int64) + 1, 0), inp["wl"].L)))
+
+
+def score_kernel_bytes(wl, A):
+    """Compulsory HBM bytes of one routed-scoring launch: every key once
+    (128 code bytes + 4 scale bytes for fp8, 256 bytes for bf16), the routed
+    q rows, the head weights and positions. Score rows written for the
+    selection are intermediate and not counted."""
+    per_key = 132 if wl.k_dtype == 1 else 256
+    return wl.L * per_key + wl.T * A * 128 * 2 + wl.T * wl.H * 4 + wl.T * 4
+
+
+def cpu_baseline(inp, wl, budget_s=12.0):
+    """The oracle (float64 numpy) on the host cores: whole steps of the same
+    workload (decode the inputs, then the full MISA-dagger path for every
+    query), repeated until about budget_s seconds have passed."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    kdt = O.KDT_FP8 if inp["k_scale"] is not None else O.KDT_BF16
+    t0 = time.perf_counter()
+    reps, pairs = 0, 0
+    while reps == 0 or time.perf_counter() - t0 < budget_s:
+        P = O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], wl.B, kdt, inp["k_scale"])
+        O.misa_hier_topk(P, wl.A, wl.kprime, wl.k)
+        pairs += sum(P.n(t) for t in range(P.T))
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full steps of {wl.name} (all {wl.T} queries: decode inputs, routing, "
+                      f"routed scores, top-k', 64-head rerank, top-k) in {dt:.1f} s"}
+
+
+def traffic_from_profiles(kernel_tag):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 PMC
+    summaries, or None when they are missing or the kernel source changed."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "score_keys_c4_pmc.json")
+    src = os.path.join(ROOT, "sparse_attention_indexer_block_amd", "csrc", "score_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary paths")
+    ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        _fail_multi_gpu(max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))))
+
+    import torch
+    import sparse_attention_indexer_block_amd as S
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    S.lib()
+
+    name = "c4_hier_decode_128k"
+    wl, inp, tensors = load_inputs(name)
+    pairs = pairs_of(inp)
+    ms, kms = time_path(S, "hier", wl, tensors, args.steps, args.warmup, use_graphs=not args.eager,
+                        kernel=["score_keys", "score_gather", "route_partial", "block_sums", "topk"])
+    value = pairs / (ms * 1e-3)
+
+    score_ms, score_n = kms["score_keys"]
+    algo_bytes = score_kernel_bytes(wl, wl.A)
+    achieved = algo_bytes / (score_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles("score_keys")
+    rec = {
+        "metric": "indexer query-key pairs/sec incl. top-k at L=128K; % of HBM/MFMA roofline",
+        "value": value,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: MISA-dagger decode, T={wl.T}, L={wl.L}, H={wl.H}->A={wl.A}, "
+                               f"d={wl.d}, fp8 e4m3 K + fp32 per-token scale, bf16 q, B={wl.B}, "
+                               f"k'={wl.kprime}, k={wl.k}",
+                   "global_batch": wl.T, "seq_len": wl.L, "parallelism": "none (1 GPU)",
+                   "timing": "eager calls" if args.eager else "HIP graph replay per step",
+                   "input_rotation_bytes": "> 600 MiB"},
+        "roofline": {"bound": "hbm", "kernel": "score_keys (routed MFMA scoring)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel_avg_ms": score_ms, "kernel_launches": score_n,
+                     "algorithmic_bytes_per_launch": algo_bytes},
+        "kernels_avg_ms": {k: v[0] for k, v in kms.items()},
+    }
+    if not args.no_extra:
+        extra = {}
+        steps = max(20, args.steps // 4)
+        for label, path, nm, A in [("misa_c4", "misa", name, None),
+                                   ("dense_dsa_c4", "misa", name, 64),
+                                   ("misa_c5", "misa", "c5_glm5_hisa_128k", None),
+                                   ("hisa_c5", "hisa", "c5_glm5_hisa_128k", None),
+                                   ("misa_c2", "misa", "c2_decode_batch", None),
+                                   ("misa_c3_prefill", "misa", "c3_causal_prefill", None)]:
+            w2, i2, t2 = (wl, inp, tensors) if nm == name else load_inputs(nm)
+            st = steps if "c3" not in nm else 5
+            m2, k2 = time_path(S, path, w2, t2, st, 2, use_graphs=not args.eager, A=A,
+                               kernel=["score_keys", "score_gather"])
+            p2 = pairs_of(i2)
+            e = {"pairs_per_s": p2 / (m2 * 1e-3), "ms_per_step": m2,
+                 "score_keys_avg_ms": k2["score_keys"][0], "score_gather_avg_ms": k2["score_gather"][0]}
+            if k2["score_keys"][0]:
+                flops = 2.0 * (A or w2.A) * 128 * p2
+                e["score_keys_tflops"] = flops / (k2["score_keys"][0] * 1e-3) / 1e12
+                e["score_keys_hbm_gbs"] = score_kernel_bytes(w2, A or w2.A) / (k2["score_keys"][0] * 1e-3) / 1e9
+            extra[label] = e
+            if nm != name:
+                del t2
+                torch.cuda.empty_cache()
+        if extra["dense_dsa_c4"]["pairs_per_s"]:
+            extra["misa_over_dense_dsa_c4"] = extra["misa_c4"]["pairs_per_s"] / extra["dense_dsa_c4"]["pairs_per_s"]
+        rec["secondary"] = extra
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        rec["cpu_baseline"] = cpu_baseline(inp, wl)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
