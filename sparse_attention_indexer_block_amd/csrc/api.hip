@@ -44,20 +44,20 @@ static std::mutex g_prof_mu;
 static bool g_prof_on = false;
 static std::vector<ProfRec> g_prof;
 
-void prof_begin(const char* name, hipStream_t stream) {
-  if (!g_prof_on) return;
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof_on) return false;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfRec r;
   r.name = name;
-  if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return;
-  (void)hipEventRecord(r.start, stream);
+  if (hipEventCreate(&r.start) != hipSuccess) return false;
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return false;
+  }
   g_prof.push_back(r);
-}
-
-void prof_end(hipStream_t stream) {
-  if (!g_prof_on) return;
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof.empty()) (void)hipEventRecord(g_prof.back().stop, stream);
+  *start = r.start;
+  *stop = r.stop;
+  return true;
 }
 
 // ---------------------------------------------------------------- workspace
@@ -72,11 +72,12 @@ struct Bump {
 };
 
 struct Plan {
-  size_t ksum = 0, tsum = 0, pmax = 0, heads = 0, beta = 0;
+  size_t ksum = 0, tsum = 0, pmax = 0, heads = 0, beta = 0, qr = 0, wr = 0;
   size_t S = 0;
-  size_t ghist = 0, rkeys = 0, ridx = 0, rcnt = 0, gkeys = 0, gidx = 0;
+  size_t rmm = 0, ghist = 0, done = 0, rkeys = 0, ridx = 0, rcnt = 0, gkeys = 0, gidx = 0;
   size_t cand = 0, ncand = 0, S2 = 0, blocks = 0, nblocks = 0;
-  long long cand_ld = 0;
+  long long S_ld = 0, cand_ld = 0, S2_ld = 0, beta_ld = 0;
+  long long zero_words = 0;  // ghist + done, cleared by the first kernel that needs them
   int Mmax = 0, mm = 0;
   size_t total = 0;
 };
@@ -88,9 +89,12 @@ static void plan_long(Bump& bp, Plan& pl, int rows, int max_n) {
   if (max_n <= topk_lds_cap()) return;
   const size_t nch = (size_t)topk_long_chunks(max_n);
   const size_t rld = nch * (size_t)topk_long_chunk();
-  const size_t need_hist = (size_t)rows * topk_coarse_bins() * 4;
+  const size_t nmm = nch > (size_t)score_max_splits() ? nch : (size_t)score_max_splits();
   // one set of scratch serves every selection of a call (they run in order)
-  pl.ghist = bp.take(need_hist);
+  pl.rmm = bp.take(nmm * rows * 2 * 4);
+  pl.zero_words = (long long)rows * topk_coarse_bins() + rows;
+  pl.ghist = bp.take((size_t)pl.zero_words * 4);
+  pl.done = pl.ghist + (size_t)rows * topk_coarse_bins() * 4;
   pl.rkeys = bp.take((size_t)rows * rld * 4);
   pl.ridx = bp.take((size_t)rows * rld * 4);
   pl.rcnt = bp.take((size_t)rows * nch * 4);
@@ -120,32 +124,41 @@ static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, i
     case MISA_OP_SCORE_TOPK:
       plan_route(bp, pl, p);
       pl.heads = bp.take((size_t)T * A * 4);
-      pl.S = bp.take((size_t)T * L * 4);
+      pl.qr = bp.take((size_t)T * A * 128 * 2);
+      pl.wr = bp.take((size_t)T * A * 4);
+      pl.S_ld = padded_ld(L);
+      pl.S = bp.take((size_t)T * pl.S_ld * 4);
       plan_long(bp, pl, T, L);
       break;
     case MISA_OP_HIER_TOPK: {
       plan_route(bp, pl, p);
       pl.heads = bp.take((size_t)T * A * 4);
-      pl.S = bp.take((size_t)T * L * 4);
-      pl.cand_ld = kprime < L ? kprime : L;
+      pl.qr = bp.take((size_t)T * A * 128 * 2);
+      pl.wr = bp.take((size_t)T * A * 4);
+      pl.S_ld = padded_ld(L);
+      pl.S = bp.take((size_t)T * pl.S_ld * 4);
+      pl.cand_ld = padded_ld(kprime < L ? kprime : L);
       pl.cand = bp.take((size_t)T * pl.cand_ld * 4);
       pl.ncand = bp.take((size_t)T * 4);
-      pl.S2 = bp.take((size_t)T * pl.cand_ld * 4);
-      plan_long(bp, pl, T, L);  // covers the k' stage and the final stage (cand_ld <= L)
+      pl.S2_ld = pl.cand_ld;
+      pl.S2 = bp.take((size_t)T * pl.S2_ld * 4);
+      plan_long(bp, pl, T, L);  // covers the k' stage and the final stage (k' <= L)
       break;
     }
     case MISA_OP_HISA_TOPK: {
       plan_route(bp, pl, p);
       pl.Mmax = ceil_div(L, p->B);
       pl.mm = m < pl.Mmax ? m : pl.Mmax;
-      pl.beta = bp.take((size_t)T * pl.Mmax * 4);
+      pl.beta_ld = padded_ld(pl.Mmax);
+      pl.beta = bp.take((size_t)T * pl.beta_ld * 4);
       pl.blocks = bp.take((size_t)T * pl.mm * 4);
       pl.nblocks = bp.take((size_t)T * 4);
       const long long mb = (long long)pl.mm * p->B;
-      pl.cand_ld = mb < L ? mb : L;
+      pl.cand_ld = padded_ld(mb < L ? mb : L);
       pl.cand = bp.take((size_t)T * pl.cand_ld * 4);
       pl.ncand = bp.take((size_t)T * 4);
-      pl.S2 = bp.take((size_t)T * pl.cand_ld * 4);
+      pl.S2_ld = pl.cand_ld;
+      pl.S2 = bp.take((size_t)T * pl.S2_ld * 4);
       const int mx = pl.Mmax > (int)pl.cand_ld ? pl.Mmax : (int)pl.cand_ld;
       plan_long(bp, pl, T, mx);
       break;
@@ -221,21 +234,25 @@ static misa_status check_out(const void* ptr, const char* name) {
 // ---------------------------------------------------------------- pipelines
 
 static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws,
-                             int A, int32_t* heads, float* r, float* beta, int beta_ld) {
+                             int A, int32_t* heads, float* r, float* beta, int beta_ld,
+                             uint16_t* qr = nullptr, float* wr = nullptr) {
   const bool fp8 = p->k_dtype == MISA_K_FP8_E4M3FN;
   double* ksum = at<double>(ws, pl.ksum);
   double* tsum = at<double>(ws, pl.tsum);
   double* pmax = at<double>(ws, pl.pmax);
-  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr), "block sums");
-  HIP_TRY(launch_tail_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, p->T, p->pos, tsum), "tail sums");
+  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum),
+          "block sums");
   HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, tsum, pmax, heads, r,
-                       beta, beta_ld),
+                       beta, beta_ld, qr, wr),
           "router");
   return MISA_OK;
 }
 
-static TopkLongWs long_ws(const Plan& pl, void* ws) {
+static TopkLongWs long_ws(const Plan& pl, void* ws, int nmm) {
   TopkLongWs lw;
+  lw.rmm = at<uint32_t>(ws, pl.rmm);
+  lw.nmm = nmm;
+  lw.done = at<uint32_t>(ws, pl.done);
   lw.ghist = at<uint32_t>(ws, pl.ghist);
   lw.rkeys = at<uint32_t>(ws, pl.rkeys);
   lw.ridx = at<int32_t>(ws, pl.ridx);
@@ -245,12 +262,22 @@ static TopkLongWs long_ws(const Plan& pl, void* ws) {
   return lw;
 }
 
-static misa_status run_topk(const LaunchCtx& cx, const TopkArgs& a, const Plan& pl, void* ws, int max_n) {
+// Top-k of rows of up to max_n items. Long rows need each row's key range:
+// `nmm` > 0 means the scoring kernel already wrote it (and cleared the
+// selection counters); otherwise a range pass runs first.
+static misa_status run_topk(const LaunchCtx& cx, const TopkArgs& a, const Plan& pl, void* ws,
+                            int max_n, int nmm = 0) {
   if (max_n <= topk_lds_cap()) {
     HIP_TRY(launch_topk_rows(cx, a, max_n), "top-k");
-  } else {
-    HIP_TRY(launch_topk_long(cx, a, long_ws(pl, ws), max_n), "top-k (long rows)");
+    return MISA_OK;
   }
+  if (nmm == 0) {
+    HIP_TRY(launch_topk_range(cx, a, at<uint32_t>(ws, pl.rmm), at<uint32_t>(ws, pl.ghist),
+                              pl.zero_words, max_n),
+            "top-k range");
+    nmm = topk_long_chunks(max_n);
+  }
+  HIP_TRY(launch_topk_long(cx, a, long_ws(pl, ws, nmm), max_n), "top-k (long rows)");
   return MISA_OK;
 }
 
@@ -278,25 +305,37 @@ static TopkArgs topk_args(const misa_problem* p) {
   return a;
 }
 
-// Routed scores of every visible key into S[T, L].
+// Routed scores of every visible key into S[T, S_ld]. Returns in *nmm the
+// number of per-split key ranges written for long-row selection (0 if none).
 static misa_status run_routed_scores(const LaunchCtx& cx, const misa_problem* p, const Plan& pl,
-                                     void* ws, int A, const int32_t* heads_in) {
-  const int32_t* heads = heads_in;
-  if (!heads) {
-    int32_t* hw = at<int32_t>(ws, pl.heads);
-    if (A == p->H) {
-      heads = nullptr;  // dense: slot j is head j, no routing needed
-    } else {
-      MISA_TRY(run_route(cx, p, pl, ws, A, hw, nullptr, nullptr, 0));
-      heads = hw;
-    }
-  }
+                                     void* ws, int A, const int32_t* heads, int* nmm) {
   ScoreArgs sa = score_args(p);
-  sa.heads = heads;
+  uint16_t* qr = at<uint16_t>(ws, pl.qr);
+  float* wr = at<float>(ws, pl.wr);
+  if (heads) {
+    // caller-chosen heads: pack their q rows and weights
+    HIP_TRY(launch_gather_heads(cx, p->q, p->w, heads, p->T, p->H, A, qr, wr), "head gather");
+  } else if (A < p->H) {
+    // routing packs the q rows and weights of the chosen heads as it selects them
+    MISA_TRY(run_route(cx, p, pl, ws, A, at<int32_t>(ws, pl.heads), nullptr, nullptr, 0, qr, wr));
+  }
+  if (heads || A < p->H) {
+    sa.q = qr;
+    sa.w = wr;
+    sa.H = A;
+  }  // else dense: all H heads in their own order
   sa.A = A;
   sa.S = at<float>(ws, pl.S);
-  sa.S_ld = p->L;
-  HIP_TRY(launch_score_keys(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "routed scoring");
+  sa.S_ld = pl.S_ld;
+  const bool long_rows = p->L > topk_lds_cap();
+  if (long_rows) {
+    sa.rmm = at<uint32_t>(ws, pl.rmm);
+    sa.zero = at<uint32_t>(ws, pl.ghist);
+    sa.zero_n = pl.zero_words;
+  }
+  int nsplit = 0;
+  HIP_TRY(launch_score_keys(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN, &nsplit), "routed scoring");
+  *nmm = long_rows ? nsplit : 0;
   return MISA_OK;
 }
 
@@ -338,7 +377,7 @@ misa_status misa_block_means(const misa_problem* p, float* kbar, void* ws, size_
   MISA_TRY(check_ws(pl, ws, ws_bytes));
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
   HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, p->k_dtype == MISA_K_FP8_E4M3FN, p->L, p->B,
-                            at<double>(ws, pl.ksum), kbar),
+                            at<double>(ws, pl.ksum), kbar, 0, nullptr, nullptr),
           "block means");
   return MISA_OK;
 }
@@ -368,15 +407,16 @@ misa_status misa_score_topk(const misa_problem* p, int32_t A, const int32_t* hea
   const Plan pl = make_plan(p, MISA_OP_SCORE_TOPK, A, 1, k, 1);
   MISA_TRY(check_ws(pl, ws, ws_bytes));
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
-  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads));
+  int nmm = 0;
+  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads, &nmm));
   TopkArgs ta = topk_args(p);
   ta.S = at<float>(ws, pl.S);
-  ta.S_ld = p->L;
+  ta.S_ld = pl.S_ld;
   ta.k = k;
   ta.out_idx = idx;
   ta.out_score = scores;
   ta.out_ld = k;
-  return run_topk(cx, ta, pl, ws, p->L);
+  return run_topk(cx, ta, pl, ws, p->L, nmm);
 }
 
 misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* heads, int32_t kprime,
@@ -393,29 +433,32 @@ misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* head
   const Plan pl = make_plan(p, MISA_OP_HIER_TOPK, A, kprime, k, 1);
   MISA_TRY(check_ws(pl, ws, ws_bytes));
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
-  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads));
+  int nmm = 0;
+  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads, &nmm));
   int32_t* cand = at<int32_t>(ws, pl.cand);
   int32_t* ncand = at<int32_t>(ws, pl.ncand);
+  const int kc = kprime < p->L ? kprime : p->L;  // candidates kept per query
   // coarse stage: top-k' of the routed scores (indices only)
   TopkArgs ta = topk_args(p);
   ta.S = at<float>(ws, pl.S);
-  ta.S_ld = p->L;
-  ta.k = (int)pl.cand_ld;
+  ta.S_ld = pl.S_ld;
+  ta.k = kc;
   ta.out_idx = cand;
   ta.out_ld = pl.cand_ld;
   ta.out_count = ncand;
-  MISA_TRY(run_topk(cx, ta, pl, ws, p->L));
+  MISA_TRY(run_topk(cx, ta, pl, ws, p->L, nmm));
   // fine stage: all H heads rescore the candidates, then top-k
   ScoreArgs sa = score_args(p);
   sa.cand = cand;
   sa.cand_ld = pl.cand_ld;
+  sa.cand_max = kc;
   sa.ncand = ncand;
   sa.S = at<float>(ws, pl.S2);
-  sa.S_ld = pl.cand_ld;
+  sa.S_ld = pl.S2_ld;
   HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "rerank scoring");
   TopkArgs tb = topk_args(p);
   tb.S = at<float>(ws, pl.S2);
-  tb.S_ld = pl.cand_ld;
+  tb.S_ld = pl.S2_ld;
   tb.row_n = ncand;
   tb.row_idx = cand;
   tb.idx_ld = pl.cand_ld;
@@ -423,7 +466,7 @@ misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* head
   tb.out_idx = idx;
   tb.out_score = scores;
   tb.out_ld = k;
-  return run_topk(cx, tb, pl, ws, (int)pl.cand_ld);
+  return run_topk(cx, tb, pl, ws, kc);
 }
 
 misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,
@@ -439,12 +482,12 @@ misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx,
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
   float* beta = at<float>(ws, pl.beta);
   // Stage 1: block scores of every visible block, then the top-m blocks
-  MISA_TRY(run_route(cx, p, pl, ws, 1, nullptr, nullptr, beta, pl.Mmax));
+  MISA_TRY(run_route(cx, p, pl, ws, 1, nullptr, nullptr, beta, (int)pl.beta_ld));
   int32_t* blocks = at<int32_t>(ws, pl.blocks);
   int32_t* nblocks = at<int32_t>(ws, pl.nblocks);
   TopkArgs tb = topk_args(p);
   tb.S = beta;
-  tb.S_ld = pl.Mmax;
+  tb.S_ld = pl.beta_ld;
   tb.n_div = p->B;
   tb.k = pl.mm;
   tb.out_idx = blocks;
@@ -454,19 +497,21 @@ misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx,
   // Stage 2: the full indexer on the tokens of the chosen blocks, then top-k
   int32_t* cand = at<int32_t>(ws, pl.cand);
   int32_t* ncand = at<int32_t>(ws, pl.ncand);
+  const int ncmax = (long long)pl.mm * p->B < p->L ? pl.mm * p->B : p->L;  // candidate bound
   HIP_TRY(launch_expand_blocks(cx, blocks, nblocks, pl.mm, p->pos, p->L, p->B, p->T, cand,
                                pl.cand_ld, ncand),
           "block expansion");
   ScoreArgs sa = score_args(p);
   sa.cand = cand;
   sa.cand_ld = pl.cand_ld;
+  sa.cand_max = ncmax;
   sa.ncand = ncand;
   sa.S = at<float>(ws, pl.S2);
-  sa.S_ld = pl.cand_ld;
+  sa.S_ld = pl.S2_ld;
   HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "refine scoring");
   TopkArgs tf = topk_args(p);
   tf.S = at<float>(ws, pl.S2);
-  tf.S_ld = pl.cand_ld;
+  tf.S_ld = pl.S2_ld;
   tf.row_n = ncand;
   tf.row_idx = cand;
   tf.idx_ld = pl.cand_ld;
@@ -474,7 +519,7 @@ misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx,
   tf.out_idx = idx;
   tf.out_score = scores;
   tf.out_ld = k;
-  return run_topk(cx, tf, pl, ws, (int)pl.cand_ld);
+  return run_topk(cx, tf, pl, ws, ncmax);
 }
 
 const char* misa_status_str(int32_t status) {

@@ -3,17 +3,20 @@
 // per-kernel timing (HIP events on the launch stream) wraps each launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <utility>
 
 namespace misa {
 
 constexpr int kHeadDimHost = 128;  // the only head dim the kernels implement
 
-// Profiling hooks (implemented in api.hip). prof_begin/prof_end record a pair
-// of HIP events around one launch when profiling is enabled.
-void prof_begin(const char* name, hipStream_t stream);
-void prof_end(hipStream_t stream);
+// Profiling hook (implemented in api.hip): when profiling is enabled it
+// creates a start/stop event pair for the launch named `name` and returns true.
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
 struct LaunchCtx {
   hipStream_t stream;
@@ -21,46 +24,80 @@ struct LaunchCtx {
   template <typename... KArgs, typename... Args>
   hipError_t launch(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
                     Args... args) const {
-    prof_begin(name, stream);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (prof_events(name, &e0, &e1)) {
+      // hipExtLaunchKernel stamps the events with the kernel's own start/end
+      std::tuple<KArgs...> tup(static_cast<KArgs>(args)...);
+      void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+      fill_arg_ptrs(tup, ptrs, std::index_sequence_for<KArgs...>{});
+      hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs,
+                                        shmem, stream, e0, e1, 0);
+      return e != hipSuccess ? e : hipGetLastError();
+    }
     kernel<<<grid, block, shmem, stream>>>(static_cast<KArgs>(args)...);
-    hipError_t e = hipGetLastError();
-    prof_end(stream);
-    return e;
+    return hipGetLastError();
+  }
+
+ private:
+  template <typename Tup, size_t... I>
+  static void fill_arg_ptrs(Tup& tup, void** ptrs, std::index_sequence<I...>) {
+    ((ptrs[I] = static_cast<void*>(&std::get<I>(tup))), ...);
   }
 };
 
+// Row stride (in elements) of internal [rows, n] buffers: a multiple of 64 so
+// rows start 256-byte aligned and can be read with 16-byte vector loads.
+inline long long padded_ld(long long n) { return ((n + 63) / 64) * 64; }
+
 // ---- router side (route_kernels.hip)
+// Full-block key sums ksum[ceil(L/B), 128] (and optional means kbar) and, when
+// tsum is given, the sum of each query's last (possibly partial) block.
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
-                             int L, int B, double* ksum, float* kbar);
-hipError_t launch_tail_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
-                            int L, int B, int T, const int32_t* pos, double* tsum);
+                             int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
+                             double* tsum);
 int route_chunks(int L, int B);
+// Router: heads[T,A] (ascending), optional r[T,H], optional HISA block scores
+// beta, and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed
+// in slot order (so scoring needs no head indirection).
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
                         int T, int H, int L, int B, int A, const double* ksum, const double* tsum,
-                        double* pmax, int32_t* heads, float* r_out, float* beta, int beta_ld);
+                        double* pmax, int32_t* heads, float* r_out, float* beta, int beta_ld,
+                        uint16_t* qr, float* wr);
+// Pack q rows and weights of given heads [T,A] in slot order (ids outside [0,H)
+// give zero rows and weights).
+hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,
+                               const int32_t* heads, int T, int H, int A, uint16_t* qr, float* wr);
 
 // ---- scoring (score_kernels.hip)
 struct ScoreArgs {
-  const uint16_t* q;     // [T,H,128] bf16
+  const uint16_t* q;     // [T,H,128] bf16; slot j < A of query t scores row j
   const float* w;        // [T,H]
-  const int32_t* heads;  // [T,A] or null (slot j scores head j)
-  int A, H, T;
+  int A, H, T;           // A <= H rows of each query are scored (H is the row stride)
   const void* K;         // [L,128] bf16 or e4m3fn
   const float* kscale;   // [L] (fp8)
   int L;
   const int32_t* pos;    // [T]
   const int32_t* cand;   // gather mode: [T, cand_ld] key indices
   long long cand_ld;
+  int cand_max;          // gather mode: bound on ncand[t]
   const int32_t* ncand;  // gather mode: [T] candidate counts
   float* S;              // output rows
   long long S_ld;
+  uint32_t* rmm;         // optional [nsplit, T, 2] per-split {min, max} score key of each row
+  uint32_t* zero;        // optional buffer the first workgroup clears ...
+  long long zero_n;      // ... (zero_n 32-bit words)
   int tiles_per_split;
   int ngroups;
   int reverse;
+  int nsplit;
+  int target_wgs;        // workgroups to aim for (0: default)
 };
-// Routed (or dense with heads == null, A == H) scores of every visible key:
-// S[t, s] = sum_j w[t,h_j] ReLU(q[t,h_j] . k[s]) for s < n_t.
-hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8);
+// Scores of every visible key over the first A rows of each query's q and w
+// (the routed rows packed by the router, or all H heads for the dense indexer):
+// S[t, s] = sum_{j<A} w[t,j] ReLU(q[t,j] . k[s]) for s < n_t. The number of
+// key splits (rows of rmm) is returned in *nsplit_out.
+int score_max_splits();
+hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* nsplit_out);
 // Dense scores of gathered keys: S[t, j] = I_all(t, cand[t, j]) for j < ncand[t].
 hipError_t launch_score_gather(const LaunchCtx& cx, ScoreArgs a, bool fp8);
 
@@ -88,7 +125,10 @@ hipError_t launch_topk_rows(const LaunchCtx& cx, const TopkArgs& a, int max_n);
 // Workspace of the long-row path; every [rows, *] array has row stride
 // topk_long_chunks(max_n) * topk_long_chunk().
 struct TopkLongWs {
-  uint32_t* ghist;     // [rows, 4096]
+  const uint32_t* rmm; // [nmm, rows, 2] row key ranges written by the scoring kernel
+  int nmm;
+  uint32_t* done;      // [rows] completion counters (zero on entry)
+  uint32_t* ghist;     // [rows, 4096] (zero on entry)
   uint32_t* rkeys;     // [rows, stride] candidate keys (one region per chunk)
   int32_t* ridx;       // [rows, stride] candidate indices
   int32_t* rcnt;       // [rows, nchunk]
@@ -100,6 +140,10 @@ int topk_long_chunk();
 int topk_coarse_bins();
 hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLongWs& ws,
                             int max_n);
+// Rows whose key range is not known yet: per-chunk ranges into rmm_out
+// [topk_long_chunks(max_n), rows, 2] (and ghist/done cleared).
+hipError_t launch_topk_range(const LaunchCtx& cx, const TopkArgs& a, uint32_t* rmm_out,
+                             uint32_t* zero, long long zero_n, int max_n);
 
 hipError_t launch_fill_u32(const LaunchCtx& cx, uint32_t* p, size_t n, uint32_t v);
 hipError_t launch_expand_blocks(const LaunchCtx& cx, const int32_t* blocks, const int32_t* nblocks,

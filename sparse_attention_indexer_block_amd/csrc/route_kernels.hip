@@ -14,93 +14,114 @@
 namespace misa {
 
 // -------------------------------------------------------------------------
-// Eight consecutive key dims [8*dg, 8*dg+8) of key s, widened to float64.
+// One 16-byte slice of key s, dims [DPT*dg, DPT*dg + DPT) (DPT = 8 bf16 or 16
+// fp8 codes), widened to float64; fp8 codes are multiplied by the key's scale,
+// which is exact in float64.
 template <bool FP8>
-__device__ __forceinline__ void load_key8_f64(const void* K, const float* kscale, int s, int dg,
-                                              double out[8]) {
-  if constexpr (!FP8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(K) +
-                                                    (size_t)s * kHeadDim + dg * 8);
+struct KeySlice {
+  static constexpr int DPT = FP8 ? 16 : 8;
+  static __device__ __forceinline__ u32x4 load(const void* K, int s, int dg) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(K) + (size_t)s * kHeadDim * (FP8 ? 1 : 2);
+    return *reinterpret_cast<const u32x4*>(base + 16 * dg);
+  }
+  static __device__ __forceinline__ void widen(u32x4 v, double sc, double* out) {
+    if constexpr (!FP8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      out[2 * j] = (double)bf16_bits_to_f32(v[j] & 0xffffu);
-      out[2 * j + 1] = (double)bf16_bits_to_f32(v[j] >> 16);
-    }
-  } else {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(K) +
-                                                    (size_t)s * kHeadDim + dg * 8);
-    const double sc = (double)kscale[s];
+      for (int j = 0; j < 4; ++j) {
+        out[2 * j] = (double)bf16_bits_to_f32(v[j] & 0xffffu);
+        out[2 * j + 1] = (double)bf16_bits_to_f32(v[j] >> 16);
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float a, b, c, d;
-      fp8x2_to_f32<false>(v[j], a, b);
-      fp8x2_to_f32<true>(v[j], c, d);
-      out[4 * j + 0] = (double)a * sc;
-      out[4 * j + 1] = (double)b * sc;
-      out[4 * j + 2] = (double)c * sc;
-      out[4 * j + 3] = (double)d * sc;
+      for (int j = 0; j < 4; ++j) {
+        float a, b, c, d;
+        fp8x2_to_f32<false>(v[j], a, b);
+        fp8x2_to_f32<true>(v[j], c, d);
+        out[4 * j + 0] = (double)a * sc;
+        out[4 * j + 1] = (double)b * sc;
+        out[4 * j + 2] = (double)c * sc;
+        out[4 * j + 3] = (double)d * sc;
+      }
     }
   }
-}
+};
 
 // Sum of key rows [s0, s1) in float64, one workgroup of 256 threads; thread
-// (rl, dg) takes rows rl, rl+16, ... and dims [8dg, 8dg+8). Result lands in
-// red[0][*] ... the caller reads column sums from `red`.
+// (rl, dg) takes rows rl, rl + RL, ... and one 16-byte slice of dims. Four rows
+// per thread are loaded before any is added, so the loads overlap. Column sums
+// are left in red[r][d] (r < RL) for the caller to add up.
 template <bool FP8>
-__device__ __forceinline__ void sum_rows_f64(const void* K, const float* kscale, int s0, int s1,
+struct RowSum {
+  static constexpr int DPT = KeySlice<FP8>::DPT;
+  static constexpr int NG = kHeadDim / DPT;  // slices per key
+  static constexpr int RL = 256 / NG;        // rows in flight per pass
+  static __device__ __forceinline__ void run(const void* K, const float* kscale, int s0, int s1,
                                              double (*red)[kHeadDim]) {
-  const int tid = threadIdx.x, dg = tid & 15, rl = tid >> 4;
-  double acc[8];
+    const int tid = threadIdx.x, dg = tid % NG, rl = tid / NG;
+    double acc[DPT];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-  for (int s = s0 + rl; s < s1; s += 16) {
-    double v[8];
-    load_key8_f64<FP8>(K, kscale, s, dg, v);
+    for (int e = 0; e < DPT; ++e) acc[e] = 0.0;
+    constexpr int U = 4;
+    for (int sb = s0 + rl; sb < s1; sb += RL * U) {
+      u32x4 v[U];
+      double sc[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+      for (int u = 0; u < U; ++u) {
+        const int s = sb + RL * u;
+        v[u] = u32x4{0u, 0u, 0u, 0u};
+        sc[u] = 0.0;
+        if (s < s1) {
+          v[u] = KeySlice<FP8>::load(K, s, dg);
+          if constexpr (FP8) sc[u] = (double)kscale[s];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        double x[DPT];
+        KeySlice<FP8>::widen(v[u], sc[u], x);
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) acc[e] += x[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) red[rl][dg * DPT + e] = acc[e];
+    __syncthreads();
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[rl][dg * 8 + e] = acc[e];
-  __syncthreads();
-}
+};
 
-// ksum[b,:] = sum of keys of block b = [b*B, min((b+1)*B, L)) (float64).
-// kbar (optional) = ksum / count rounded once to float32.
+// Workgroups [0, M): ksum[b,:] = sum of the keys of block b = [b*B, min((b+1)*B, L))
+// in float64, and (optional) kbar = ksum / count rounded once to float32.
+// Workgroups [M, M+T): tsum[t,:] = sum of the keys of query t's last block
+// [(M_t-1)*B, n_t), possibly partial; zero when the query sees no key.
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* kscale, int L,
-                                                    int B, double* ksum, float* kbar) {
-  __shared__ double red[16][kHeadDim];
+                                                    int B, int M, double* ksum, float* kbar,
+                                                    const int32_t* pos, double* tsum) {
+  constexpr int RL = RowSum<FP8>::RL;
+  __shared__ double red[RL][kHeadDim];
   const int b = blockIdx.x;
-  const long long s0 = (long long)b * B;
-  const int s1 = (int)(s0 + B < L ? s0 + B : L);
-  sum_rows_f64<FP8>(K, kscale, (int)s0, s1, red);
-  const int tid = threadIdx.x;
-  if (tid < kHeadDim) {
-    double s = 0.0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += red[r][tid];
-    ksum[(size_t)b * kHeadDim + tid] = s;
-    if (kbar) kbar[(size_t)b * kHeadDim + tid] = (float)(s / (double)(s1 - (int)s0));
+  int s0, s1;
+  if (b < M) {
+    s0 = (int)((long long)b * B);
+    s1 = (int)((long long)s0 + B < L ? (long long)s0 + B : L);
+  } else {
+    const int n = visible_len(pos[b - M], L);
+    const int Mt = (int)(((long long)n + B - 1) / B);
+    s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
+    s1 = n;
   }
-}
-
-// tsum[t,:] = sum of the keys of query t's last block [(M_t-1)*B, n_t)
-// (possibly partial); zero when the query sees no key.
-template <bool FP8>
-__global__ __launch_bounds__(256) void k_tail_sums(const void* K, const float* kscale, int L, int B,
-                                                   const int32_t* pos, double* tsum) {
-  __shared__ double red[16][kHeadDim];
-  const int t = blockIdx.x;
-  const int n = visible_len(pos[t], L);
-  const int Mt = (int)(((long long)n + B - 1) / B);
-  const int s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
-  sum_rows_f64<FP8>(K, kscale, s0, n, red);
+  RowSum<FP8>::run(K, kscale, s0, s1, red);
   const int tid = threadIdx.x;
   if (tid < kHeadDim) {
     double s = 0.0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += red[r][tid];
-    tsum[(size_t)t * kHeadDim + tid] = s;
+    for (int r = 0; r < RL; ++r) s += red[r][tid];
+    if (b < M) {
+      ksum[(size_t)b * kHeadDim + tid] = s;
+      if (kbar) kbar[(size_t)b * kHeadDim + tid] = (float)(s / (double)(s1 - s0));
+    } else {
+      tsum[(size_t)(b - M) * kHeadDim + tid] = s;
+    }
   }
 }
 
@@ -118,10 +139,14 @@ __global__ __launch_bounds__(256) void k_route_partial(const uint16_t* q, const 
                                                        const int32_t* pos, int H, int L, int B,
                                                        int nchunk, const double* ksum,
                                                        double* pmax, float* beta, int beta_ld) {
-  __shared__ double ks[kRouteChunk][kHeadDim];
+  // rows past the chunk's last block stay zero, so every wave can always
+  // process four rows at a time (kRouteChunk + 4 rows)
+  __shared__ double ks[kRouteChunk + 4][kHeadDim];
+  __shared__ float qs[kHeadDim][kWave];  // q[t, h, i] at qs[i][h]: lanes read consecutive words
   __shared__ double wmax[4][kWave];
   const int c = blockIdx.x, t = blockIdx.y;
-  const int tid = threadIdx.x, h = tid & 63, j = tid >> 6;
+  const int tid = threadIdx.x, h = tid & 63;
+  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int n = visible_len(pos[t], L);
   const int Mt = (int)(((long long)n + B - 1) / B);
   const int F = Mt > 0 ? Mt - 1 : 0;  // full blocks before the last one
@@ -133,25 +158,38 @@ __global__ __launch_bounds__(256) void k_route_partial(const uint16_t* q, const 
     return;
   }
   const int nb = b1 - b0;
-  for (int e = tid; e < nb * kHeadDim; e += 256) ks[e / kHeadDim][e % kHeadDim] = ksum[(size_t)b0 * kHeadDim + e];
-
-  const bool active = h < H;
-  float qf[kHeadDim];
-  if (active) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)t * H + h) * kHeadDim);
+  {
+    // stage this chunk's block sums (16 B per load, all loads issued first)
+    constexpr int U = kRouteChunk * kHeadDim / 2 / 256;
+    const f64x2* src = reinterpret_cast<const f64x2*>(ksum + (size_t)b0 * kHeadDim);
+    f64x2* dst = reinterpret_cast<f64x2*>(&ks[0][0]);
+    const int n2 = nb * kHeadDim / 2;
+    f64x2 v[U];
 #pragma unroll
-    for (int v = 0; v < kHeadDim / 8; ++v) {
-      const u32x4 x = src[v];
+    for (int u = 0; u < U; ++u) {
+      v[u] = f64x2{0.0, 0.0};
+      if (tid + 256 * u < n2) v[u] = src[tid + 256 * u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) dst[tid + 256 * u] = v[u];
+    if (tid < 4 * kHeadDim / 2) dst[kRouteChunk * kHeadDim / 2 + tid] = f64x2{0.0, 0.0};
+  }
+  {
+    // stage q[t, :, :] transposed; wave j loads dims [32j, 32j+32) of every head
+    const bool act = h < H;
+    u32x4 x[4];
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)t * H + (act ? h : 0)) * kHeadDim + 32 * j);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[v] = act ? src[v] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qf[8 * v + 2 * e] = bf16_bits_to_f32(x[e] & 0xffffu);
-        qf[8 * v + 2 * e + 1] = bf16_bits_to_f32(x[e] >> 16);
+        qs[32 * j + 8 * v + 2 * e][h] = bf16_bits_to_f32(x[v][e] & 0xffffu);
+        qs[32 * j + 8 * v + 2 * e + 1][h] = bf16_bits_to_f32(x[v][e] >> 16);
       }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kHeadDim; ++i) qf[i] = 0.f;
   }
+  const bool active = h < H;
   const double wh = active ? (double)w[(size_t)t * H + h] : 0.0;
   __syncthreads();
 
@@ -161,12 +199,11 @@ __global__ __launch_bounds__(256) void k_route_partial(const uint16_t* q, const 
   for (int bl = bl0; bl < bl1; bl += 4) {
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     const int cnt = min(4, bl1 - bl);
-#pragma unroll
+#pragma unroll 8
     for (int i = 0; i < kHeadDim; ++i) {
-      const double qd = (double)qf[i];
+      const double qd = (double)qs[i][h];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u < cnt) acc[u] = fma(qd, ks[bl + u][i], acc[u]);
+      for (int u = 0; u < 4; ++u) acc[u] = fma(qd, ks[bl + u][i], acc[u]);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -198,24 +235,50 @@ __global__ __launch_bounds__(64) void k_route_select(const uint16_t* q, const fl
                                                     const int32_t* pos, int H, int L, int B, int A,
                                                     int nchunk, const double* pmax,
                                                     const double* tsum, int32_t* heads,
-                                                    float* r_out, float* beta, int beta_ld) {
+                                                    float* r_out, float* beta, int beta_ld,
+                                                    uint16_t* qr, float* wr) {
   __shared__ double rs[kWave];
+  __shared__ double ts[kHeadDim];
   const int t = blockIdx.x, h = threadIdx.x;
   const bool active = h < H;
   const int n = visible_len(pos[t], L);
   const int Mt = (int)(((long long)n + B - 1) / B);
+  {
+    const f64x2 v = reinterpret_cast<const f64x2*>(tsum + (size_t)t * kHeadDim)[h];
+    reinterpret_cast<f64x2*>(ts)[h] = v;
+  }
+  u32x4 qv[kHeadDim / 8];
+  if (active) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)t * H + h) * kHeadDim);
+#pragma unroll
+    for (int v = 0; v < kHeadDim / 8; ++v) qv[v] = src[v];
+  }
   double m = 0.0;
-  for (int c = 0; c < nchunk; ++c) {
-    const double v = pmax[((size_t)t * nchunk + c) * kWave + h];
+  const double* pm = pmax + (size_t)t * nchunk * kWave + h;
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = pm[(size_t)(c + u) * kWave];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = v[u] > m ? v[u] : m;
+  }
+  for (; c < nchunk; ++c) {
+    const double v = pm[(size_t)c * kWave];
     m = v > m ? v : m;
   }
+  __syncthreads();
   if (Mt > 0) {
     const int cnt = n - (int)((long long)(Mt - 1) * B);
     double acc = 0.0;
     if (active) {
-      const uint16_t* qr = q + ((size_t)t * H + h) * kHeadDim;
-      const double* ts = tsum + (size_t)t * kHeadDim;
-      for (int i = 0; i < kHeadDim; ++i) acc = fma((double)bf16_bits_to_f32(qr[i]), ts[i], acc);
+#pragma unroll
+      for (int v = 0; v < kHeadDim / 8; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = fma((double)bf16_bits_to_f32(qv[v][e] & 0xffffu), ts[8 * v + 2 * e], acc);
+          acc = fma((double)bf16_bits_to_f32(qv[v][e] >> 16), ts[8 * v + 2 * e + 1], acc);
+        }
     }
     const double rho = acc / (double)cnt;
     m = rho > m ? rho : m;
@@ -235,27 +298,48 @@ __global__ __launch_bounds__(64) void k_route_select(const uint16_t* q, const fl
     const bool sel = active && rank < A;
     const uint64_t mask = wave_ballot(sel);
     if (sel) heads[(size_t)t * A + lanes_below(mask)] = h;
+    if (qr) {
+      // the routed q rows and weights, packed in slot order for the scoring kernel
+      if (sel) {
+        const int j = lanes_below(mask);
+        wr[(size_t)t * A + j] = w[(size_t)t * H + h];
+        const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)t * H + h) * kHeadDim);
+        u32x4* dst = reinterpret_cast<u32x4*>(qr + ((size_t)t * A + j) * kHeadDim);
+#pragma unroll
+        for (int v = 0; v < kHeadDim / 8; ++v) dst[v] = src[v];
+      }
+    }
   }
+}
+
+// Pack the q rows and weights of caller-given heads in slot order; one wave
+// per (query, slot), each lane copying 4 bytes.
+__global__ __launch_bounds__(64) void k_gather_heads(const uint16_t* q, const float* w,
+                                                     const int32_t* heads, int H, int A,
+                                                     uint16_t* qr, float* wr) {
+  const int t = blockIdx.y, j = blockIdx.x, lane = threadIdx.x;
+  const int h = heads[(size_t)t * A + j];
+  const bool ok = h >= 0 && h < H;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(q + ((size_t)t * H + (ok ? h : 0)) * kHeadDim);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(qr + ((size_t)t * A + j) * kHeadDim);
+  dst[lane] = ok ? src[lane] : 0u;
+  if (lane == 0) wr[(size_t)t * A + j] = ok ? w[(size_t)t * H + h] : 0.f;
 }
 
 // -------------------------------------------------------------------------
 // Host launchers.
 
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
-                             int L, int B, double* ksum, float* kbar) {
+                             int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
+                             double* tsum) {
   const int M = (int)(((long long)L + B - 1) / B);
-  if (M == 0) return hipSuccess;
+  const int grid = M + (tsum ? T : 0);
+  if (grid == 0) return hipSuccess;
   if (fp8)
-    return cx.launch("block_sums", k_block_sums<true>, dim3(M), dim3(256), 0, K, kscale, L, B, ksum, kbar);
-  return cx.launch("block_sums", k_block_sums<false>, dim3(M), dim3(256), 0, K, kscale, L, B, ksum, kbar);
-}
-
-hipError_t launch_tail_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
-                            int L, int B, int T, const int32_t* pos, double* tsum) {
-  if (T == 0) return hipSuccess;
-  if (fp8)
-    return cx.launch("tail_sums", k_tail_sums<true>, dim3(T), dim3(256), 0, K, kscale, L, B, pos, tsum);
-  return cx.launch("tail_sums", k_tail_sums<false>, dim3(T), dim3(256), 0, K, kscale, L, B, pos, tsum);
+    return cx.launch("block_sums", k_block_sums<true>, dim3(grid), dim3(256), 0, K, kscale, L, B, M,
+                     ksum, kbar, pos, tsum);
+  return cx.launch("block_sums", k_block_sums<false>, dim3(grid), dim3(256), 0, K, kscale, L, B, M,
+                   ksum, kbar, pos, tsum);
 }
 
 int route_chunks(int L, int B) {
@@ -266,7 +350,8 @@ int route_chunks(int L, int B) {
 
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
                         int T, int H, int L, int B, int A, const double* ksum, const double* tsum,
-                        double* pmax, int32_t* heads, float* r_out, float* beta, int beta_ld) {
+                        double* pmax, int32_t* heads, float* r_out, float* beta, int beta_ld,
+                        uint16_t* qr, float* wr) {
   if (T == 0) return hipSuccess;
   const int nch = route_chunks(L, B);
   hipError_t e;
@@ -278,7 +363,13 @@ hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, 
                   H, L, B, nch, ksum, pmax, beta, beta_ld);
   if (e != hipSuccess) return e;
   return cx.launch("route_select", k_route_select, dim3(T), dim3(64), 0, q, w, pos, H, L, B, A, nch,
-                   (const double*)pmax, tsum, heads, r_out, beta, beta_ld);
+                   (const double*)pmax, tsum, heads, r_out, beta, beta_ld, qr, wr);
+}
+
+hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,
+                               const int32_t* heads, int T, int H, int A, uint16_t* qr, float* wr) {
+  if (T == 0) return hipSuccess;
+  return cx.launch("gather_heads", k_gather_heads, dim3(A, T), dim3(64), 0, q, w, heads, H, A, qr, wr);
 }
 
 }  // namespace misa

@@ -22,11 +22,14 @@ constexpr int kLdsStride = kHeadDim + 8;  // bf16 per key row in LDS (16 B pad)
 
 template <int AP, int WR, int RPW, int CPW, bool FP8, bool GATHER>
 __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
+  // key tiles in flight per workgroup (fewer when the row tiles use many registers)
+  constexpr int R = (RPW >= 4 && !FP8) ? 2 : 4;
   constexpr int WC = 4 / WR;
   constexpr int ROWS = WR * RPW * 16;
   constexpr int QW = ROWS / AP;                     // queries per workgroup
   constexpr int KT = WC * CPW * 16;                 // keys per LDS tile
   constexpr int TPQ = AP >= 16 ? AP / 16 : 1;       // row tiles per query
+  constexpr int NQ = RPW / TPQ;                     // query slots per lane
   constexpr int CH_PER_ROW = FP8 ? 8 : 16;          // 16-byte global chunks per key row
   constexpr int CHUNKS = KT * CH_PER_ROW / 256;     // chunks per thread per tile
   static_assert(AP >= 4 && (AP & (AP - 1)) == 0, "AP must be a power of two >= 4");
@@ -40,11 +43,14 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   __shared__ int kkey[2][KT];
   __shared__ int qn[QW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / WC, wc = wave % WC;
   const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
   const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
 
+  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (long long i = tid; i < p.zero_n; i += 256) p.zero[i] = 0u;
   if (tid < QW) {
     const int t = g * QW + tid;
     int nn = 0;
@@ -58,48 +64,18 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   const int ntiles = (nmax + KT - 1) / KT;
   const int tile0 = split * p.tiles_per_split;
   const int tile1 = min(ntiles, tile0 + p.tiles_per_split);
-  if (tile0 >= tile1) return;  // uniform over the workgroup
-
-  // ---- A operand (gathered q rows) and epilogue weights, kept in registers.
-  bf16x8 afrag[RPW][4];
-  float wv[RPW][4];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int rt = wr * RPW + r;
-    {
-      const int row = rt * 16 + (lane & 15);
-      const int qi = row / AP, j = row % AP, t = g * QW + qi;
-      int h = -1;
-      if (t < p.T && j < p.A) h = p.heads ? p.heads[(size_t)t * p.A + j] : j;
-      if (h >= p.H) h = -1;  // out-of-range head ids score nothing
-      if (h >= 0) {
-        const bf16x8* src = reinterpret_cast<const bf16x8*>(
-            p.q + ((size_t)t * p.H + h) * kHeadDim + 32 * (lane >> 4));
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = src[ks];
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = bf16x8{};
-      }
+  if (tile0 >= tile1) {  // uniform over the workgroup
+    if (!GATHER && p.rmm && tid < QW && g * QW + tid < p.T) {
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2] = 0xffffffffu;  // empty range
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2 + 1] = 0u;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rt * 16 + 4 * (lane >> 4) + i;
-      const int qi = row / AP, j = row % AP, t = g * QW + qi;
-      float wvv = 0.f;
-      if (t < p.T && j < p.A) {
-        const int h = p.heads ? p.heads[(size_t)t * p.A + j] : j;
-        if (h >= 0 && h < p.H) wvv = p.w[(size_t)t * p.H + h];
-      }
-      wv[r][i] = wvv;
-    }
+    return;
   }
 
-  // ---- staging of one key tile: global -> registers -> LDS
-  u32x4 stage[CHUNKS];
-  uint32_t stage_flip[CHUNKS];  // fp8: 0x80008000 when the key's scale is negative
-  float stage_sc = 0.f;
-  int stage_key = -1;
+  // ---- staging of key tiles: global -> registers (R tiles in flight) -> LDS
+  u32x4 stage[R][CHUNKS];
+  float stage_sc[R];
+  int stage_key[R];
   const int qt0 = g * QW;  // gather: the single query
 
   auto key_of = [&](int tile, int kr) -> int {
@@ -111,120 +87,427 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
     }
   };
 
-  auto load_tile = [&](int tile) {
+  auto load_tile = [&](int tile, int rr) {
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int c = tid + 256 * u;
       const int kr = c / CH_PER_ROW, part = c % CH_PER_ROW;
       const int s = key_of(tile, kr);
-      stage_flip[u] = 0u;
       if (s >= 0) {
         const uint8_t* base = reinterpret_cast<const uint8_t*>(p.K) +
                               (size_t)s * (FP8 ? kHeadDim : 2 * kHeadDim) + 16 * part;
-        stage[u] = *reinterpret_cast<const u32x4*>(base);
-        if constexpr (FP8) stage_flip[u] = p.kscale[s] < 0.f ? 0x80008000u : 0u;
+        stage[rr][u] = *reinterpret_cast<const u32x4*>(base);
       } else {
-        stage[u] = u32x4{0u, 0u, 0u, 0u};
+        stage[rr][u] = u32x4{0u, 0u, 0u, 0u};
       }
     }
     if (tid < KT) {
-      stage_key = key_of(tile, tid);
-      stage_sc = (FP8 && stage_key >= 0) ? fabsf(p.kscale[stage_key]) : 1.f;
+      stage_key[rr] = key_of(tile, tid);
+      stage_sc[rr] = (FP8 && stage_key[rr] >= 0) ? p.kscale[stage_key[rr]] : 1.f;
     }
   };
 
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int rr) {
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int c = tid + 256 * u;
       const int kr = c / CH_PER_ROW, part = c % CH_PER_ROW;
       if constexpr (FP8) {
-        // 16 e4m3 codes -> 16 bf16 (exact); fold a negative scale's sign in.
-        const uint32_t f = stage_flip[u];
+        // 16 e4m3 codes -> 16 bf16 (exact)
         u32x4 lo, hi;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          lo[2 * e] = fp8x2_to_bf16x2<false>(stage[u][e]) ^ f;
-          lo[2 * e + 1] = fp8x2_to_bf16x2<true>(stage[u][e]) ^ f;
-          hi[2 * e] = fp8x2_to_bf16x2<false>(stage[u][2 + e]) ^ f;
-          hi[2 * e + 1] = fp8x2_to_bf16x2<true>(stage[u][2 + e]) ^ f;
+          lo[2 * e] = fp8x2_to_bf16x2<false>(stage[rr][u][e]);
+          lo[2 * e + 1] = fp8x2_to_bf16x2<true>(stage[rr][u][e]);
+          hi[2 * e] = fp8x2_to_bf16x2<false>(stage[rr][u][2 + e]);
+          hi[2 * e + 1] = fp8x2_to_bf16x2<true>(stage[rr][u][2 + e]);
         }
         uint16_t* dst = &ktile[buf][kr * kLdsStride + 16 * part];
         *reinterpret_cast<u32x4*>(dst) = lo;
         *reinterpret_cast<u32x4*>(dst + 8) = hi;
       } else {
-        *reinterpret_cast<u32x4*>(&ktile[buf][kr * kLdsStride + 8 * part]) = stage[u];
+        *reinterpret_cast<u32x4*>(&ktile[buf][kr * kLdsStride + 8 * part]) = stage[rr][u];
       }
     }
     if (tid < KT) {
-      ksc[buf][tid] = stage_sc;
-      kkey[buf][tid] = stage_key;
+      ksc[buf][tid] = stage_sc[rr];
+      kkey[buf][tid] = stage_key[rr];
     }
   };
 
-  load_tile(tile0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int tile = tile0; tile < tile1; ++tile) {
-    const int cur = (tile - tile0) & 1;
-    const bool more = tile + 1 < tile1;
-    if (more) load_tile(tile + 1);
-
-    // ---- MFMA: acc[r][c] = q rows (r) x 16 keys (c), K = 128 in 4 steps
-    f32x4 acc[RPW][CPW];
+  // ---- A operand (q rows of the scored heads) and epilogue weights, kept in
+  // registers; issued before the key stream.
+  bf16x8 afrag[RPW][4];
+  float wv[RPW][4];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int col = (wc * CPW + c) * 16 + (lane & 15);
-      const bf16x8* bsrc =
-          reinterpret_cast<const bf16x8*>(&ktile[cur][col * kLdsStride + 32 * (lane >> 4)]);
+  for (int r = 0; r < RPW; ++r) {
+    const int rt = wr * RPW + r;
+    {
+      const int row = rt * 16 + (lane & 15);
+      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      if (t < p.T && j < p.A) {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(
+            p.q + ((size_t)t * p.H + j) * kHeadDim + 32 * (lane >> 4));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = src[ks];
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = bf16x8{};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rt * 16 + 4 * (lane >> 4) + i;
+      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      wv[r][i] = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
+    }
+  }
+
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr)
+    if (tile0 + rr < tile1) load_tile(tile0 + rr, rr);
+
+  // per query slot of this lane: visible length, output row and score range
+  const bool writer = AP >= 16 ? (lane < 16) : (AP == 8 ? ((lane & 16) == 0) : true);
+  int q_n[NQ];
+  float* q_row[NQ];
+  float smin[NQ], smax[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const int rt0 = wr * RPW + s * TPQ;
+    const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * (lane >> 4)) / AP;
+    const int t = g * QW + qi;
+    q_n[s] = writer ? qn[qi] : 0;
+    q_row[s] = p.S + (size_t)(t < p.T ? t : 0) * p.S_ld;
+    smin[s] = __builtin_huge_valf();
+    smax[s] = -__builtin_huge_valf();
+  }
+
+  for (int tbase = tile0; tbase < tile1; tbase += R) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int tile = tbase + rr;
+      if (tile >= tile1) break;  // uniform
+      const int cur = (tile - tile0) & 1;
+      store_tile(cur, rr);
+      __syncthreads();
+      if (tile + R < tile1) load_tile(tile + R, rr);
+
+      // ---- MFMA: acc[r][c] = q rows (r) x 16 keys (c), K = 128 in 4 steps
+      f32x4 acc[RPW][CPW];
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int col = (wc * CPW + c) * 16 + (lane & 15);
+        const bf16x8* bsrc =
+            reinterpret_cast<const bf16x8*>(&ktile[cur][col * kLdsStride + 32 * (lane >> 4)]);
+        bf16x8 bfrag[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) bfrag[ks] = bsrc[ks];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[r][ks], bfrag[ks], a4, 0, 0, 0);
+          acc[r][c] = a4;
+        }
+      }
+
+      // ---- epilogue: ReLU, times w, sum over the query's head slots, times |scale|
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int colt = (wc * CPW + c) * 16 + (lane & 15);
+        float kscale = 1.f;
+        if constexpr (FP8) {
+          kscale = ksc[cur][colt];
+          // a negative scale flips the key's sign inside the ReLU (rare: uniform branch)
+          if (__builtin_amdgcn_read_exec() & wave_ballot(kscale < 0.f)) {
+            const float sgn = kscale < 0.f ? -1.f : 1.f;
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[r][c][i] *= sgn;
+            kscale = fabsf(kscale);
+          }
+        }
+        const bool valid_key = !GATHER || kkey[cur][colt] >= 0;
+        const int col = tile * KT + colt;
+#pragma unroll
+        for (int s = 0; s < NQ; ++s) {
+          const int r0 = s * TPQ;
+          float part = 0.f;
+#pragma unroll
+          for (int tq = 0; tq < TPQ; ++tq)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part += wv[r0 + tq][i] * fmaxf(acc[r0 + tq][c][i], 0.f);
+          if constexpr (AP >= 8) part += __shfl_xor(part, 16, kWave);
+          if constexpr (AP >= 16) part += __shfl_xor(part, 32, kWave);
+          if (col < q_n[s] && valid_key) {
+            const float v = part * kscale;
+            q_row[s][col] = v;
+            smin[s] = fminf(smin[s], v);
+            smax[s] = fmaxf(smax[s], v);
+          }
+        }
+      }
+    }
+  }
+
+  if (!GATHER && p.rmm) {
+    // lanes that share a query sit in one 16-lane group: reduce there
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      float lo = smin[s], hi = smax[s];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, kWave));
+        hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+      }
+      const int rt0 = wr * RPW + s * TPQ;
+      const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * (lane >> 4)) / AP;
+      const int t = g * QW + qi;
+      if (writer && (lane & 15) == 0 && t < p.T) {
+        // an empty range (no visible key here) stays {max key, 0}
+        const bool any = lo <= hi;
+        p.rmm[((size_t)split * p.T + t) * 2] = any ? score_key(lo) : 0xffffffffu;
+        p.rmm[((size_t)split * p.T + t) * 2 + 1] = any ? score_key(hi) : 0u;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode-shaped batches: every (query, head-slot) row of the workgroup fits in
+// one wave (RPW row tiles), so the waves split the keys instead of the rows and
+// each wave loads its own B fragments straight from global memory: no LDS, no
+// barriers, D groups of 16 keys in flight per wave. Lane l covers key
+// (l mod 16) of a group and head dims [32*(l/16), 32*(l/16) + 32).
+template <int AP, int RPW, bool FP8, bool GATHER>
+__global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
+  constexpr int ROWS = RPW * 16;
+  constexpr int QW = ROWS / AP;                     // queries per workgroup
+  constexpr int TPQ = AP >= 16 ? AP / 16 : 1;       // row tiles per query
+  constexpr int NQ = RPW / TPQ;                     // query slots per lane
+  constexpr int D = (RPW >= 8 && !FP8) ? 2 : 4;     // key groups in flight per wave
+  constexpr int NV = FP8 ? 2 : 4;                   // 16-byte loads per lane per group
+  constexpr int KT = 64;                            // keys per tile (4 waves x 16)
+  static_assert(AP >= 4 && (AP & (AP - 1)) == 0, "AP must be a power of two >= 4");
+  static_assert(ROWS % AP == 0 && QW >= 1, "row tiles must hold whole queries");
+  static_assert(AP < 16 || RPW % TPQ == 0, "a wave must hold whole queries");
+  static_assert(!GATHER || QW == 1, "gather mode scores one query per workgroup");
+
+  __shared__ int qn[QW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
+  const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
+
+  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (long long i = tid; i < p.zero_n; i += 256) p.zero[i] = 0u;
+  if (tid < QW) {
+    const int t = g * QW + tid;
+    int nn = 0;
+    if (t < p.T) nn = GATHER ? p.ncand[t] : visible_len(p.pos[t], p.L);
+    qn[tid] = nn;
+  }
+  __syncthreads();
+  int nmax = 0;
+#pragma unroll
+  for (int i = 0; i < QW; ++i) nmax = qn[i] > nmax ? qn[i] : nmax;
+  const int ntiles = (nmax + KT - 1) / KT;
+  const int tile0 = split * p.tiles_per_split;
+  const int tile1 = min(ntiles, tile0 + p.tiles_per_split);
+  if (tile0 >= tile1) {  // uniform over the workgroup
+    if (!GATHER && p.rmm && tid < QW && g * QW + tid < p.T) {
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2] = 0xffffffffu;  // empty range
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2 + 1] = 0u;
+    }
+    return;
+  }
+  const int ngroups = tile1 - tile0;  // this wave's groups: one per tile, key offset 16*wave
+  const int qt0 = g * QW;
+  const int kcol = lane & 15;
+  const int slice = lane >> 4;
+
+  auto key_of = [&](int gi) -> int {
+    const int col = (tile0 + gi) * KT + 16 * wave + kcol;
+    if constexpr (GATHER) {
+      return col < qn[0] ? p.cand[(size_t)qt0 * p.cand_ld + col] : -1;
+    } else {
+      return col < p.L ? col : -1;
+    }
+  };
+
+  u32x4 kv[D][NV];
+  float ksv[D];
+  int keyv[D];
+  auto load_group = [&](int gi, int slot) {
+    const int s = key_of(gi);
+    keyv[slot] = s;
+    if (s >= 0) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(
+          reinterpret_cast<const uint8_t*>(p.K) + (size_t)s * (FP8 ? kHeadDim : 2 * kHeadDim) +
+          slice * NV * 16);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) kv[slot][v] = src[v];
+      ksv[slot] = FP8 ? p.kscale[s] : 1.f;
+    } else {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) kv[slot][v] = u32x4{0u, 0u, 0u, 0u};
+      ksv[slot] = 1.f;
+    }
+  };
+
+  // ---- A operand (q rows of the scored heads) and epilogue weights, kept in
+  // registers; issued before the key stream so the first MFMA waits on one
+  // round trip only.
+  bf16x8 afrag[RPW][4];
+  float wv[RPW][4];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    {
+      const int row = r * 16 + (lane & 15);
+      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      if (t < p.T && j < p.A) {
+        const bf16x8* src = reinterpret_cast<const bf16x8*>(
+            p.q + ((size_t)t * p.H + j) * kHeadDim + 32 * slice);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = src[ks];
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = bf16x8{};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r * 16 + 4 * slice + i;
+      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      wv[r][i] = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
+    }
+  }
+
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < ngroups) load_group(d, d);
+
+  const bool writer = AP >= 16 ? (lane < 16) : (AP == 8 ? ((lane & 16) == 0) : true);
+  int q_n[NQ];
+  float* q_row[NQ];
+  float smin[NQ], smax[NQ];
+#pragma unroll
+  for (int s = 0; s < NQ; ++s) {
+    const int rt0 = s * TPQ;
+    const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * slice) / AP;
+    const int t = g * QW + qi;
+    q_n[s] = writer ? qn[qi] : 0;
+    q_row[s] = p.S + (size_t)(t < p.T ? t : 0) * p.S_ld;
+    smin[s] = __builtin_huge_valf();
+    smax[s] = -__builtin_huge_valf();
+  }
+
+  for (int gb = 0; gb < ngroups; gb += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int gi = gb + d;
+      if (gi >= ngroups) break;  // uniform
+      // B fragments for the four K steps (fp8 codes widen exactly to bf16)
       bf16x8 bfrag[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bfrag[ks] = bsrc[ks];
+      for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (FP8) {
+          const uint32_t w0 = kv[d][ks >> 1][(ks & 1) * 2], w1 = kv[d][ks >> 1][(ks & 1) * 2 + 1];
+          u32x4 b;
+          b[0] = fp8x2_to_bf16x2<false>(w0);
+          b[1] = fp8x2_to_bf16x2<true>(w0);
+          b[2] = fp8x2_to_bf16x2<false>(w1);
+          b[3] = fp8x2_to_bf16x2<true>(w1);
+          bfrag[ks] = __builtin_bit_cast(bf16x8, b);
+        } else {
+          bfrag[ks] = __builtin_bit_cast(bf16x8, kv[d][ks]);
+        }
+      }
+      float kscale = ksv[d];
+      const int key = keyv[d];
+      const int col = (tile0 + gi) * KT + 16 * wave + kcol;
+      if (gi + D < ngroups) load_group(gi + D, d);
+
+      f32x4 acc[RPW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[r][ks], bfrag[ks], a4, 0, 0, 0);
-        acc[r][c] = a4;
+        acc[r] = a4;
       }
-    }
-
-    // ---- epilogue: ReLU, times w, sum over the query's head slots
+      if constexpr (FP8) {
+        // a negative scale flips the key's sign inside the ReLU (rare: uniform branch)
+        if (wave_ballot(kscale < 0.f)) {
+          const float sgn = kscale < 0.f ? -1.f : 1.f;
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int colt = (wc * CPW + c) * 16 + (lane & 15);
-      const float kscale = FP8 ? ksc[cur][colt] : 1.f;
-      const int key = kkey[cur][colt];
+          for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int r0 = 0; r0 < RPW; r0 += TPQ) {
+            for (int i = 0; i < 4; ++i) acc[r][i] *= sgn;
+          kscale = fabsf(kscale);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+        const int r0 = s * TPQ;
         float part = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < TPQ; ++rr) {
+        for (int tq = 0; tq < TPQ; ++tq)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part += wv[r0 + rr][i] * fmaxf(acc[r0 + rr][c][i], 0.f);
-        }
+          for (int i = 0; i < 4; ++i) part += wv[r0 + tq][i] * fmaxf(acc[r0 + tq][i], 0.f);
         if constexpr (AP >= 8) part += __shfl_xor(part, 16, kWave);
         if constexpr (AP >= 16) part += __shfl_xor(part, 32, kWave);
-        const int rt0 = wr * RPW + r0;
-        const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * (lane >> 4)) / AP;
-        const bool writer = AP >= 16 ? (lane < 16) : (AP == 8 ? ((lane & 16) == 0) : true);
-        const int t = g * QW + qi;
-        const int col = tile * KT + colt;
-        if (writer && col < qn[qi] && key >= 0) {
-          p.S[(size_t)t * p.S_ld + col] = part * kscale;
+        if (col < q_n[s] && (!GATHER || key >= 0)) {
+          const float v = part * kscale;
+          q_row[s][col] = v;
+          smin[s] = fminf(smin[s], v);
+          smax[s] = fmaxf(smax[s], v);
         }
       }
     }
+  }
 
-    if (more) store_tile(cur ^ 1);
+  if (!GATHER && p.rmm) {
+    // per query: lanes of one wave reduce, then the four waves meet in LDS
+    __shared__ float rlo[4][QW], rhi[4][QW];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      float lo = smin[s], hi = smax[s];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, off, kWave));
+        hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
+      }
+      const int rt0 = s * TPQ;
+      const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * slice) / AP;
+      if (writer && (lane & 15) == 0) {
+        rlo[wave][qi] = lo;
+        rhi[wave][qi] = hi;
+      }
+    }
     __syncthreads();
+    if (tid < QW && g * QW + tid < p.T) {
+      float lo = rlo[0][tid], hi = rhi[0][tid];
+#pragma unroll
+      for (int w2 = 1; w2 < 4; ++w2) {
+        lo = fminf(lo, rlo[w2][tid]);
+        hi = fmaxf(hi, rhi[w2][tid]);
+      }
+      const bool any = lo <= hi;
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2] = any ? score_key(lo) : 0xffffffffu;
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2 + 1] = any ? score_key(hi) : 0u;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host side: pick an instantiation for the padded head count and batch.
+
+int score_max_splits() { return 2048; }
 
 static int pad_heads(int A) {
   int ap = 4;
@@ -233,75 +516,142 @@ static int pad_heads(int A) {
 }
 
 template <int AP, int WR, int RPW, int CPW, bool GATHER>
-static hipError_t run_score(const LaunchCtx& cx, ScoreArgs a, bool fp8, const char* name) {
+static hipError_t run_score(const LaunchCtx& cx, ScoreArgs a, bool fp8, const char* name,
+                            int* nsplit_out) {
   constexpr int WC = 4 / WR;
   constexpr int QW = WR * RPW * 16 / AP;
   constexpr int KT = WC * CPW * 16;
-  const long long max_cols = GATHER ? a.cand_ld : (long long)a.L;
+  const long long max_cols = GATHER ? (long long)a.cand_max : (long long)a.L;
   const int tiles = (int)((max_cols + KT - 1) / KT);
   int groups, splits;
+  const int target = a.target_wgs > 0 ? a.target_wgs : 2048;
   if (GATHER) {
     groups = a.T;
-    // aim for ~2048 workgroups in total, at least 2 tiles each
-    splits = (2048 + groups - 1) / groups;
+    // aim for `target` workgroups in total, at least 2 tiles each
+    splits = (target + groups - 1) / groups;
     splits = splits > (tiles + 1) / 2 ? (tiles + 1) / 2 : splits;
   } else {
     groups = (a.T + QW - 1) / QW;
-    splits = (2048 + groups - 1) / groups;
-    splits = splits > (tiles + 3) / 4 ? (tiles + 3) / 4 : splits;
+    const int min_tiles = a.target_wgs > 0 ? 1 : 4;
+    splits = (target + groups - 1) / groups;
+    splits = splits > (tiles + min_tiles - 1) / min_tiles ? (tiles + min_tiles - 1) / min_tiles : splits;
   }
   if (splits < 1) splits = 1;
   a.tiles_per_split = (tiles + splits - 1) / splits;
   splits = (tiles + a.tiles_per_split - 1) / a.tiles_per_split;
   if (splits < 1) splits = 1;
   a.ngroups = groups;
+  a.nsplit = splits;
+  if (nsplit_out) *nsplit_out = splits;
   dim3 grid = GATHER ? dim3(splits, groups) : dim3(groups, splits);
   if (fp8) return cx.launch(name, k_score<AP, WR, RPW, CPW, true, GATHER>, grid, dim3(256), 0, a);
   return cx.launch(name, k_score<AP, WR, RPW, CPW, false, GATHER>, grid, dim3(256), 0, a);
 }
 
-hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8) {
+template <int AP, int RPW, bool GATHER>
+static hipError_t run_direct(const LaunchCtx& cx, ScoreArgs a, bool fp8, const char* name,
+                             int* nsplit_out) {
+  constexpr int QW = RPW * 16 / AP;
+  constexpr int KT = 64;
+  const long long max_cols = GATHER ? (long long)a.cand_max : (long long)a.L;
+  const int tiles = (int)((max_cols + KT - 1) / KT);
+  const int groups = GATHER ? a.T : (a.T + QW - 1) / QW;
+  const int target = a.target_wgs > 0 ? a.target_wgs : 512;
+  int splits = (target + groups - 1) / groups;
+  const int min_tiles = a.target_wgs > 0 ? 1 : 4;  // four 16-key groups per wave by default
+  if (splits > (tiles + min_tiles - 1) / min_tiles) splits = (tiles + min_tiles - 1) / min_tiles;
+  if (splits < 1) splits = 1;
+  a.tiles_per_split = (tiles + splits - 1) / splits;
+  splits = (tiles + a.tiles_per_split - 1) / a.tiles_per_split;
+  if (splits < 1) splits = 1;
+  a.ngroups = groups;
+  a.nsplit = splits;
+  if (nsplit_out) *nsplit_out = splits;
+  const dim3 grid = GATHER ? dim3(splits, groups) : dim3(groups, splits);
+  if (fp8) return cx.launch(name, k_score_direct<AP, RPW, true, GATHER>, grid, dim3(256), 0, a);
+  return cx.launch(name, k_score_direct<AP, RPW, false, GATHER>, grid, dim3(256), 0, a);
+}
+
+// Row tiles (of 16 rows) that cover every query of a decode batch in one wave.
+static int direct_rpw(long long rows) {
+  if (rows <= 16) return 1;
+  if (rows <= 32) return 2;
+  if (rows <= 64) return 4;
+  if (rows <= 128) return 8;
+  return 0;  // too many rows for one wave: use the LDS-tiled kernel
+}
+
+hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* nsplit_out) {
   if (a.T == 0) return hipSuccess;
   const int ap = pad_heads(a.A);
   const long long rows = (long long)a.T * ap;
   // Prefill-like batches (many queries whose prefixes grow) go heavy-first.
   a.reverse = 1;
+  const int rpw = direct_rpw(rows);
+  const char* nm = "score_keys";
+  if (rpw > 0 && (ap < 16 || rpw * 16 >= ap)) {
+    switch (ap) {
+      case 4:
+        if (rpw == 1) return run_direct<4, 1, false>(cx, a, fp8, nm, nsplit_out);
+        if (rpw == 2) return run_direct<4, 2, false>(cx, a, fp8, nm, nsplit_out);
+        if (rpw == 4) return run_direct<4, 4, false>(cx, a, fp8, nm, nsplit_out);
+        return run_direct<4, 8, false>(cx, a, fp8, nm, nsplit_out);
+      case 8:
+        if (rpw == 1) return run_direct<8, 1, false>(cx, a, fp8, nm, nsplit_out);
+        if (rpw == 2) return run_direct<8, 2, false>(cx, a, fp8, nm, nsplit_out);
+        if (rpw == 4) return run_direct<8, 4, false>(cx, a, fp8, nm, nsplit_out);
+        return run_direct<8, 8, false>(cx, a, fp8, nm, nsplit_out);
+      case 16:
+        if (rpw == 1) return run_direct<16, 1, false>(cx, a, fp8, nm, nsplit_out);
+        if (rpw == 2) return run_direct<16, 2, false>(cx, a, fp8, nm, nsplit_out);
+        if (rpw == 4) return run_direct<16, 4, false>(cx, a, fp8, nm, nsplit_out);
+        return run_direct<16, 8, false>(cx, a, fp8, nm, nsplit_out);
+      case 32:
+        if (rpw <= 2) return run_direct<32, 2, false>(cx, a, fp8, nm, nsplit_out);
+        if (rpw == 4) return run_direct<32, 4, false>(cx, a, fp8, nm, nsplit_out);
+        return run_direct<32, 8, false>(cx, a, fp8, nm, nsplit_out);
+      default:
+        if (rpw <= 4) return run_direct<64, 4, false>(cx, a, fp8, nm, nsplit_out);
+        return run_direct<64, 8, false>(cx, a, fp8, nm, nsplit_out);
+    }
+  }
   switch (ap) {
     case 4:
-      if (rows <= 64) return run_score<4, 4, 1, 4, false>(cx, a, fp8, "score_keys");
-      if (rows <= 128) return run_score<4, 4, 2, 4, false>(cx, a, fp8, "score_keys");
-      return run_score<4, 4, 4, 4, false>(cx, a, fp8, "score_keys");
+      if (rows <= 64) return run_score<4, 4, 1, 4, false>(cx, a, fp8, nm, nsplit_out);
+      if (rows <= 128) return run_score<4, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
+      return run_score<4, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
     case 8:
-      if (rows <= 64) return run_score<8, 4, 1, 4, false>(cx, a, fp8, "score_keys");
-      if (rows <= 128) return run_score<8, 4, 2, 4, false>(cx, a, fp8, "score_keys");
-      return run_score<8, 4, 4, 4, false>(cx, a, fp8, "score_keys");
+      if (rows <= 64) return run_score<8, 4, 1, 4, false>(cx, a, fp8, nm, nsplit_out);
+      if (rows <= 128) return run_score<8, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
+      return run_score<8, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
     case 16:
-      if (rows <= 64) return run_score<16, 4, 1, 4, false>(cx, a, fp8, "score_keys");
-      if (rows <= 128) return run_score<16, 4, 2, 4, false>(cx, a, fp8, "score_keys");
-      return run_score<16, 4, 4, 4, false>(cx, a, fp8, "score_keys");
+      if (rows <= 64) return run_score<16, 4, 1, 4, false>(cx, a, fp8, nm, nsplit_out);
+      if (rows <= 128) return run_score<16, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
+      return run_score<16, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
     case 32:
-      if (rows <= 128) return run_score<32, 4, 2, 4, false>(cx, a, fp8, "score_keys");
-      return run_score<32, 4, 4, 4, false>(cx, a, fp8, "score_keys");
+      if (rows <= 128) return run_score<32, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
+      return run_score<32, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
     default:
-      return run_score<64, 4, 4, 4, false>(cx, a, fp8, "score_keys");
+      return run_score<64, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
   }
 }
 
 hipError_t launch_score_gather(const LaunchCtx& cx, ScoreArgs a, bool fp8) {
   if (a.T == 0) return hipSuccess;
   a.reverse = 0;
-  a.heads = nullptr;
+  a.rmm = nullptr;
   a.A = a.H;
   const int ap = pad_heads(a.H);
+  const char* nm = "score_gather";
   switch (ap) {
     case 4:
     case 8:
     case 16:
-      return run_score<16, 1, 1, 1, true>(cx, a, fp8, "score_gather");
+      return run_direct<16, 1, true>(cx, a, fp8, nm, nullptr);
     case 32:
-      return run_score<32, 1, 2, 1, true>(cx, a, fp8, "score_gather");
+      return run_direct<32, 2, true>(cx, a, fp8, nm, nullptr);
     default:
-      return run_score<64, 1, 4, 1, true>(cx, a, fp8, "score_gather");
+      return run_direct<64, 4, true>(cx, a, fp8, nm, nullptr);
   }
 }
 
