@@ -74,10 +74,10 @@ struct Bump {
 struct Plan {
   size_t ksum = 0, tsum = 0, pmax = 0, heads = 0, beta = 0, qr = 0, wr = 0;
   size_t S = 0;
-  size_t rmm = 0, ghist = 0, done = 0, rkeys = 0, ridx = 0, rcnt = 0, gkeys = 0, gidx = 0;
+  size_t rmm = 0, ghist = 0, rec = 0, gcnt = 0, off = 0, eqb = 0, bkeys = 0, bpos = 0;
   size_t cand = 0, ncand = 0, S2 = 0, blocks = 0, nblocks = 0;
   long long S_ld = 0, cand_ld = 0, S2_ld = 0, beta_ld = 0;
-  long long zero_words = 0;  // ghist + done, cleared by the first kernel that needs them
+  long long zero_words = 0;  // ghist, cleared by the first kernel that needs it
   int Mmax = 0, mm = 0;
   size_t total = 0;
 };
@@ -92,21 +92,21 @@ static void plan_long(Bump& bp, Plan& pl, int rows, int max_n) {
   const size_t nmm = nch > (size_t)score_max_splits() ? nch : (size_t)score_max_splits();
   // one set of scratch serves every selection of a call (they run in order)
   pl.rmm = bp.take(nmm * rows * 2 * 4);
-  pl.zero_words = (long long)rows * topk_coarse_bins() + rows;
+  pl.zero_words = (long long)rows * topk_coarse_bins();
   pl.ghist = bp.take((size_t)pl.zero_words * 4);
-  pl.done = pl.ghist + (size_t)rows * topk_coarse_bins() * 4;
-  pl.rkeys = bp.take((size_t)rows * rld * 4);
-  pl.ridx = bp.take((size_t)rows * rld * 4);
-  pl.rcnt = bp.take((size_t)rows * nch * 4);
-  pl.gkeys = bp.take((size_t)rows * rld * 4);
-  pl.gidx = bp.take((size_t)rows * rld * 4);
+  pl.rec = bp.take((size_t)rows * topk_long_rec_bytes());
+  pl.gcnt = bp.take((size_t)rows * nch * 4);
+  pl.off = bp.take((size_t)rows * nch * 4);
+  pl.eqb = bp.take((size_t)rows * nch * 4);
+  pl.bkeys = bp.take((size_t)rows * rld * 4);
+  pl.bpos = bp.take((size_t)rows * rld * 4);
 }
 
 static void plan_route(Bump& bp, Plan& pl, const misa_problem* p) {
   const int M = ceil_div(p->L, p->B);
   pl.ksum = bp.take((size_t)M * 128 * 8);
   pl.tsum = bp.take((size_t)p->T * 128 * 8);
-  pl.pmax = bp.take((size_t)p->T * route_chunks(p->L, p->B) * 64 * 8);
+  pl.pmax = bp.take((size_t)p->T * (route_chunks(p->L, p->B) + 1) * 64 * 8);  // tile maxima + last block
 }
 
 static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, int m) {
@@ -189,7 +189,7 @@ static misa_status check_problem(const misa_problem* p, bool need_queries) {
     return fail(MISA_ERR_INVALID_ARG, "k_dtype = %d is not a misa_kdtype", p->k_dtype);
   if (p->d != kHeadDimHost) return fail(MISA_ERR_UNSUPPORTED, "d = %d (only d = 128 is supported)", p->d);
   if (p->H > 64) return fail(MISA_ERR_UNSUPPORTED, "H = %d (at most 64 heads are supported)", p->H);
-  if (p->L > (1 << 28)) return fail(MISA_ERR_UNSUPPORTED, "L = %d exceeds 2^28 keys", p->L);
+  if (p->L > (1 << 23)) return fail(MISA_ERR_UNSUPPORTED, "L = %d exceeds 2^23 keys", p->L);
   if (p->T > (1 << 24)) return fail(MISA_ERR_UNSUPPORTED, "T = %d exceeds 2^24 queries", p->T);
   if (!p->K) return fail(MISA_ERR_INVALID_ARG, "K is NULL");
   if (!aligned(p->K, 16)) return fail(MISA_ERR_INVALID_ARG, "K must be 16-byte aligned");
@@ -252,13 +252,13 @@ static TopkLongWs long_ws(const Plan& pl, void* ws, int nmm) {
   TopkLongWs lw;
   lw.rmm = at<uint32_t>(ws, pl.rmm);
   lw.nmm = nmm;
-  lw.done = at<uint32_t>(ws, pl.done);
   lw.ghist = at<uint32_t>(ws, pl.ghist);
-  lw.rkeys = at<uint32_t>(ws, pl.rkeys);
-  lw.ridx = at<int32_t>(ws, pl.ridx);
-  lw.rcnt = at<int32_t>(ws, pl.rcnt);
-  lw.gkeys = at<uint32_t>(ws, pl.gkeys);
-  lw.gidx = at<int32_t>(ws, pl.gidx);
+  lw.rec = at<void>(ws, pl.rec);
+  lw.gcnt = at<int32_t>(ws, pl.gcnt);
+  lw.off = at<int32_t>(ws, pl.off);
+  lw.eqb = at<int32_t>(ws, pl.eqb);
+  lw.bkeys = at<uint32_t>(ws, pl.bkeys);
+  lw.bpos = at<int32_t>(ws, pl.bpos);
   return lw;
 }
 

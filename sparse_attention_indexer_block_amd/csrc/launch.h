@@ -55,6 +55,7 @@ inline long long padded_ld(long long n) { return ((n + 63) / 64) * 64; }
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
                              double* tsum);
+// Router tiles of 16 blocks; the pmax workspace holds T * (route_chunks + 1) * 64 doubles.
 int route_chunks(int L, int B);
 // Router: heads[T,A] (ascending), optional r[T,H], optional HISA block scores
 // beta, and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed
@@ -121,27 +122,30 @@ struct TopkArgs {
 // Rows no longer than `cap` elements: one workgroup per row in LDS.
 int topk_lds_cap();
 hipError_t launch_topk_rows(const LaunchCtx& cx, const TopkArgs& a, int max_n);
-// Long rows: histogram + filter over many workgroups, then per-row selection.
-// Workspace of the long-row path; every [rows, *] array has row stride
-// topk_long_chunks(max_n) * topk_long_chunk().
+// Long rows: coarse histogram, threshold bin, exact rank inside that bin, and
+// ordered emission, each pass spread over many workgroups. Every [rows, *]
+// array below has row stride topk_long_chunks(max_n) (per chunk) or
+// topk_long_chunks(max_n) * topk_long_chunk() (per item).
 struct TopkLongWs {
   const uint32_t* rmm; // [nmm, rows, 2] row key ranges written by the scoring kernel
   int nmm;
-  uint32_t* done;      // [rows] completion counters (zero on entry)
-  uint32_t* ghist;     // [rows, 4096] (zero on entry)
-  uint32_t* rkeys;     // [rows, stride] candidate keys (one region per chunk)
-  int32_t* ridx;       // [rows, stride] candidate indices
-  int32_t* rcnt;       // [rows, nchunk]
-  uint32_t* gkeys;     // [rows, stride] ordered copy when candidates overflow LDS
-  int32_t* gidx;       // [rows, stride]
+  uint32_t* ghist;     // [rows, topk_coarse_bins()] (zero on entry)
+  void* rec;           // [rows] per-row records of topk_long_rec_bytes()
+  int32_t* gcnt;       // [rows, nchunk] items above the threshold bin
+  int32_t* off;        // [rows, nchunk] kept items above tau before each chunk
+  int32_t* eqb;        // [rows, nchunk] items equal to tau before each chunk
+  uint32_t* bkeys;     // [rows, stride] threshold-bin keys
+  int32_t* bpos;       // [rows, stride] their positions
 };
 int topk_long_chunks(int max_n);
 int topk_long_chunk();
+int topk_long_max_chunks();
+size_t topk_long_rec_bytes();
 int topk_coarse_bins();
 hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLongWs& ws,
                             int max_n);
 // Rows whose key range is not known yet: per-chunk ranges into rmm_out
-// [topk_long_chunks(max_n), rows, 2] (and ghist/done cleared).
+// [topk_long_chunks(max_n), rows, 2] (and `zero` cleared).
 hipError_t launch_topk_range(const LaunchCtx& cx, const TopkArgs& a, uint32_t* rmm_out,
                              uint32_t* zero, long long zero_n, int max_n);
 

@@ -126,188 +126,226 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
 }
 
 // -------------------------------------------------------------------------
-// Router over the full blocks that precede each query's last block.
-// grid (nchunk, T), 256 threads: lane = head h, wave j takes a contiguous
-// quarter of this chunk's blocks. Writes, per (t, chunk, h), the largest
-// block sum . q[t,h] floored at zero, divided by B (= max_b ReLU(rho)).
-// With WITH_BETA it also writes the HISA block score
-// beta(t,b) = sum_h w[t,h] ReLU(rho(t,h,b)) of every full block.
-constexpr int kRouteChunk = 32;  // blocks per workgroup
+// Router scores rho(t,h,b) = q[t,h] . Kbar_b as float64 matrix products.
+// grid (ntiles, ceil(T / QG)), 256 threads: tile c holds blocks
+// [16c, 16c + 16), staged once in LDS and kept in registers for QG queries; wave w takes heads [16w, 16w + 16). One v_mfma_f64_16x16x4 step
+// takes four head dims; lane l feeds head (A) and block (B) l % 16 with dims
+// [32(l/16), 32(l/16) + 32), one per step, so its operands are contiguous.
+// The result D[row][col] sits at lane col + 16 * (row % 4), element row / 4.
+// Writes, per (t, tile, h), max over the tile's full blocks of ReLU(rho)
+// (zero for tiles past the query's blocks); the tile holding query t's last
+// (possibly partial) block also writes that block's rho to ptail[t, h]. With
+// WITH_BETA it writes the HISA block score beta(t,b) = sum_h w[t,h] ReLU(rho)
+// of every visible block.
+constexpr int kRouteTile = 16;  // blocks per workgroup
 
-template <bool WITH_BETA>
-__global__ __launch_bounds__(256) void k_route_partial(const uint16_t* q, const float* w,
-                                                       const int32_t* pos, int H, int L, int B,
-                                                       int nchunk, const double* ksum,
-                                                       double* pmax, float* beta, int beta_ld) {
-  // rows past the chunk's last block stay zero, so every wave can always
-  // process four rows at a time (kRouteChunk + 4 rows)
-  __shared__ double ks[kRouteChunk + 4][kHeadDim];
-  __shared__ float qs[kHeadDim][kWave];  // q[t, h, i] at qs[i][h]: lanes read consecutive words
-  __shared__ double wmax[4][kWave];
-  const int c = blockIdx.x, t = blockIdx.y;
-  const int tid = threadIdx.x, h = tid & 63;
-  const int j = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int n = visible_len(pos[t], L);
-  const int Mt = (int)(((long long)n + B - 1) / B);
-  const int F = Mt > 0 ? Mt - 1 : 0;  // full blocks before the last one
-  const int b0 = c * kRouteChunk;
-  const int b1 = min(b0 + kRouteChunk, F);
-  double* out = pmax + ((size_t)t * nchunk + c) * kWave;
-  if (b0 >= b1) {
-    if (tid < kWave) out[tid] = 0.0;
-    return;
-  }
-  const int nb = b1 - b0;
-  {
-    // stage this chunk's block sums (16 B per load, all loads issued first)
-    constexpr int U = kRouteChunk * kHeadDim / 2 / 256;
-    const f64x2* src = reinterpret_cast<const f64x2*>(ksum + (size_t)b0 * kHeadDim);
-    f64x2* dst = reinterpret_cast<f64x2*>(&ks[0][0]);
-    const int n2 = nb * kHeadDim / 2;
-    f64x2 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v[u] = f64x2{0.0, 0.0};
-      if (tid + 256 * u < n2) v[u] = src[tid + 256 * u];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) dst[tid + 256 * u] = v[u];
-    if (tid < 4 * kHeadDim / 2) dst[kRouteChunk * kHeadDim / 2 + tid] = f64x2{0.0, 0.0};
-  }
-  {
-    // stage q[t, :, :] transposed; wave j loads dims [32j, 32j+32) of every head
-    const bool act = h < H;
-    u32x4 x[4];
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)t * H + (act ? h : 0)) * kHeadDim + 32 * j);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) x[v] = act ? src[v] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qs[32 * j + 8 * v + 2 * e][h] = bf16_bits_to_f32(x[v][e] & 0xffffu);
-        qs[32 * j + 8 * v + 2 * e + 1][h] = bf16_bits_to_f32(x[v][e] >> 16);
-      }
-  }
-  const bool active = h < H;
-  const double wh = active ? (double)w[(size_t)t * H + h] : 0.0;
-  __syncthreads();
+// max over the 16 lanes of each row of the wave (every lane gets its row's max)
+template <int CTRL>
+__device__ __forceinline__ double dpp_max(double v) {
+  const int2 b = __builtin_bit_cast(int2, v);
+  int2 o;
+  o.x = __builtin_amdgcn_update_dpp(0, b.x, CTRL, 0xf, 0xf, false);
+  o.y = __builtin_amdgcn_update_dpp(0, b.y, CTRL, 0xf, 0xf, false);
+  const double ov = __builtin_bit_cast(double, o);
+  return ov > v ? ov : v;
+}
+__device__ __forceinline__ double row_max16(double v) {
+  v = dpp_max<0x121>(v);  // row_ror:1
+  v = dpp_max<0x122>(v);  // row_ror:2
+  v = dpp_max<0x124>(v);  // row_ror:4
+  return dpp_max<0x128>(v);  // row_ror:8
+}
 
-  const int per = (nb + 3) / 4;
-  const int bl0 = j * per, bl1 = min(nb, bl0 + per);
-  double m = 0.0;
-  for (int bl = bl0; bl < bl1; bl += 4) {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    const int cnt = min(4, bl1 - bl);
-#pragma unroll 8
-    for (int i = 0; i < kHeadDim; ++i) {
-      const double qd = (double)qs[i][h];
+template <bool WITH_BETA, int kRouteQG>
+__global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const float* w,
+                                                    const int32_t* pos, int T, int H, int L, int B,
+                                                    int ntiles, const double* ksum,
+                                                    const double* tsum, double* pmax,
+                                                    double* ptail, float* beta, int beta_ld) {
+  __shared__ f64x2 kt[kRouteTile][kHeadDim / 2 + 1];  // padded rows
+  __shared__ double bsum[4][kRouteTile];
+  const int tile = blockIdx.x, tq0 = blockIdx.y * kRouteQG;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int M = (int)(((long long)L + B - 1) / B);
+  const int b0 = tile * kRouteTile;
+  const int blk = b0 + col;
+  const int h_a = kRouteTile * wv + col;  // head fed by this lane's A operand
+  // per query of the group: visible blocks and the A operand (32 bf16 dims)
+  int n_q[kRouteQG], mt_q[kRouteQG];
+  u32x4 qv[kRouteQG][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[u] = fma(qd, ks[bl + u][i], acc[u]);
+  for (int i = 0; i < kRouteQG; ++i) {
+    const int t = tq0 + i;
+    n_q[i] = t < T ? visible_len(pos[t], L) : 0;
+    const bool ok = t < T && h_a < H;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)(ok ? t : 0) * H + (ok ? h_a : 0)) * kHeadDim + 32 * g);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) qv[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
+  }
+  {
+    // stage the tile's block sums (16 KB): four 16-byte loads per thread
+    f64x2 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u, r = i >> 6, c2 = i & 63;
+      x[u] = b0 + r < M ? reinterpret_cast<const f64x2*>(ksum + (size_t)(b0 + r) * kHeadDim)[c2] : f64x2{0.0, 0.0};
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (u < cnt) {
-        m = acc[u] > m ? acc[u] : m;
-        if constexpr (WITH_BETA) {
-          const double rho = acc[u] / (double)B;
-          const double contrib = active ? wh * (rho > 0.0 ? rho : 0.0) : 0.0;
-          const double s = wave_sum(contrib);
-          if (h == 0) beta[(size_t)t * beta_ld + b0 + bl + u] = (float)s;
-        }
-      }
+      const int i = tid + 256 * u;
+      kt[i >> 6][i & 63] = x[u];
     }
   }
-  wmax[j][h] = m;
   __syncthreads();
-  if (tid < kWave) {
-    double mm = wmax[0][tid];
+  f64x2 kv[16];
 #pragma unroll
-    for (int jj = 1; jj < 4; ++jj) mm = wmax[jj][tid] > mm ? wmax[jj][tid] : mm;
-    out[tid] = mm / (double)B;
+  for (int v = 0; v < 16; ++v) kv[v] = kt[col][16 * g + v];
+
+#pragma unroll
+  for (int i = 0; i < kRouteQG; ++i) {
+    const int t = tq0 + i;
+    if (t >= T) break;  // uniform
+    const int n = n_q[i];
+    const int Mt = (int)(((long long)n + B - 1) / B);
+    double* pm = pmax + ((size_t)t * ntiles + tile) * kWave;
+    if (b0 >= Mt) {  // uniform: no block of this tile is visible
+      if (tid < kWave) pm[tid] = 0.0;
+      continue;
+    }
+    const bool valid = blk < Mt;
+    const bool tail = blk == Mt - 1;
+    // B operand: the block sums, or this query's own sum for its last block
+    f64x2 kb[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) kb[v] = valid ? kv[v] : f64x2{0.0, 0.0};
+    if (tail) {
+      const f64x2* src = reinterpret_cast<const f64x2*>(tsum + (size_t)t * kHeadDim + 32 * g);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) kb[v] = src[v];
+    }
+    // two accumulation chains (even and odd dims) keep the matrix unit busy
+    f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int s = 0; s < 32; s += 2) {
+      const uint32_t word = qv[i][s >> 3][(s >> 1) & 3];
+      const double a0 = (double)bf16_bits_to_f32(word & 0xffffu);
+      const double a1 = (double)bf16_bits_to_f32(word >> 16);
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, kb[s >> 1][0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, kb[s >> 1][1], acc1, 0, 0, 0);
+    }
+    const f64x4 acc = acc0 + acc1;
+    // this lane holds heads 16 wv + 4 e + g (e = 0..3) against block blk
+    const double cnt = tail ? (double)(n - (Mt - 1) * B) : (double)B;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0);
+      if (col == 0) pm[kRouteTile * wv + 4 * e + g] = m / (double)B;
+    }
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ptail[(size_t)t * kWave + kRouteTile * wv + 4 * e + g] = acc[e] / cnt;
+    }
+    if constexpr (WITH_BETA) {
+      double part = 0.0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int hh = kRouteTile * wv + 4 * e + g;
+        const double rho = acc[e] / cnt;
+        part += (hh < H && rho > 0.0) ? (double)w[(size_t)t * H + hh] * rho : 0.0;
+      }
+      part += __shfl_xor(part, 16, kWave);
+      part += __shfl_xor(part, 32, kWave);
+      if (lane < kRouteTile) bsum[wv][lane] = part;
+      __syncthreads();
+      if (tid < kRouteTile && b0 + tid < Mt) {
+        const double s = bsum[0][tid] + bsum[1][tid] + bsum[2][tid] + bsum[3][tid];
+        beta[(size_t)t * beta_ld + b0 + tid] = (float)s;
+      }
+      __syncthreads();
+    }
   }
 }
 
-// Final router step, one wave per query: fold in the query's last (possibly
-// partial) block, form r(t,h) = w[t,h] * max_b ReLU(rho), and keep the first A
-// heads under (-r, h). heads[t,:] is written in ascending head order.
-__global__ __launch_bounds__(64) void k_route_select(const uint16_t* q, const float* w,
-                                                    const int32_t* pos, int H, int L, int B, int A,
-                                                    int nchunk, const double* pmax,
-                                                    const double* tsum, int32_t* heads,
-                                                    float* r_out, float* beta, int beta_ld,
-                                                    uint16_t* qr, float* wr) {
+// Final router step, 256 threads per query: r(t,h) = w[t,h] * max_b ReLU(rho)
+// over the tile maxima and the last block, then the first A heads under
+// (-r, h). heads[t,:] is written in ascending head order; with qr the routed q
+// rows and weights are packed in the same order for the scoring kernel. Every
+// global read is issued up front (none depends on another).
+__global__ __launch_bounds__(256) void k_route_select(const uint16_t* q, const float* w,
+                                                     const int32_t* pos, int H, int L, int B, int A,
+                                                     int ntiles, const double* pmax,
+                                                     const double* ptail, int32_t* heads,
+                                                     float* r_out, uint16_t* qr, float* wr) {
+  __shared__ double part[4][kWave];
   __shared__ double rs[kWave];
-  __shared__ double ts[kHeadDim];
-  const int t = blockIdx.x, h = threadIdx.x;
-  const bool active = h < H;
+  __shared__ int rank_part[4][kWave];
+  __shared__ u32x4 qs[kWave * kHeadDim / 8];  // q[t] as 16-byte words
+  const int t = blockIdx.x, tid = threadIdx.x, h = tid & 63, j = tid >> 6;
   const int n = visible_len(pos[t], L);
-  const int Mt = (int)(((long long)n + B - 1) / B);
-  {
-    const f64x2 v = reinterpret_cast<const f64x2*>(tsum + (size_t)t * kHeadDim)[h];
-    reinterpret_cast<f64x2*>(ts)[h] = v;
-  }
-  u32x4 qv[kHeadDim / 8];
-  if (active) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)t * H + h) * kHeadDim);
+  const bool active = h < H;
+  const float wt = active ? w[(size_t)t * H + h] : 0.f;
+  const double rho_tail = ptail[(size_t)t * kWave + h];
+  if (qr) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + (size_t)t * H * kHeadDim);
+    const int nw = H * kHeadDim / 8;
 #pragma unroll
-    for (int v = 0; v < kHeadDim / 8; ++v) qv[v] = src[v];
+    for (int u = 0; u < 4; ++u)
+      if (tid + 256 * u < nw) qs[tid + 256 * u] = src[tid + 256 * u];
   }
+  const double* pm = pmax + (size_t)t * ntiles * kWave + h;
   double m = 0.0;
-  const double* pm = pmax + (size_t)t * nchunk * kWave + h;
-  int c = 0;
-  for (; c + 8 <= nchunk; c += 8) {
-    double v[8];
+  constexpr int U = 16;
+  for (int c0 = j; c0 < ntiles; c0 += 4 * U) {
+    double v[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = pm[(size_t)(c + u) * kWave];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      v[u] = c < ntiles ? pm[(size_t)c * kWave] : 0.0;
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) m = v[u] > m ? v[u] : m;
+    for (int u = 0; u < U; ++u) m = v[u] > m ? v[u] : m;
   }
-  for (; c < nchunk; ++c) {
-    const double v = pm[(size_t)c * kWave];
-    m = v > m ? v : m;
+  part[j][h] = m;
+  __syncthreads();
+  const int Mt = (int)(((long long)n + B - 1) / B);
+  double r = 0.0;
+  if (j == 0) {
+    m = part[0][h];
+#pragma unroll
+    for (int jj = 1; jj < 4; ++jj) m = part[jj][h] > m ? part[jj][h] : m;
+    if (Mt > 0) m = rho_tail > m ? rho_tail : m;
+    r = active ? (double)wt * m + 0.0 : -__builtin_huge_val();
+    if (r_out && active) r_out[(size_t)t * H + h] = (float)r;
+    rs[h] = r;
   }
   __syncthreads();
-  if (Mt > 0) {
-    const int cnt = n - (int)((long long)(Mt - 1) * B);
-    double acc = 0.0;
-    if (active) {
+  if (!heads) return;
+  {
+    // rank of head h: wave j compares it with heads [16j, 16j + 16)
+    const double rh = rs[h];
+    double r2[16];
 #pragma unroll
-      for (int v = 0; v < kHeadDim / 8; ++v)
+    for (int u = 0; u < 16; ++u) r2[u] = rs[16 * j + u];
+    int c = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc = fma((double)bf16_bits_to_f32(qv[v][e] & 0xffffu), ts[8 * v + 2 * e], acc);
-          acc = fma((double)bf16_bits_to_f32(qv[v][e] >> 16), ts[8 * v + 2 * e + 1], acc);
-        }
-    }
-    const double rho = acc / (double)cnt;
-    m = rho > m ? rho : m;
-    if (beta) {
-      const double contrib = active ? (double)w[(size_t)t * H + h] * (rho > 0.0 ? rho : 0.0) : 0.0;
-      const double s = wave_sum(contrib);
-      if (h == 0) beta[(size_t)t * beta_ld + Mt - 1] = (float)s;
-    }
+    for (int u = 0; u < 16; ++u) c += (r2[u] > rh) || (r2[u] == rh && 16 * j + u < h);
+    rank_part[j][h] = c;
   }
-  const double r = active ? (double)w[(size_t)t * H + h] * m + 0.0 : -__builtin_huge_val();
-  if (r_out && active) r_out[(size_t)t * H + h] = (float)r;
-  if (heads) {
-    rs[h] = r;
-    __syncthreads();
-    int rank = 0;
-    for (int h2 = 0; h2 < kWave; ++h2) rank += (rs[h2] > r) || (rs[h2] == r && h2 < h);
-    const bool sel = active && rank < A;
-    const uint64_t mask = wave_ballot(sel);
-    if (sel) heads[(size_t)t * A + lanes_below(mask)] = h;
+  __syncthreads();
+  if (j != 0) return;
+  const int rank = rank_part[0][h] + rank_part[1][h] + rank_part[2][h] + rank_part[3][h];
+  const bool sel = active && rank < A;
+  const uint64_t mask = wave_ballot(sel);
+  if (sel) {
+    const int slot = lanes_below(mask);
+    heads[(size_t)t * A + slot] = h;
     if (qr) {
-      // the routed q rows and weights, packed in slot order for the scoring kernel
-      if (sel) {
-        const int j = lanes_below(mask);
-        wr[(size_t)t * A + j] = w[(size_t)t * H + h];
-        const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)t * H + h) * kHeadDim);
-        u32x4* dst = reinterpret_cast<u32x4*>(qr + ((size_t)t * A + j) * kHeadDim);
+      wr[(size_t)t * A + slot] = wt;
+      u32x4* dst = reinterpret_cast<u32x4*>(qr + ((size_t)t * A + slot) * kHeadDim);
 #pragma unroll
-        for (int v = 0; v < kHeadDim / 8; ++v) dst[v] = src[v];
-      }
+      for (int v = 0; v < kHeadDim / 8; ++v) dst[v] = qs[h * (kHeadDim / 8) + v];
     }
   }
 }
@@ -344,7 +382,7 @@ hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* ks
 
 int route_chunks(int L, int B) {
   const int M = (int)(((long long)L + B - 1) / B);
-  const int c = (M + kRouteChunk - 1) / kRouteChunk;
+  const int c = (M + kRouteTile - 1) / kRouteTile;
   return c < 1 ? 1 : c;
 }
 
@@ -353,17 +391,29 @@ hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, 
                         double* pmax, int32_t* heads, float* r_out, float* beta, int beta_ld,
                         uint16_t* qr, float* wr) {
   if (T == 0) return hipSuccess;
-  const int nch = route_chunks(L, B);
+  const int nt = route_chunks(L, B);
+  double* ptail = pmax + (size_t)T * nt * kWave;
   hipError_t e;
-  if (beta)
-    e = cx.launch("route_partial", k_route_partial<true>, dim3(nch, T), dim3(256), 0, q, w, pos, H,
-                  L, B, nch, ksum, pmax, beta, beta_ld);
+  // one query per workgroup while that still leaves few workgroups per CU;
+  // past that, pairs of queries share each staged tile
+  const bool pair = (long long)nt * T > 2048;
+  const dim3 grid(nt, pair ? (T + 1) / 2 : T);
+  if (beta && pair)
+    e = cx.launch("route_mfma", k_route_mfma<true, 2>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
+                  ksum, tsum, pmax, ptail, beta, beta_ld);
+  else if (beta)
+    e = cx.launch("route_mfma", k_route_mfma<true, 1>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
+                  ksum, tsum, pmax, ptail, beta, beta_ld);
+  else if (pair)
+    e = cx.launch("route_mfma", k_route_mfma<false, 2>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
+                  ksum, tsum, pmax, ptail, beta, beta_ld);
   else
-    e = cx.launch("route_partial", k_route_partial<false>, dim3(nch, T), dim3(256), 0, q, w, pos,
-                  H, L, B, nch, ksum, pmax, beta, beta_ld);
+    e = cx.launch("route_mfma", k_route_mfma<false, 1>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
+                  ksum, tsum, pmax, ptail, beta, beta_ld);
   if (e != hipSuccess) return e;
-  return cx.launch("route_select", k_route_select, dim3(T), dim3(64), 0, q, w, pos, H, L, B, A, nch,
-                   (const double*)pmax, tsum, heads, r_out, beta, beta_ld, qr, wr);
+  if (!heads && !r_out) return hipSuccess;  // block scores only
+  return cx.launch("route_select", k_route_select, dim3(T), dim3(256), 0, q, w, pos, H, L, B, A, nt,
+                   (const double*)pmax, (const double*)ptail, heads, r_out, qr, wr);
 }
 
 hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,

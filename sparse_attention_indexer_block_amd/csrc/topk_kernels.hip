@@ -11,21 +11,35 @@
 // index and the output is deterministic.
 //
 // Rows that fit in LDS are handled by one workgroup each. Longer rows are split
-// over many workgroups: a histogram pass (bins spread between the row's
-// smallest and largest key, which the scoring kernel reports), then a pass
-// that keeps each chunk's items at or above the threshold bin in index order;
-// the last workgroup of a row to finish gathers the survivors and selects.
+// over many workgroups: a coarse histogram (bins spread between the row's
+// smallest and largest key, which the scoring kernel reports) locates the
+// threshold bin; only that bin's items are ranked exactly; every chunk then
+// writes its kept items at an offset from a per-chunk prefix count.
 #include "device_common.h"
 #include "launch.h"
 
 namespace misa {
 
 constexpr int kLdsCap = 16384;     // items per row selected inside LDS
-constexpr int kLongChunk = 8192;   // items per workgroup in the long-row passes
+constexpr int kChunk = 4096;       // items per workgroup in the long-row passes
+constexpr int kMaxChunks = 2048;   // chunks per long row (rows up to 2^23 items)
+constexpr int kResolveCap = 16384; // boundary-bin items resolved inside LDS
 constexpr int kCoarseBits = 12;
-constexpr int kCoarseBins = 1 << kCoarseBits;
+constexpr int kCoarseBins = 1 << kCoarseBits;  // long rows: bins of the first pass
+constexpr int kFineBins = 2048;                  // rows in one workgroup
 constexpr int kListCap = 4096;     // survivors of the first radix digit kept in LDS
 constexpr int kRankCap = 128;      // lists this short are ranked pairwise instead of by digits
+
+template <int NT>
+struct RegShared {
+  static constexpr int NW = NT / kWave;
+  uint32_t red[NW][8];
+  uint32_t wmin[NW], wmax[NW];
+  int wgt[NW], weq[NW];
+  uint32_t umin, umax;
+  uint32_t base;
+  int rem;
+};
 
 template <int NT>
 struct TopkShared {
@@ -43,9 +57,22 @@ struct TopkShared {
   uint32_t tau;
   int need;
   uint32_t list[kListCap];
+  RegShared<NT> reg;
 };
 
 __device__ __forceinline__ int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// First-pass bins are linear in the score between the row's smallest and
+// largest values (monotone in the score, so a bin holds a contiguous range of
+// keys); a zero or non-finite span puts everything in bin 0.
+__device__ __forceinline__ float lin_scale(float lo, float hi, int nb) {
+  const float span = hi - lo;
+  return (span > 0.f && span < __builtin_huge_valf()) ? (float)nb / span : 0.f;
+}
+__device__ __forceinline__ uint32_t lin_bin(uint32_t key, float lo, float scale, int nb) {
+  const float f = (key_score(key) - lo) * scale;
+  return (uint32_t)fminf(fmaxf(f, 0.f), (float)(nb - 1));
+}
 
 __device__ __forceinline__ int row_length(const TopkArgs a, int row) {
   if (a.row_n) return a.row_n[row];
@@ -439,32 +466,6 @@ __device__ __forceinline__ void load_ints(const int32_t* src, int n, int32_t* ds
   for (int i = 4 * n4 + tid; i < n; i += NT) dst[i] = src[i];
 }
 
-// One workgroup per row; the row's keys (and indices) are staged in LDS.
-template <int NT>
-__global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a, int cap) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-  __shared__ TopkShared<NT> sm;
-  const int row = blockIdx.x;
-  const int n = min(row_length(a, row), cap);
-  uint32_t* keys = dyn;
-  int32_t* idx = reinterpret_cast<int32_t*>(dyn + cap);
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  load_keys<NT, 4>(a.S + (size_t)row * a.S_ld, n, keys, lo, hi);
-  if (a.row_idx) load_ints<NT, 4>(a.row_idx + (size_t)row * a.idx_ld, n, idx);
-  block_minmax<NT>(lo, hi, sm);
-  int32_t* oi = a.out_idx + (size_t)row * a.out_ld;
-  float* os = a.out_score ? a.out_score + (size_t)row * a.out_ld : nullptr;
-  int32_t* oc = a.out_count ? a.out_count + row : nullptr;
-  auto key_at = [=](int i) { return keys[i]; };
-  if (a.row_idx) {
-    auto idx_at = [=](int i) { return idx[i]; };
-    select_row<NT>(key_at, idx_at, n, a.k, sm.umin, sm.umax, sm, oi, os, oc);
-  } else {
-    auto idx_at = [=](int i) { return i; };
-    select_row<NT>(key_at, idx_at, n, a.k, sm.umin, sm.umax, sm, oi, os, oc);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Long rows.
 
@@ -482,201 +483,593 @@ __device__ __forceinline__ void row_range(const uint32_t* rmm, int nmm, int rows
   block_minmax<NT>(lo, hi, sm);
 }
 
-__device__ __forceinline__ int range_shift(uint32_t umin, uint32_t umax) {
-  const uint32_t span = umax - umin;
-  const int bits = span ? 32 - __clz(span) : 0;
-  return bits > kCoarseBits ? bits - kCoarseBits : 0;
+
+// ---------------------------------------------------------------------------
+// Long rows: five short passes, each spread over many workgroups.
+//   hist    (chunk, row): coarse histogram of (key - umin) >> shift into ghist
+//   bin     (row)       : threshold bin b* holding the k-th largest, and the
+//                         rank rem of the k-th item inside it
+//   count   (chunk, row): items above b* per chunk; items inside b* appended
+//                         to the row's boundary list (key, position)
+//   resolve (row)       : exact k-th key tau and the number need_eq of items
+//                         equal to tau that are kept; per-chunk output offsets
+//   emit    (chunk, row): every chunk writes its kept items, in position
+//                         order, at its offset
+// Positions are indices inside the row; with row_idx the emitted index is
+// row_idx[position].
+
+struct LongRec {
+  float xlo;       // smallest score of the row
+  float scale;     // bin = lin_bin(key, xlo, scale, kCoarseBins)
+  uint32_t bstar;  // threshold bin
+  uint32_t rem;    // rank of the k-th item inside the threshold bin (1-based)
+  uint32_t tau;    // k-th largest key
+  uint32_t need;   // items equal to tau that are kept (lowest positions first)
+  uint32_t bcount; // boundary list length
+  uint32_t pad;
+};
+
+__device__ __forceinline__ uint32_t coarse_bin(uint32_t u, float xlo, float scale) {
+  return lin_bin(u, xlo, scale, kCoarseBins);
 }
 
-// grid (nchunk, rows): histogram of (key - umin) >> shift, summed in ghist.
+// Keys of items [s0 + 4*j, s0 + 4*j + 4) of a row (j-th group of four), with
+// positions past s1 marked absent. Row starts are 16-byte aligned.
+__device__ __forceinline__ void load_group4(const float* row, int s0, int s1, int j, uint32_t u[4],
+                                            bool in[4]) {
+  const int s = s0 + 4 * j;
+  if (s + 4 <= s1) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(row + s);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u[e] = score_key(v[e]);
+      in[e] = true;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      in[e] = s + e < s1;
+      u[e] = in[e] ? score_key(row[s + e]) : 0u;
+    }
+  }
+}
+
+// Workgroup layout of a chunk in the count and emit passes: wave w owns the
+// contiguous items [w * kChunk / NW, (w + 1) * kChunk / NW); its g-th group of
+// four items at lane l starts at item 4 * (l + 64 * g) of that range.
+constexpr int kLongNT = 256;
+constexpr int kGroups = kChunk / 4 / kLongNT;  // groups of four items per lane
+
 template <int NT>
-__global__ __launch_bounds__(NT) void k_topk_hist(TopkArgs a, const uint32_t* rmm, int nmm,
+__global__ __launch_bounds__(NT) void k_long_hist(TopkArgs a, const uint32_t* rmm, int nmm,
                                                   uint32_t* ghist) {
   __shared__ uint32_t lh[kCoarseBins];
   __shared__ TopkShared<NT> sm;
-  const int row = blockIdx.y, chunk = blockIdx.x;
+  const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int n = row_length(a, row);
-  const int s0 = chunk * kLongChunk, s1 = min(n, s0 + kLongChunk);
-  if (s0 >= s1) return;
-  row_range<NT>(rmm, nmm, a.rows, row, sm);
-  const uint32_t umin = sm.umin;
-  const int sh = range_shift(umin, sm.umax);
-  for (int b = threadIdx.x; b < kCoarseBins; b += NT) lh[b] = 0u;
-  __syncthreads();
-  constexpr int U = kLongChunk / 4 / NT;
-  const f32x4* s4 = reinterpret_cast<const f32x4*>(a.S + (size_t)row * a.S_ld + s0);
-  const int m4 = (s1 - s0) >> 2;
-  f32x4 v[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = u * NT + threadIdx.x;
-    if (j < m4) v[u] = s4[j];
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = u * NT + threadIdx.x;
-    if (j < m4) {
-      atomicAdd(&lh[(score_key(v[u][0]) - umin) >> sh], 1u);
-      atomicAdd(&lh[(score_key(v[u][1]) - umin) >> sh], 1u);
-      atomicAdd(&lh[(score_key(v[u][2]) - umin) >> sh], 1u);
-      atomicAdd(&lh[(score_key(v[u][3]) - umin) >> sh], 1u);
-    }
-  }
+  const int s0 = chunk * kChunk, s1 = min(n, s0 + kChunk);
+  if (s0 >= s1 || a.k >= n) return;  // uniform
+  // keys first, the row range (a reduction over the scoring splits) meanwhile
   const float* src = a.S + (size_t)row * a.S_ld;
-  for (int i = s0 + 4 * m4 + threadIdx.x; i < s1; i += NT) atomicAdd(&lh[(score_key(src[i]) - umin) >> sh], 1u);
+  uint32_t u[kGroups][4];
+  bool in[kGroups][4];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) load_group4(src, s0, s1, g * NT + tid, u[g], in[g]);
+  for (int b = tid; b < kCoarseBins; b += NT) lh[b] = 0u;
+  row_range<NT>(rmm, nmm, a.rows, row, sm);
+  const float xlo = key_score(sm.umin), scale = lin_scale(xlo, key_score(sm.umax), kCoarseBins);
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (in[g][e]) atomicAdd(&lh[coarse_bin(u[g][e], xlo, scale)], 1u);
   __syncthreads();
   uint32_t* gh = ghist + (size_t)row * kCoarseBins;
-  for (int b = threadIdx.x; b < kCoarseBins; b += NT)
-    if (lh[b]) atomicAdd(&gh[b], lh[b]);
+  for (int b = tid; b < kCoarseBins; b += NT) {
+    const uint32_t c = lh[b];
+    if (c) atomicAdd(&gh[b], c);
+  }
 }
 
-// grid (nchunk, rows): keep, in index order, this chunk's items whose bin is
-// at or above the row's threshold bin (everything when k >= n); the last
-// workgroup of the row to finish gathers all survivors in chunk order and
-// selects the top-k.
+// One workgroup per row: the threshold bin, from the finished histogram. Also
+// clears the row's boundary list counter for the count pass.
 template <int NT>
-__global__ __launch_bounds__(NT) void k_topk_filter_select(TopkArgs a, const uint32_t* rmm, int nmm,
-                                                          const uint32_t* ghist, uint32_t* rkeys,
-                                                          int32_t* ridx, int32_t* rcnt,
-                                                          uint32_t* done, int nchunk, long long rld,
-                                                          uint32_t* gkeys, int32_t* gidx, int cap) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+__global__ __launch_bounds__(NT) void k_long_bin(TopkArgs a, const uint32_t* rmm, int nmm,
+                                                 const uint32_t* ghist, LongRec* rec) {
   __shared__ TopkShared<NT> sm;
-  __shared__ int coff[1025];
-  constexpr int NW = TopkShared<NT>::NW;
-  const int row = blockIdx.y, chunk = blockIdx.x;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int row = blockIdx.x;
   const int n = row_length(a, row);
+  if (a.k >= n) return;  // take everything: no threshold
   row_range<NT>(rmm, nmm, a.rows, row, sm);
-  const uint32_t umin = sm.umin, umax = sm.umax;
-  const int sh = range_shift(umin, umax);
-  uint32_t bstar = 0u;
-  if (a.k < n) {
-    // the row histogram, staged in LDS after the chunk area
-    uint32_t* gh = dyn + kLongChunk;
-    const u32x4* src = reinterpret_cast<const u32x4*>(ghist + (size_t)row * kCoarseBins);
-    for (int i = tid; i < kCoarseBins / 4; i += NT) reinterpret_cast<u32x4*>(gh)[i] = src[i];
-    __syncthreads();
-    find_bin<NT>(gh, kCoarseBins, a.k, sm);
-    bstar = (uint32_t)sm.digit;
+  const float xlo = key_score(sm.umin), scale = lin_scale(xlo, key_score(sm.umax), kCoarseBins);
+  find_bin<NT>(ghist + (size_t)row * kCoarseBins, kCoarseBins, a.k, sm);
+  if (threadIdx.x == 0) {
+    LongRec r{};
+    r.xlo = xlo;
+    r.scale = scale;
+    r.bstar = (uint32_t)sm.digit;
+    r.rem = (uint32_t)sm.rem;
+    r.bcount = 0u;
+    rec[row] = r;
   }
-  const int s0 = chunk * kLongChunk, s1 = min(n, s0 + kLongChunk);
-  int total = 0;
-  if (s0 < s1) {
-    // stage the chunk's keys in LDS, then count and write survivors in order
-    uint32_t* ck = dyn;
-    uint32_t lo = 0u, hi = 0u;
-    const int len = s1 - s0;
-    load_keys<NT, kLongChunk / 4 / NT>(a.S + (size_t)row * a.S_ld + s0, len, ck, lo, hi);
-    __syncthreads();
-    const int seg = ceil_div_i(ceil_div_i(len, NW), kWave) * kWave;
-    const int w0 = min(len, w * seg), w1 = min(len, w0 + seg);
-    int cnt = 0;
-    for (int base = w0; base < w1; base += kWave) {
-      const int i = base + lane;
-      cnt += __popcll(wave_ballot(i < w1 && ((ck[i] - umin) >> sh) >= bstar));
+}
+
+// grid (nchunk, rows): items above the threshold bin are counted per chunk;
+// items inside it go to the row's boundary list (in no particular order).
+template <int NT>
+__global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, LongRec* rec, int32_t* gcnt, int nch,
+                                                   uint32_t* bkeys, int32_t* bpos, long long rld) {
+  __shared__ int wsum[NT / kWave];
+  const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int n = row_length(a, row);
+  const int s0 = chunk * kChunk, s1 = min(n, s0 + kChunk);
+  if (s0 >= s1 || a.k >= n) return;  // uniform
+  const float* src = a.S + (size_t)row * a.S_ld;
+  const int ws0 = s0 + w * (kChunk / (NT / kWave));
+  uint32_t u[kGroups][4];
+  bool in[kGroups][4];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) load_group4(src, ws0, s1, lane + kWave * g, u[g], in[g]);
+  const float xlo = rec[row].xlo, scale = rec[row].scale;
+  const uint32_t bstar = rec[row].bstar;
+  int above = 0, nb = 0;
+  uint64_t bm[kGroups][4];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t b = coarse_bin(u[g][e], xlo, scale);
+      above += (in[g][e] && b > bstar) ? 1 : 0;
+      bm[g][e] = wave_ballot(in[g][e] && b == bstar);
+      nb += __popcll(bm[g][e]);
     }
-    if (lane == 0) sm.wgt[w] = cnt;
-    __syncthreads();
-    int out = 0;
-    for (int i = 0; i < NW; ++i) {
-      out += i < w ? sm.wgt[i] : 0;
-      total += sm.wgt[i];
-    }
-    uint32_t* kd = rkeys + (size_t)row * rld + s0;
-    int32_t* id = ridx + (size_t)row * rld + s0;
-    for (int base = w0; base < w1; base += kWave) {
-      const int i = base + lane;
-      const uint32_t u = i < w1 ? ck[i] : 0u;
-      const bool keep = i < w1 && ((u - umin) >> sh) >= bstar;
-      const uint64_t m = wave_ballot(keep);
-      if (keep) {
-        const int p = out + lanes_below(m);
-        kd[p] = u;
-        id[p] = s0 + i;
+  if (nb) {
+    // one list reservation per wave
+    uint32_t base = 0u;
+    if (lane == 0) base = atomicAdd(&rec[row].bcount, (uint32_t)nb);
+    base = __shfl(base, 0, kWave);
+    uint32_t* kd = bkeys + (size_t)row * rld;
+    int32_t* pd = bpos + (size_t)row * rld;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((bm[g][e] >> lane) & 1ull) {
+          const uint32_t at = base + (uint32_t)lanes_below(bm[g][e]);
+          kd[at] = u[g][e];
+          pd[at] = ws0 + 4 * (lane + kWave * g) + e;
+        }
+        base += (uint32_t)__popcll(bm[g][e]);
       }
-      out += __popcll(m);
+  }
+  above = wave_sum(above);
+  if (lane == 0) wsum[w] = above;
+  __syncthreads();
+  if (tid == 0) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) s += wsum[i];
+    gcnt[(size_t)row * nch + chunk] = s;
+  }
+}
+
+// One workgroup per row: tau and need_eq from the boundary list, then per
+// chunk the number of kept items before it: off[c] counts items > tau in
+// chunks before c, eqb[c] items == tau in chunks before c.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_long_resolve(TopkArgs a, LongRec* rec, const int32_t* gcnt,
+                                                     int32_t* off, int32_t* eqb, int nch,
+                                                     const uint32_t* bkeys, const int32_t* bpos,
+                                                     long long rld) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];  // [kResolveCap] boundary keys
+  __shared__ TopkShared<NT> sm;
+  __shared__ int cgt[kMaxChunks], ceq[kMaxChunks];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int n = row_length(a, row);
+  if (a.k >= n) return;
+  const int nc = (n + kChunk - 1) / kChunk;
+  const int cb = (int)rec[row].bcount;
+  const int rem = (int)rec[row].rem;
+  const uint32_t* gk = bkeys + (size_t)row * rld;
+  const int32_t* gp = bpos + (size_t)row * rld;
+  const bool in_lds = cb <= kResolveCap;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = tid; i < cb; i += NT) {
+    const uint32_t x = gk[i];
+    if (in_lds) dyn[i] = x;
+    lo = min(lo, x);
+    hi = max(hi, x);
+  }
+  for (int c = tid; c < nc; c += NT) {
+    cgt[c] = gcnt[(size_t)row * nch + c];
+    ceq[c] = 0;
+  }
+  block_minmax<NT>(lo, hi, sm);  // synchronises
+  uint32_t tau;
+  int need_eq;
+  if (rem >= cb) {
+    // every item of the boundary bin is kept
+    tau = sm.umin;
+    need_eq = cb;
+  } else if (in_lds) {
+    auto key_at = [=](int i) { return dyn[i]; };
+    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
+  } else {
+    auto key_at = [=](int i) { return gk[i]; };
+    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
+  }
+  for (int i = tid; i < cb; i += NT) {
+    const uint32_t x = in_lds ? dyn[i] : gk[i];
+    const int c = gp[i] / kChunk;
+    if (x > tau) atomicAdd(&cgt[c], 1);
+    else if (x == tau) atomicAdd(&ceq[c], 1);
+  }
+  __syncthreads();
+  // exclusive scans over the row's chunks, NT at a time
+  int gt_run = 0, eq_run = 0;
+  for (int c0 = 0; c0 < nc; c0 += NT) {
+    const int c = c0 + tid;
+    const int g = c < nc ? cgt[c] : 0, e = c < nc ? ceq[c] : 0;
+    int gtot, etot;
+    const int gi = block_scan<NT>(g, sm, &gtot);
+    const int ei = block_scan<NT>(e, sm, &etot);
+    if (c < nc) {
+      off[(size_t)row * nch + c] = gt_run + gi - g;
+      eqb[(size_t)row * nch + c] = eq_run + ei - e;
     }
+    gt_run += gtot;
+    eq_run += etot;
   }
-  // publish this chunk and find out whether it is the row's last one
-  __syncthreads();
   if (tid == 0) {
-    rcnt[(size_t)row * nchunk + chunk] = total;
-    __threadfence();
-    const uint32_t prev = atomicAdd(&done[row], 1u);
-    sm.flag = prev == (uint32_t)(nchunk - 1);
+    rec[row].tau = tau;
+    rec[row].need = (uint32_t)need_eq;
   }
-  __syncthreads();
-  if (!sm.flag) return;
-  __threadfence();
-  // last workgroup of the row: offsets of every chunk's survivors
-  for (int c = tid; c < nchunk; c += NT)
-    coff[c + 1] = __hip_atomic_load(&rcnt[(size_t)row * nchunk + c], __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-  if (tid == 0) {
-    coff[0] = 0;
-    done[row] = 0u;  // ready for the next call
-  }
-  __syncthreads();
-  if (tid == 0)
-    for (int c = 0; c < nchunk; ++c) coff[c + 1] += coff[c];
-  __syncthreads();
-  const int C = coff[nchunk];
+}
+
+// grid (nchunk, rows): write the chunk's kept items in position order.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const int32_t* off,
+                                                  const int32_t* eqb, int nch) {
+  constexpr int NW = NT / kWave;
+  __shared__ int wgt[NW], weq[NW];
+  const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int n = row_length(a, row);
+  const bool take_all = a.k >= n;
+  const int nsel = take_all ? n : a.k;
   int32_t* oi = a.out_idx + (size_t)row * a.out_ld;
   float* os = a.out_score ? a.out_score + (size_t)row * a.out_ld : nullptr;
-  int32_t* oc = a.out_count ? a.out_count + row : nullptr;
-  // copy every chunk's survivors, in chunk order, to keys[0, C) / idx[0, C)
-  auto gather = [&](uint32_t* keys, int32_t* idx) {
-    uint32_t lo = 0xffffffffu, hi = 0u;
-    constexpr int U = 4;
-    for (int base = 0; base < C; base += NT * U) {
-      uint32_t kv[U];
-      int32_t iv[U];
+  if (chunk == 0) {
+    for (int p = nsel + tid; p < a.k; p += NT) {
+      oi[p] = -1;
+      if (os) os[p] = -__builtin_huge_valf();
+    }
+    if (a.out_count && tid == 0) a.out_count[row] = nsel;
+  }
+  const int s0 = chunk * kChunk, s1 = min(n, s0 + kChunk);
+  if (s0 >= s1) return;  // uniform
+  const float* src = a.S + (size_t)row * a.S_ld;
+  const int32_t* ri = a.row_idx ? a.row_idx + (size_t)row * a.idx_ld : nullptr;
+  const int ws0 = s0 + w * (kChunk / NW);
+  uint32_t u[kGroups][4];
+  bool in[kGroups][4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = base + u * NT + tid;
-        if (j < C) {
-          int lo_c = 0, hi_c = nchunk - 1;  // chunk c with coff[c] <= j < coff[c+1]
-          while (lo_c < hi_c) {
-            const int mid = (lo_c + hi_c + 1) >> 1;
-            if (coff[mid] <= j) lo_c = mid; else hi_c = mid - 1;
-          }
-          const size_t at = (size_t)row * rld + (size_t)lo_c * kLongChunk + (j - coff[lo_c]);
-          kv[u] = rkeys[at];
-          iv[u] = ridx[at];
+  for (int g = 0; g < kGroups; ++g) load_group4(src, ws0, s1, lane + kWave * g, u[g], in[g]);
+  if (take_all) {
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (in[g][e]) {
+          const int s = ws0 + 4 * (lane + kWave * g) + e;
+          oi[s] = ri ? ri[s] : s;
+          if (os) os[s] = key_score(u[g][e]);
         }
+    return;
+  }
+  const uint32_t tau = rec[row].tau;
+  const int need = (int)rec[row].need;
+  // per lane and group: items above tau (low half) and equal to it (high half)
+  int cnt[kGroups];
+  int tot = 0;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c += (in[g][e] && u[g][e] > tau) ? 1 : 0;
+      c += (in[g][e] && u[g][e] == tau) ? (1 << 16) : 0;
+    }
+    cnt[g] = c;
+    tot += c;
+  }
+  tot = wave_sum(tot);
+  if (lane == 0) {
+    wgt[w] = tot & 0xffff;
+    weq[w] = tot >> 16;
+  }
+  __syncthreads();
+  int gt_run = off[(size_t)row * nch + chunk], eq_run = eqb[(size_t)row * nch + chunk];
+  for (int i = 0; i < w; ++i) {
+    gt_run += wgt[i];
+    eq_run += weq[i];
+  }
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int inc = wave_inclusive_scan(cnt[g]);
+    const int exc = inc - cnt[g];
+    int gt_b = gt_run + (exc & 0xffff), eq_b = eq_run + (exc >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!in[g][e]) continue;
+      const int s = ws0 + 4 * (lane + kWave * g) + e;
+      int p = -1;
+      if (u[g][e] > tau) {
+        p = gt_b + min(eq_b, need);
+        ++gt_b;
+      } else if (u[g][e] == tau) {
+        if (eq_b < need) p = gt_b + eq_b;
+        ++eq_b;
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = base + u * NT + tid;
-        if (j < C) {
-          keys[j] = kv[u];
-          idx[j] = iv[u];
-          lo = min(lo, kv[u]);
-          hi = max(hi, kv[u]);
-        }
+      if (p >= 0 && p < a.k) {
+        oi[p] = ri ? ri[s] : s;
+        if (os) os[p] = key_score(u[g][e]);
       }
     }
-    block_minmax<NT>(lo, hi, sm);
-  };
-  if (C <= cap) {
-    uint32_t* keys = dyn;
-    int32_t* idx = reinterpret_cast<int32_t*>(dyn + cap);
-    gather(keys, idx);
-    auto key_at = [=](int i) { return keys[i]; };
-    auto idx_at = [=](int i) { return idx[i]; };
-    select_row<NT>(key_at, idx_at, C, a.k, sm.umin, sm.umax, sm, oi, os, oc);
-  } else {
-    // more survivors than LDS holds (heavy ties): select from a global copy
-    uint32_t* keys = gkeys + (size_t)row * rld;
-    int32_t* idx = gidx + (size_t)row * rld;
-    gather(keys, idx);
-    __threadfence_block();
-    __syncthreads();
-    auto key_at = [=](int i) { return keys[i]; };
-    auto idx_at = [=](int i) { return idx[i]; };
-    select_row<NT>(key_at, idx_at, C, a.k, sm.umin, sm.umax, sm, oi, os, oc);
+    const int wtot = __shfl(inc, kWave - 1, kWave);
+    gt_run += wtot & 0xffff;
+    eq_run += wtot >> 16;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Rows of up to NT * 4 * G items: one workgroup per row, keys in registers.
+// Wave w owns items [w * 256G, (w + 1) * 256G); lane l holds, for g < G, the
+// four items starting at w * 256G + 4 * (l + 64 g) (one 16-byte load each), so
+// (g, lane, element) is the items' order inside the wave.
+//
+// Threshold: 4-bit digits of the offset key v = key - umin, most significant
+// first. Each pass counts the 16 sub-ranges of the current range with packed
+// per-thread counters (no atomics), reduces them over the workgroup, and keeps
+// the sub-range that holds the rem-th largest item.
+
+
+template <int NT, int G>
+__device__ __forceinline__ void reg_threshold(const uint32_t (&u)[G][4], const bool (&in)[G][4], int k,
+                                              uint32_t umin, uint32_t umax, RegShared<NT>& sm,
+                                              uint32_t& tau, int& need_eq) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const uint32_t span = umax - umin;
+  int bits = span ? 32 - __clz(span) : 0;
+  uint32_t base = 0u;  // offset of the current range [base, base + 2^bits)
+  int rem = k;
+  while (bits > 0) {
+    const int wd = bits < 4 ? bits : 4;
+    const int sh = bits - wd;
+    uint32_t c[8];  // c[j]: count of sub-range 2j (low half), 2j + 1 (high half)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = 0u;
+#pragma unroll
+    for (int g0 = 0; g0 < G; g0 += 2) {
+      uint64_t x = 0;  // 4-bit counters: at most 8 items per round
+#pragma unroll
+      for (int g = g0; g < g0 + 2 && g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t v = u[g][e] - umin - base;
+          const bool inr = in[g][e] && (bits >= 32 || (v >> bits) == 0u);
+          x += inr ? (1ull << (4 * (v >> sh))) : 0ull;
+        }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] += (uint32_t)((x >> (8 * j)) & 0xfu) | ((uint32_t)((x >> (8 * j + 4)) & 0xfu) << 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = wave_total_u32(c[j]);
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sm.red[w][j] = c[j];
+    }
+    __syncthreads();
+    if (w == 0) {
+      // lanes 0..7 add one packed column over the waves; lane 0 walks the
+      // sub-ranges from the top
+      uint32_t col = 0u;
+      if (lane < 8)
+#pragma unroll
+        for (int i = 0; i < NW; ++i) col += sm.red[i][lane];
+      int above = 0, pick = 0, r = rem;
+#pragma unroll
+      for (int b = 15; b >= 0; --b) {
+        const uint32_t packed = (uint32_t)__builtin_amdgcn_readlane((int)col, b >> 1);
+        const int cnt = (int)((packed >> (16 * (b & 1))) & 0xffffu);
+        if (b < (1 << wd) && pick == 0 && above < r && r <= above + cnt) {
+          pick = b + 1;  // chosen sub-range, plus one
+          r -= above;
+        }
+        above += b < (1 << wd) ? cnt : 0;
+      }
+      if (lane == 0) {
+        sm.base = base + ((uint32_t)(pick > 0 ? pick - 1 : 0) << sh);
+        sm.rem = r;
+      }
+    }
+    __syncthreads();
+    base = sm.base;
+    rem = sm.rem;
+    bits = sh;
+  }
+  tau = base + umin;
+  need_eq = rem;
+}
+
+// Emit the selection in item order: items with key > tau, plus the first
+// need_eq items equal to tau (all items when take_all). Writes positions below
+// k only.
+template <int NT, int G, bool WITH_SCORE, typename IdxOf>
+__device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], const bool (&in)[G][4], int seg0,
+                                         bool take_all, uint32_t tau, int need_eq, int k,
+                                         RegShared<NT>& sm, IdxOf idx_of, int32_t* out_idx,
+                                         float* out_score) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  int cnt[G];
+  int tot = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool gt = in[g][e] && (take_all || u[g][e] > tau);
+      const bool eq = in[g][e] && !take_all && u[g][e] == tau;
+      c += (gt ? 1 : 0) + (eq ? (1 << 16) : 0);
+    }
+    cnt[g] = c;
+    tot += c;
+  }
+  tot = (int)wave_total_u32((uint32_t)tot);
+  if (lane == 0) {
+    sm.wgt[w] = tot & 0xffff;
+    sm.weq[w] = tot >> 16;
+  }
+  __syncthreads();
+  int gt_run = 0, eq_run = 0;
+  for (int i = 0; i < w; ++i) {
+    gt_run += sm.wgt[i];
+    eq_run += sm.weq[i];
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int inc = wave_inclusive_scan(cnt[g]);
+    const int exc = inc - cnt[g];
+    int gt_b = gt_run + (exc & 0xffff), eq_b = eq_run + (exc >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!in[g][e]) continue;
+      const int s = seg0 + 4 * (lane + kWave * g) + e;
+      int p = -1;
+      if (take_all || u[g][e] > tau) {
+        p = gt_b + min(eq_b, need_eq);
+        ++gt_b;
+      } else if (u[g][e] == tau) {
+        if (eq_b < need_eq) p = gt_b + eq_b;
+        ++eq_b;
+      }
+      if (p >= 0 && p < k) {
+        out_idx[p] = idx_of(g, e, s);
+        if (WITH_SCORE) out_score[p] = key_score(u[g][e]);
+      }
+    }
+    const int wt = __builtin_amdgcn_readlane(inc, kWave - 1);
+    gt_run += wt & 0xffff;
+    eq_run += wt >> 16;
+  }
+}
+
+template <int NT, int G>
+__global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
+  __shared__ TopkShared<NT> sm;
+  __shared__ uint32_t cand[kListCap];  // keys of the threshold bin
+  constexpr int NW = NT / kWave;
+  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n = min(row_length(a, row), NT * 4 * G);
+  const int seg0 = w * 256 * G;
+  const float* src = a.S + (size_t)row * a.S_ld;
+  const int32_t* ri = a.row_idx ? a.row_idx + (size_t)row * a.idx_ld : nullptr;
+  uint32_t u[G][4];
+  bool in[G][4];
+  i32x4 ix[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    load_group4(src, seg0, n, lane + kWave * g, u[g], in[g]);
+    const int s = seg0 + 4 * (lane + kWave * g);
+    if (ri && s + 4 <= n) {
+      ix[g] = *reinterpret_cast<const i32x4*>(ri + s);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ix[g][e] = (ri && s + e < n) ? ri[s + e] : s + e;
+    }
+  }
+  int32_t* oi = a.out_idx + (size_t)row * a.out_ld;
+  float* os = a.out_score ? a.out_score + (size_t)row * a.out_ld : nullptr;
+  const int k = a.k;
+  const bool take_all = k >= n;
+  uint32_t tau = 0u;
+  int need_eq = 0;
+  if (!take_all) {
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (in[g][e]) {
+          lo = min(lo, u[g][e]);
+          hi = max(hi, u[g][e]);
+        }
+    for (int b = tid; b < kFineBins; b += NT) sm.hist[b] = 0u;
+    block_minmax<NT>(lo, hi, sm);  // synchronises
+    const float xlo = key_score(sm.umin);
+    const float scale = lin_scale(xlo, key_score(sm.umax), kFineBins);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (in[g][e]) atomicAdd(&sm.hist[lin_bin(u[g][e], xlo, scale, kFineBins)], 1u);
+    __syncthreads();
+    find_bin<NT>(sm.hist, kFineBins, k, sm);
+    const uint32_t bstar = (uint32_t)sm.digit;
+    const int rem = sm.rem;
+    const int c = (int)sm.hist[bstar];
+    if (c <= kListCap) {
+      // the threshold bin's keys, in no particular order
+      if (tid == 0) sm.nlist = 0;
+      __syncthreads();
+      uint32_t clo = 0xffffffffu, chi = 0u;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = in[g][e] && lin_bin(u[g][e], xlo, scale, kFineBins) == bstar;
+          const uint64_t m = wave_ballot(keep);
+          if (m) {
+            int at = 0;
+            if (lane == 0) at = atomicAdd(&sm.nlist, __popcll(m));
+            at = __shfl(at, 0, kWave);
+            if (keep) cand[at + lanes_below(m)] = u[g][e];
+          }
+          if (keep) {
+            clo = min(clo, u[g][e]);
+            chi = max(chi, u[g][e]);
+          }
+        }
+      block_minmax<NT>(clo, chi, sm);  // synchronises (cand complete)
+      if (rem >= c) {
+        tau = sm.umin;  // the whole bin is kept
+        need_eq = c;
+      } else if (c <= kRankCap) {
+        for (int i = tid; i < c; i += NT) sm.list[i] = cand[i];
+        __syncthreads();
+        rank_in_list<NT>(c, rem, sm, tau, need_eq);
+      } else {
+        auto key_at = [&](int i) { return cand[i]; };
+        radix_threshold<NT>(key_at, c, rem, sm.umin, sm.umax, sm, tau, need_eq);
+      }
+    } else {
+      // a crowded bin (heavy ties): digit-by-digit search over every item
+      reg_threshold<NT, G>(u, in, k, sm.umin, sm.umax, sm.reg, tau, need_eq);
+    }
+  }
+  auto idx_of = [&](int g, int e, int) { return ix[g][e]; };
+  if (os) reg_emit<NT, G, true>(u, in, seg0, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
+  else reg_emit<NT, G, false>(u, in, seg0, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
+  const int nsel = take_all ? n : k;
+  for (int p = nsel + tid; p < k; p += NT) {
+    oi[p] = -1;
+    if (os) os[p] = -__builtin_huge_valf();
+  }
+  if (a.out_count && tid == 0) a.out_count[row] = nsel;
 }
 
 // grid (nchunk, rows): {min, max} score key of each chunk into rmm[chunk, row];
@@ -689,7 +1082,7 @@ __global__ __launch_bounds__(NT) void k_topk_range(TopkArgs a, uint32_t* rmm, ui
   if (zero && row == 0 && chunk == 0)
     for (long long i = threadIdx.x; i < zero_n; i += NT) zero[i] = 0u;
   const int n = row_length(a, row);
-  const int s0 = chunk * kLongChunk, s1 = min(n, s0 + kLongChunk);
+  const int s0 = chunk * kChunk, s1 = min(n, s0 + kChunk);
   uint32_t lo = 0xffffffffu, hi = 0u;
   const float* src = a.S + (size_t)row * a.S_ld;
   for (int i = s0 + threadIdx.x; i < s1; i += NT) {
@@ -749,49 +1142,51 @@ __global__ __launch_bounds__(256) void k_expand_blocks(const int32_t* blocks, co
 // Host launchers.
 
 int topk_lds_cap() { return kLdsCap; }
-int topk_long_chunk() { return kLongChunk; }
+int topk_long_chunk() { return kChunk; }
 int topk_coarse_bins() { return kCoarseBins; }
-int topk_long_chunks(int max_n) { return max_n <= 0 ? 1 : (max_n + kLongChunk - 1) / kLongChunk; }
-
-template <int NT>
-static hipError_t rows_launch(const LaunchCtx& cx, const TopkArgs& a, int cap) {
-  const size_t shmem = (size_t)cap * 4u * (a.row_idx ? 2u : 1u);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_rows<NT>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsCap * 8));
-    attr_set = true;
-  }
-  return cx.launch("topk_rows", k_topk_rows<NT>, dim3(a.rows), dim3(NT), shmem, a, cap);
-}
+int topk_long_chunks(int max_n) { return max_n <= 0 ? 1 : (max_n + kChunk - 1) / kChunk; }
+int topk_long_max_chunks() { return kMaxChunks; }
+size_t topk_long_rec_bytes() { return sizeof(LongRec); }
 
 hipError_t launch_topk_rows(const LaunchCtx& cx, const TopkArgs& a, int max_n) {
   if (a.rows == 0) return hipSuccess;
-  int cap = max_n < 64 ? 64 : ((max_n + 63) / 64) * 64;
-  if (cap > kLdsCap) cap = kLdsCap;
-  // few rows: wide workgroups; many rows (prefill): several workgroups per CU
-  if (a.rows <= 1024) return rows_launch<1024>(cx, a, cap);
-  return rows_launch<256>(cx, a, cap);
+  if (max_n > kLdsCap) return hipErrorInvalidValue;
+  const dim3 grid(a.rows);
+  if (max_n <= 1024) return cx.launch("topk_rows", k_topk_rows<256, 1>, grid, dim3(256), 0, a);
+  if (max_n <= 4096) return cx.launch("topk_rows", k_topk_rows<1024, 1>, grid, dim3(1024), 0, a);
+  if (max_n <= 8192) return cx.launch("topk_rows", k_topk_rows<1024, 2>, grid, dim3(1024), 0, a);
+  return cx.launch("topk_rows", k_topk_rows<1024, 4>, grid, dim3(1024), 0, a);
 }
 
 hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLongWs& ws, int max_n) {
   if (a.rows == 0) return hipSuccess;
   const int nch = topk_long_chunks(max_n);
-  if (nch > 1024) return hipErrorInvalidValue;
-  const long long rld = (long long)nch * kLongChunk;
-  hipError_t e = cx.launch("topk_hist", k_topk_hist<256>, dim3(nch, a.rows), dim3(256), 0, a,
-                           (const uint32_t*)ws.rmm, ws.nmm, ws.ghist);
+  if (nch > kMaxChunks) return hipErrorInvalidValue;
+  const long long rld = (long long)nch * kChunk;
+  LongRec* rec = reinterpret_cast<LongRec*>(ws.rec);
+  const dim3 grid(nch, a.rows);
+  hipError_t e = cx.launch("topk_hist", k_long_hist<kLongNT>, grid, dim3(kLongNT), 0, a, ws.rmm,
+                           ws.nmm, ws.ghist);
   if (e != hipSuccess) return e;
-  const size_t shmem = (size_t)kLdsCap * 8;
+  e = cx.launch("topk_bin", k_long_bin<1024>, dim3(a.rows), dim3(1024), 0, a, ws.rmm, ws.nmm,
+                (const uint32_t*)ws.ghist, rec);
+  if (e != hipSuccess) return e;
+  e = cx.launch("topk_count", k_long_count<kLongNT>, grid, dim3(kLongNT), 0, a, rec, ws.gcnt, nch,
+                ws.bkeys, ws.bpos, rld);
+  if (e != hipSuccess) return e;
+  const size_t shmem = (size_t)kResolveCap * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_topk_filter_select<1024>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_long_resolve<1024>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     attr_set = true;
   }
-  return cx.launch("topk_filter_select", k_topk_filter_select<1024>, dim3(nch, a.rows), dim3(1024),
-                   shmem, a, (const uint32_t*)ws.rmm, ws.nmm, (const uint32_t*)ws.ghist, ws.rkeys,
-                   ws.ridx, ws.rcnt, ws.done, nch, rld, ws.gkeys, ws.gidx, kLdsCap);
+  e = cx.launch("topk_resolve", k_long_resolve<1024>, dim3(a.rows), dim3(1024), shmem, a, rec,
+                (const int32_t*)ws.gcnt, ws.off, ws.eqb, nch, (const uint32_t*)ws.bkeys,
+                (const int32_t*)ws.bpos, rld);
+  if (e != hipSuccess) return e;
+  return cx.launch("topk_emit", k_long_emit<kLongNT>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,
+                   (const int32_t*)ws.off, (const int32_t*)ws.eqb, nch);
 }
 
 hipError_t launch_topk_range(const LaunchCtx& cx, const TopkArgs& a, uint32_t* rmm_out,
