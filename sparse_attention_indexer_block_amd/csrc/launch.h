@@ -122,18 +122,18 @@ struct TopkArgs {
 // Rows no longer than `cap` elements: one workgroup per row in LDS.
 int topk_lds_cap();
 hipError_t launch_topk_rows(const LaunchCtx& cx, const TopkArgs& a, int max_n);
-// Long rows: coarse histogram, threshold bin, exact rank inside that bin, and
-// ordered emission, each pass spread over many workgroups. Every [rows, *]
-// array below has row stride topk_long_chunks(max_n) (per chunk) or
-// topk_long_chunks(max_n) * topk_long_chunk() (per item).
+// Long rows: coarse histogram, threshold bin with per-chunk counts and the
+// bin's items, then exact rank inside that bin and ordered emission, each pass
+// spread over many workgroups. Every [rows, *] array below has row stride
+// topk_long_chunks(max_n) (per chunk) or topk_long_chunks(max_n) *
+// topk_long_chunk() (per item).
 struct TopkLongWs {
   const uint32_t* rmm; // [nmm, rows, 2] row key ranges written by the scoring kernel
   int nmm;
   uint32_t* ghist;     // [rows, topk_coarse_bins()] (zero on entry)
+  uint32_t* bcount;    // [rows] boundary list lengths (zero on entry)
   void* rec;           // [rows] per-row records of topk_long_rec_bytes()
   int32_t* gcnt;       // [rows, nchunk] items above the threshold bin
-  int32_t* off;        // [rows, nchunk] kept items above tau before each chunk
-  int32_t* eqb;        // [rows, nchunk] items equal to tau before each chunk
   uint32_t* bkeys;     // [rows, stride] threshold-bin keys
   int32_t* bpos;       // [rows, stride] their positions
 };

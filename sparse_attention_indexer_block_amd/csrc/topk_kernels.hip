@@ -23,7 +23,7 @@ namespace misa {
 constexpr int kLdsCap = 16384;     // items per row selected inside LDS
 constexpr int kChunk = 4096;       // items per workgroup in the long-row passes
 constexpr int kMaxChunks = 2048;   // chunks per long row (rows up to 2^23 items)
-constexpr int kResolveCap = 16384; // boundary-bin items resolved inside LDS
+constexpr int kBoundaryCap = 4096; // boundary-bin items resolved inside LDS
 constexpr int kCoarseBits = 12;
 constexpr int kCoarseBins = 1 << kCoarseBits;  // long rows: bins of the first pass
 constexpr int kFineBins = 2048;                  // rows in one workgroup
@@ -42,9 +42,9 @@ struct RegShared {
 };
 
 template <int NT>
-struct TopkShared {
+struct alignas(16) TopkShared {
   static constexpr int NW = NT / kWave;
-  uint32_t hist[2048];
+  alignas(16) uint32_t hist[2048];
   int wave_tot[NW];
   int wgt[NW];
   int weq[NW];
@@ -56,7 +56,7 @@ struct TopkShared {
   int nlist;
   uint32_t tau;
   int need;
-  uint32_t list[kListCap];
+  alignas(16) uint32_t list[kListCap];
   RegShared<NT> reg;
 };
 
@@ -485,16 +485,14 @@ __device__ __forceinline__ void row_range(const uint32_t* rmm, int nmm, int rows
 
 
 // ---------------------------------------------------------------------------
-// Long rows: five short passes, each spread over many workgroups.
-//   hist    (chunk, row): coarse histogram of (key - umin) >> shift into ghist
-//   bin     (row)       : threshold bin b* holding the k-th largest, and the
-//                         rank rem of the k-th item inside it
-//   count   (chunk, row): items above b* per chunk; items inside b* appended
-//                         to the row's boundary list (key, position)
-//   resolve (row)       : exact k-th key tau and the number need_eq of items
-//                         equal to tau that are kept; per-chunk output offsets
-//   emit    (chunk, row): every chunk writes its kept items, in position
-//                         order, at its offset
+// Long rows: three passes, each spread over (chunk, row) workgroups.
+//   hist  : coarse histogram of the row (bins linear in the score) into ghist
+//   count : threshold bin b* (the bin holding the k-th largest) from ghist;
+//           per chunk, the items above b*; the items inside b* appended to the
+//           row's boundary list (key, position)
+//   emit  : tau (k-th largest key) and need_eq (items equal to tau that are
+//           kept, lowest positions first) from the boundary list; kept items
+//           before the chunk; the chunk's kept items in position order
 // Positions are indices inside the row; with row_idx the emitted index is
 // row_idx[position].
 
@@ -503,10 +501,6 @@ struct LongRec {
   float scale;     // bin = lin_bin(key, xlo, scale, kCoarseBins)
   uint32_t bstar;  // threshold bin
   uint32_t rem;    // rank of the k-th item inside the threshold bin (1-based)
-  uint32_t tau;    // k-th largest key
-  uint32_t need;   // items equal to tau that are kept (lowest positions first)
-  uint32_t bcount; // boundary list length
-  uint32_t pad;
 };
 
 __device__ __forceinline__ uint32_t coarse_bin(uint32_t u, float xlo, float scale) {
@@ -543,7 +537,7 @@ constexpr int kGroups = kChunk / 4 / kLongNT;  // groups of four items per lane
 template <int NT>
 __global__ __launch_bounds__(NT) void k_long_hist(TopkArgs a, const uint32_t* rmm, int nmm,
                                                   uint32_t* ghist) {
-  __shared__ uint32_t lh[kCoarseBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kCoarseBins];
   __shared__ TopkShared<NT> sm;
   const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int n = row_length(a, row);
@@ -571,35 +565,16 @@ __global__ __launch_bounds__(NT) void k_long_hist(TopkArgs a, const uint32_t* rm
   }
 }
 
-// One workgroup per row: the threshold bin, from the finished histogram. Also
-// clears the row's boundary list counter for the count pass.
+// grid (nchunk, rows): every workgroup finds the row's threshold bin from the
+// finished histogram (the same answer in each), counts its chunk's items above
+// that bin, and appends the items inside it to the row's boundary list (in no
+// particular order). Chunk 0 records the rank rem of the k-th item in the bin.
 template <int NT>
-__global__ __launch_bounds__(NT) void k_long_bin(TopkArgs a, const uint32_t* rmm, int nmm,
-                                                 const uint32_t* ghist, LongRec* rec) {
-  __shared__ TopkShared<NT> sm;
-  const int row = blockIdx.x;
-  const int n = row_length(a, row);
-  if (a.k >= n) return;  // take everything: no threshold
-  row_range<NT>(rmm, nmm, a.rows, row, sm);
-  const float xlo = key_score(sm.umin), scale = lin_scale(xlo, key_score(sm.umax), kCoarseBins);
-  find_bin<NT>(ghist + (size_t)row * kCoarseBins, kCoarseBins, a.k, sm);
-  if (threadIdx.x == 0) {
-    LongRec r{};
-    r.xlo = xlo;
-    r.scale = scale;
-    r.bstar = (uint32_t)sm.digit;
-    r.rem = (uint32_t)sm.rem;
-    r.bcount = 0u;
-    rec[row] = r;
-  }
-}
-
-// grid (nchunk, rows): items above the threshold bin are counted per chunk;
-// items inside it go to the row's boundary list (in no particular order).
-template <int NT>
-__global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, LongRec* rec, int32_t* gcnt, int nch,
+__global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* rmm, int nmm,
+                                                   const uint32_t* ghist, uint32_t* bcount,
+                                                   LongRec* rec, int32_t* gcnt, int nch,
                                                    uint32_t* bkeys, int32_t* bpos, long long rld) {
-  __shared__ int wsum[NT / kWave];
+  __shared__ TopkShared<NT> sm;
   const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int n = row_length(a, row);
@@ -611,8 +586,18 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, LongRec* rec, int
   bool in[kGroups][4];
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) load_group4(src, ws0, s1, lane + kWave * g, u[g], in[g]);
-  const float xlo = rec[row].xlo, scale = rec[row].scale;
-  const uint32_t bstar = rec[row].bstar;
+  row_range<NT>(rmm, nmm, a.rows, row, sm);
+  const float xlo = key_score(sm.umin), scale = lin_scale(xlo, key_score(sm.umax), kCoarseBins);
+  find_bin<NT>(ghist + (size_t)row * kCoarseBins, kCoarseBins, a.k, sm);
+  const uint32_t bstar = (uint32_t)sm.digit;
+  if (chunk == 0 && tid == 0) {
+    LongRec r{};
+    r.xlo = xlo;
+    r.scale = scale;
+    r.bstar = bstar;
+    r.rem = (uint32_t)sm.rem;
+    rec[row] = r;
+  }
   int above = 0, nb = 0;
   uint64_t bm[kGroups][4];
 #pragma unroll
@@ -627,7 +612,7 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, LongRec* rec, int
   if (nb) {
     // one list reservation per wave
     uint32_t base = 0u;
-    if (lane == 0) base = atomicAdd(&rec[row].bcount, (uint32_t)nb);
+    if (lane == 0) base = atomicAdd(&bcount[row], (uint32_t)nb);
     base = __shfl(base, 0, kWave);
     uint32_t* kd = bkeys + (size_t)row * rld;
     int32_t* pd = bpos + (size_t)row * rld;
@@ -643,96 +628,28 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, LongRec* rec, int
         base += (uint32_t)__popcll(bm[g][e]);
       }
   }
-  above = wave_sum(above);
-  if (lane == 0) wsum[w] = above;
+  above = (int)wave_total_u32((uint32_t)above);
+  if (lane == 0) sm.wgt[w] = above;
   __syncthreads();
   if (tid == 0) {
     int s = 0;
 #pragma unroll
-    for (int i = 0; i < NT / kWave; ++i) s += wsum[i];
+    for (int i = 0; i < NT / kWave; ++i) s += sm.wgt[i];
     gcnt[(size_t)row * nch + chunk] = s;
   }
 }
 
-// One workgroup per row: tau and need_eq from the boundary list, then per
-// chunk the number of kept items before it: off[c] counts items > tau in
-// chunks before c, eqb[c] items == tau in chunks before c.
+// grid (nchunk, rows): every workgroup resolves tau (the k-th largest key) and
+// need_eq (items equal to tau that are kept, lowest positions first) from the
+// boundary list, counts the kept items of the chunks before its own, and
+// writes its chunk's kept items in position order.
 template <int NT>
-__global__ __launch_bounds__(NT) void k_long_resolve(TopkArgs a, LongRec* rec, const int32_t* gcnt,
-                                                     int32_t* off, int32_t* eqb, int nch,
-                                                     const uint32_t* bkeys, const int32_t* bpos,
-                                                     long long rld) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];  // [kResolveCap] boundary keys
-  __shared__ TopkShared<NT> sm;
-  __shared__ int cgt[kMaxChunks], ceq[kMaxChunks];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int n = row_length(a, row);
-  if (a.k >= n) return;
-  const int nc = (n + kChunk - 1) / kChunk;
-  const int cb = (int)rec[row].bcount;
-  const int rem = (int)rec[row].rem;
-  const uint32_t* gk = bkeys + (size_t)row * rld;
-  const int32_t* gp = bpos + (size_t)row * rld;
-  const bool in_lds = cb <= kResolveCap;
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = tid; i < cb; i += NT) {
-    const uint32_t x = gk[i];
-    if (in_lds) dyn[i] = x;
-    lo = min(lo, x);
-    hi = max(hi, x);
-  }
-  for (int c = tid; c < nc; c += NT) {
-    cgt[c] = gcnt[(size_t)row * nch + c];
-    ceq[c] = 0;
-  }
-  block_minmax<NT>(lo, hi, sm);  // synchronises
-  uint32_t tau;
-  int need_eq;
-  if (rem >= cb) {
-    // every item of the boundary bin is kept
-    tau = sm.umin;
-    need_eq = cb;
-  } else if (in_lds) {
-    auto key_at = [=](int i) { return dyn[i]; };
-    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
-  } else {
-    auto key_at = [=](int i) { return gk[i]; };
-    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
-  }
-  for (int i = tid; i < cb; i += NT) {
-    const uint32_t x = in_lds ? dyn[i] : gk[i];
-    const int c = gp[i] / kChunk;
-    if (x > tau) atomicAdd(&cgt[c], 1);
-    else if (x == tau) atomicAdd(&ceq[c], 1);
-  }
-  __syncthreads();
-  // exclusive scans over the row's chunks, NT at a time
-  int gt_run = 0, eq_run = 0;
-  for (int c0 = 0; c0 < nc; c0 += NT) {
-    const int c = c0 + tid;
-    const int g = c < nc ? cgt[c] : 0, e = c < nc ? ceq[c] : 0;
-    int gtot, etot;
-    const int gi = block_scan<NT>(g, sm, &gtot);
-    const int ei = block_scan<NT>(e, sm, &etot);
-    if (c < nc) {
-      off[(size_t)row * nch + c] = gt_run + gi - g;
-      eqb[(size_t)row * nch + c] = eq_run + ei - e;
-    }
-    gt_run += gtot;
-    eq_run += etot;
-  }
-  if (tid == 0) {
-    rec[row].tau = tau;
-    rec[row].need = (uint32_t)need_eq;
-  }
-}
-
-// grid (nchunk, rows): write the chunk's kept items in position order.
-template <int NT>
-__global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const int32_t* off,
-                                                  const int32_t* eqb, int nch) {
+__global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const uint32_t* bcount,
+                                                  const int32_t* gcnt, int nch, const uint32_t* bkeys,
+                                                  const int32_t* bpos, long long rld) {
   constexpr int NW = NT / kWave;
-  __shared__ int wgt[NW], weq[NW];
+  __shared__ TopkShared<NT> sm;
+  __shared__ __attribute__((aligned(16))) uint32_t blist[kBoundaryCap];
   const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int n = row_length(a, row);
@@ -768,9 +685,62 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
         }
     return;
   }
-  const uint32_t tau = rec[row].tau;
-  const int need = (int)rec[row].need;
-  // per lane and group: items above tau (low half) and equal to it (high half)
+  // ---- tau and need_eq from the boundary list
+  const int cb = (int)bcount[row];
+  const int rem = (int)rec[row].rem;
+  const uint32_t* gk = bkeys + (size_t)row * rld;
+  const int32_t* gp = bpos + (size_t)row * rld;
+  const bool in_lds = cb <= kBoundaryCap;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = tid; i < cb; i += NT) {
+    const uint32_t x = gk[i];
+    if (in_lds) blist[i] = x;
+    lo = min(lo, x);
+    hi = max(hi, x);
+  }
+  block_minmax<NT>(lo, hi, sm);  // synchronises
+  uint32_t tau;
+  int need_eq;
+  if (rem >= cb) {
+    tau = sm.umin;  // every item of the boundary bin is kept
+    need_eq = cb;
+  } else if (cb <= kRankCap) {
+    for (int i = tid; i < cb; i += NT) sm.list[i] = blist[i];
+    __syncthreads();
+    rank_in_list<NT>(cb, rem, sm, tau, need_eq);
+  } else if (in_lds) {
+    auto key_at = [&](int i) { return blist[i]; };
+    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
+  } else {
+    auto key_at = [=](int i) { return gk[i]; };
+    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
+  }
+  // ---- kept items before this chunk: above-bin counts of earlier chunks, plus
+  // the boundary items before s0 that are > tau or == tau
+  int gt_before = 0, eq_before = 0;
+  for (int c = tid; c < chunk; c += NT) gt_before += gcnt[(size_t)row * nch + c];
+  for (int i = tid; i < cb; i += NT) {
+    if (gp[i] < s0) {
+      const uint32_t x = in_lds ? blist[i] : gk[i];
+      gt_before += x > tau ? 1 : 0;
+      eq_before += x == tau ? 1 : 0;
+    }
+  }
+  gt_before = (int)wave_total_u32((uint32_t)gt_before);
+  eq_before = (int)wave_total_u32((uint32_t)eq_before);
+  if (lane == 0) {
+    sm.wgt[w] = gt_before;
+    sm.weq[w] = eq_before;
+  }
+  __syncthreads();
+  int gt_all = 0, eq_all = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    gt_all += sm.wgt[i];
+    eq_all += sm.weq[i];
+  }
+  __syncthreads();  // sm.wgt is reused below
+  // ---- this chunk, in position order
   int cnt[kGroups];
   int tot = 0;
 #pragma unroll
@@ -784,16 +754,16 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
     cnt[g] = c;
     tot += c;
   }
-  tot = wave_sum(tot);
+  tot = (int)wave_total_u32((uint32_t)tot);
   if (lane == 0) {
-    wgt[w] = tot & 0xffff;
-    weq[w] = tot >> 16;
+    sm.wgt[w] = tot & 0xffff;
+    sm.weq[w] = tot >> 16;
   }
   __syncthreads();
-  int gt_run = off[(size_t)row * nch + chunk], eq_run = eqb[(size_t)row * nch + chunk];
+  int gt_run = gt_all, eq_run = eq_all;
   for (int i = 0; i < w; ++i) {
-    gt_run += wgt[i];
-    eq_run += weq[i];
+    gt_run += sm.wgt[i];
+    eq_run += sm.weq[i];
   }
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
@@ -806,10 +776,10 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
       const int s = ws0 + 4 * (lane + kWave * g) + e;
       int p = -1;
       if (u[g][e] > tau) {
-        p = gt_b + min(eq_b, need);
+        p = gt_b + min(eq_b, need_eq);
         ++gt_b;
       } else if (u[g][e] == tau) {
-        if (eq_b < need) p = gt_b + eq_b;
+        if (eq_b < need_eq) p = gt_b + eq_b;
         ++eq_b;
       }
       if (p >= 0 && p < a.k) {
@@ -817,9 +787,9 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
         if (os) os[p] = key_score(u[g][e]);
       }
     }
-    const int wtot = __shfl(inc, kWave - 1, kWave);
-    gt_run += wtot & 0xffff;
-    eq_run += wtot >> 16;
+    const int wt = __builtin_amdgcn_readlane(inc, kWave - 1);
+    gt_run += wt & 0xffff;
+    eq_run += wt >> 16;
   }
 }
 
@@ -1168,25 +1138,12 @@ hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLo
   hipError_t e = cx.launch("topk_hist", k_long_hist<kLongNT>, grid, dim3(kLongNT), 0, a, ws.rmm,
                            ws.nmm, ws.ghist);
   if (e != hipSuccess) return e;
-  e = cx.launch("topk_bin", k_long_bin<1024>, dim3(a.rows), dim3(1024), 0, a, ws.rmm, ws.nmm,
-                (const uint32_t*)ws.ghist, rec);
-  if (e != hipSuccess) return e;
-  e = cx.launch("topk_count", k_long_count<kLongNT>, grid, dim3(kLongNT), 0, a, rec, ws.gcnt, nch,
-                ws.bkeys, ws.bpos, rld);
-  if (e != hipSuccess) return e;
-  const size_t shmem = (size_t)kResolveCap * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_long_resolve<1024>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    attr_set = true;
-  }
-  e = cx.launch("topk_resolve", k_long_resolve<1024>, dim3(a.rows), dim3(1024), shmem, a, rec,
-                (const int32_t*)ws.gcnt, ws.off, ws.eqb, nch, (const uint32_t*)ws.bkeys,
-                (const int32_t*)ws.bpos, rld);
+  e = cx.launch("topk_count", k_long_count<kLongNT>, grid, dim3(kLongNT), 0, a, ws.rmm, ws.nmm,
+                (const uint32_t*)ws.ghist, ws.bcount, rec, ws.gcnt, nch, ws.bkeys, ws.bpos, rld);
   if (e != hipSuccess) return e;
   return cx.launch("topk_emit", k_long_emit<kLongNT>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,
-                   (const int32_t*)ws.off, (const int32_t*)ws.eqb, nch);
+                   (const uint32_t*)ws.bcount, (const int32_t*)ws.gcnt, nch, (const uint32_t*)ws.bkeys,
+                   (const int32_t*)ws.bpos, rld);
 }
 
 hipError_t launch_topk_range(const LaunchCtx& cx, const TopkArgs& a, uint32_t* rmm_out,
