@@ -93,7 +93,17 @@ typedef struct misa_problem {
   const void* K;           /* [L,d]   shared indexer keys (bf16 bits or e4m3fn bytes) */
   const float* k_scale;    /* [L]     per-token scale, required iff k_dtype is fp8, else NULL */
   const int32_t* pos;      /* [T]     causal position of each query */
+  const float* kbar;       /* [ceil(L/B),d] cached block means, or NULL (see below) */
 } misa_problem;
+
+/* Cached block means (kbar). When p->kbar is NULL every call pools the keys
+ * itself. When it is set, row b of kbar stands for the mean of block b
+ * wherever block b is a complete block before a query's own last block
+ * (b < M_t - 1); each query's last block is always pooled from K, since it
+ * depends on pos[t]. The library trusts the values: results are those of the
+ * definitions evaluated with these means, which is what misa_block_means
+ * writes. Pointer must be 16-byte aligned. Used by misa_route,
+ * misa_score_topk, misa_hier_topk and hisa_topk; misa_block_means ignores it. */
 
 /* Bytes of workspace entry point `op` needs for this problem and these
  * parameters (unused parameters are ignored). Returns 0 for an invalid request;

@@ -83,9 +83,15 @@ def dequant_keys(K, k_dtype: int, k_scale=None) -> np.ndarray:
 
 
 class Problem:
-    """Decoded inputs of one indexer call (float64 copies, exact)."""
+    """Decoded inputs of one indexer call (float64 copies, exact).
 
-    def __init__(self, q_bits, w, K, pos, B, k_dtype=KDT_BF16, k_scale=None):
+    kbar, when given, is a float32 [ceil(L/B), d] array of cached block means:
+    row b stands for the mean of block b wherever that block is complete and
+    lies before the query's own last block (the router's block statistics are
+    query independent there [MISA]); a query's last block is always pooled from
+    its visible keys."""
+
+    def __init__(self, q_bits, w, K, pos, B, k_dtype=KDT_BF16, k_scale=None, kbar=None):
         self.q = decode_bf16(q_bits)                                   # [T,H,d]
         self.w = np.asarray(w, dtype=np.float32).astype(np.float64)   # [T,H]
         self.K = dequant_keys(K, k_dtype, k_scale)                     # [L,d]
@@ -93,6 +99,7 @@ class Problem:
         self.B = int(B)
         self.T, self.H, self.d = self.q.shape
         self.L = self.K.shape[0]
+        self.kbar = None if kbar is None else np.asarray(kbar, dtype=np.float32).astype(np.float64)
 
     def n(self, t: int) -> int:
         """Visible prefix length of query t: keys s <= pos[t]."""
@@ -159,7 +166,10 @@ def block_means(P: Problem, t: int) -> np.ndarray:
     rng = block_ranges(P.n(t), P.B)
     out = np.zeros((len(rng), P.d))
     for b, (s0, s1) in enumerate(rng):
-        out[b] = P.K[s0:s1].sum(axis=0) / (s1 - s0)
+        if P.kbar is not None and b < len(rng) - 1:
+            out[b] = P.kbar[b]          # cached mean of a complete earlier block
+        else:
+            out[b] = P.K[s0:s1].sum(axis=0) / (s1 - s0)
     return out
 
 

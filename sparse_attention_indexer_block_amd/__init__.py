@@ -43,7 +43,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("L", ctypes.c_int32), ("B", ctypes.c_int32), ("k_dtype", ctypes.c_int32),
                 ("q", ctypes.c_void_p), ("w", ctypes.c_void_p), ("K", ctypes.c_void_p),
-                ("k_scale", ctypes.c_void_p), ("pos", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("kbar", ctypes.c_void_p)]
 
 
 _lib = None
@@ -101,8 +101,10 @@ def _dev(t: torch.Tensor, name: str):
 
 
 def make_problem(q: Optional[torch.Tensor], w: Optional[torch.Tensor], K: torch.Tensor,
-                 pos: Optional[torch.Tensor], B: int, k_scale: Optional[torch.Tensor] = None):
-    """Fill the C problem struct from tensors (no copies)."""
+                 pos: Optional[torch.Tensor], B: int, k_scale: Optional[torch.Tensor] = None,
+                 kbar: Optional[torch.Tensor] = None):
+    """Fill the C problem struct from tensors (no copies). `kbar` is an optional
+    float32 [ceil(L/B), d] tensor of cached block means (see block_means)."""
     _dev(K, "K")
     if K.dtype in (torch.uint8, torch.float8_e4m3fn):
         kdt = KDT_FP8
@@ -128,7 +130,12 @@ def make_problem(q: Optional[torch.Tensor], w: Optional[torch.Tensor], K: torch.
         T, H, dq = q.shape
         if dq != d or tuple(w.shape) != (T, H) or tuple(pos.shape) != (T,):
             raise ValueError("shape mismatch between q [T,H,d], w [T,H], pos [T] and K [L,d]")
-    p = Problem(T, H, d, L, int(B), kdt, _ptr(q), _ptr(w), _ptr(K), _ptr(k_scale), _ptr(pos))
+    if kbar is not None:
+        _dev(kbar, "kbar")
+        if kbar.dtype != torch.float32 or tuple(kbar.shape) != (-(-L // int(B)), d):
+            raise ValueError("kbar must be float32 [ceil(L/B), d]")
+    p = Problem(T, H, d, L, int(B), kdt, _ptr(q), _ptr(w), _ptr(K), _ptr(k_scale), _ptr(pos),
+                _ptr(kbar))
     return p
 
 
@@ -155,8 +162,8 @@ def block_means(K, B, k_scale=None, ws=None):
     return kbar
 
 
-def route(q, w, K, pos, B, A, k_scale=None, with_r=False, ws=None):
-    p = make_problem(q, w, K, pos, B, k_scale)
+def route(q, w, K, pos, B, A, k_scale=None, with_r=False, ws=None, kbar=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar)
     heads = torch.empty((p.T, A), dtype=torch.int32, device=q.device)
     r = torch.empty((p.T, p.H), dtype=torch.float32, device=q.device) if with_r else None
     ws, n = _workspace(p, OP_ROUTE, q.device, ws, A=A)
@@ -169,8 +176,8 @@ def _outputs(p, k, device):
             torch.empty((p.T, k), dtype=torch.float32, device=device))
 
 
-def score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None, ws=None, out=None):
-    p = make_problem(q, w, K, pos, B, k_scale)
+def score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None, ws=None, out=None, kbar=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar)
     if heads is not None:
         _dev(heads, "heads")
         if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):
@@ -182,8 +189,9 @@ def score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None, ws=None, out=Non
     return idx, sc
 
 
-def hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, ws=None, out=None):
-    p = make_problem(q, w, K, pos, B, k_scale)
+def hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, ws=None, out=None,
+              kbar=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar)
     if heads is not None:
         _dev(heads, "heads")
         if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):
@@ -195,8 +203,8 @@ def hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, ws=None, 
     return idx, sc
 
 
-def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None):
-    p = make_problem(q, w, K, pos, B, k_scale)
+def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, kbar=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar)
     idx, sc = out if out is not None else _outputs(p, k, q.device)
     ws, n = _workspace(p, OP_HISA_TOPK, q.device, ws, m=m, k=k)
     _check(lib().hisa_topk(ctypes.byref(p), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n, _stream()))

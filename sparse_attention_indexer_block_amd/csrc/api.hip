@@ -196,6 +196,7 @@ static misa_status check_problem(const misa_problem* p, bool need_queries) {
   if (fp8 && !p->k_scale) return fail(MISA_ERR_INVALID_ARG, "k_scale is required for fp8 keys");
   if (!fp8 && p->k_scale) return fail(MISA_ERR_INVALID_ARG, "k_scale must be NULL for bf16 keys");
   if (p->k_scale && !aligned(p->k_scale, 4)) return fail(MISA_ERR_INVALID_ARG, "k_scale must be 4-byte aligned");
+  if (p->kbar && !aligned(p->kbar, 16)) return fail(MISA_ERR_INVALID_ARG, "kbar must be 16-byte aligned");
   if (need_queries && p->T > 0) {
     if (!p->q || !p->w || !p->pos) return fail(MISA_ERR_INVALID_ARG, "q, w and pos must be non-NULL");
     if (!aligned(p->q, 16)) return fail(MISA_ERR_INVALID_ARG, "q must be 16-byte aligned");
@@ -239,10 +240,12 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   double* ksum = at<double>(ws, pl.ksum);
   double* tsum = at<double>(ws, pl.tsum);
   double* pmax = at<double>(ws, pl.pmax);
-  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum),
+  // with cached block means only each query's last block is pooled here
+  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
+                            p->kbar != nullptr),
           "block sums");
-  HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, tsum, pmax, heads, r,
-                       beta, beta_ld, qr, wr),
+  HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, pmax,
+                       heads, r, beta, beta_ld, qr, wr),
           "router");
   return MISA_OK;
 }

@@ -54,16 +54,16 @@ inline long long padded_ld(long long n) { return ((n + 63) / 64) * 64; }
 // tsum is given, the sum of each query's last (possibly partial) block.
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum);
+                             double* tsum, bool tails_only = false);
 // Router tiles of 16 blocks; the pmax workspace holds T * (route_chunks + 1) * 64 doubles.
 int route_chunks(int L, int B);
 // Router: heads[T,A] (ascending), optional r[T,H], optional HISA block scores
 // beta, and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed
 // in slot order (so scoring needs no head indirection).
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
-                        int T, int H, int L, int B, int A, const double* ksum, const double* tsum,
-                        double* pmax, int32_t* heads, float* r_out, float* beta, int beta_ld,
-                        uint16_t* qr, float* wr);
+                        int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
+                        const double* tsum, double* pmax, int32_t* heads, float* r_out,
+                        float* beta, int beta_ld, uint16_t* qr, float* wr);
 // Pack q rows and weights of given heads [T,A] in slot order (ids outside [0,H)
 // give zero rows and weights).
 hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,

@@ -89,17 +89,18 @@ struct RowSum {
   }
 };
 
-// Workgroups [0, M): ksum[b,:] = sum of the keys of block b = [b*B, min((b+1)*B, L))
-// in float64, and (optional) kbar = ksum / count rounded once to float32.
-// Workgroups [M, M+T): tsum[t,:] = sum of the keys of query t's last block
-// [(M_t-1)*B, n_t), possibly partial; zero when the query sees no key.
+// Workgroup b (= blockIdx.x + b_base) in [0, M): ksum[b,:] = sum of the keys of
+// block b = [b*B, min((b+1)*B, L)) in float64, and (optional) kbar = ksum /
+// count rounded once to float32. Workgroups [M, M+T): tsum[t,:] = sum of the
+// keys of query t's last block [(M_t-1)*B, n_t), possibly partial; zero when
+// the query sees no key. b_base = M computes the query tails only.
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* kscale, int L,
                                                     int B, int M, double* ksum, float* kbar,
-                                                    const int32_t* pos, double* tsum) {
+                                                    const int32_t* pos, double* tsum, int b_base) {
   constexpr int RL = RowSum<FP8>::RL;
   __shared__ double red[RL][kHeadDim];
-  const int b = blockIdx.x;
+  const int b = (int)blockIdx.x + b_base;
   int s0, s1;
   if (b < M) {
     s0 = (int)((long long)b * B);
@@ -160,8 +161,9 @@ template <bool WITH_BETA, int kRouteQG>
 __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const float* w,
                                                     const int32_t* pos, int T, int H, int L, int B,
                                                     int ntiles, const double* ksum,
-                                                    const double* tsum, double* pmax,
-                                                    double* ptail, float* beta, int beta_ld) {
+                                                    const float* kbar, const double* tsum,
+                                                    double* pmax, double* ptail, float* beta,
+                                                    int beta_ld) {
   __shared__ f64x2 kt[kRouteTile][kHeadDim / 2 + 1];  // padded rows
   __shared__ double bsum[4][kRouteTile];
   const int tile = blockIdx.x, tq0 = blockIdx.y * kRouteQG;
@@ -184,7 +186,22 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
 #pragma unroll
     for (int v = 0; v < 4; ++v) qv[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
   }
-  {
+  if (kbar) {
+    // stage the tile's cached block means (8 KB): two 16-byte loads per thread
+    f32x4 x[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 256 * u, r = i >> 5, c4 = i & 31;
+      x[u] = b0 + r < M ? reinterpret_cast<const f32x4*>(kbar + (size_t)(b0 + r) * kHeadDim)[c4]
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 256 * u, r = i >> 5, c4 = i & 31;
+      kt[r][2 * c4] = f64x2{(double)x[u][0], (double)x[u][1]};
+      kt[r][2 * c4 + 1] = f64x2{(double)x[u][2], (double)x[u][3]};
+    }
+  } else {
     // stage the tile's block sums (16 KB): four 16-byte loads per thread
     f64x2 x[4];
 #pragma unroll
@@ -198,6 +215,8 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
       kt[i >> 6][i & 63] = x[u];
     }
   }
+  // full blocks hold sums (divide by B) or cached means (divide by 1)
+  const double div_full = kbar ? 1.0 : (double)B;
   __syncthreads();
   f64x2 kv[16];
 #pragma unroll
@@ -237,11 +256,11 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     }
     const f64x4 acc = acc0 + acc1;
     // this lane holds heads 16 wv + 4 e + g (e = 0..3) against block blk
-    const double cnt = tail ? (double)(n - (Mt - 1) * B) : (double)B;
+    const double cnt = tail ? (double)(n - (Mt - 1) * B) : div_full;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0);
-      if (col == 0) pm[kRouteTile * wv + 4 * e + g] = m / (double)B;
+      if (col == 0) pm[kRouteTile * wv + 4 * e + g] = m / div_full;
     }
     if (tail) {
 #pragma unroll
@@ -369,15 +388,17 @@ __global__ __launch_bounds__(64) void k_gather_heads(const uint16_t* q, const fl
 
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum) {
+                             double* tsum, bool tails_only) {
   const int M = (int)(((long long)L + B - 1) / B);
-  const int grid = M + (tsum ? T : 0);
+  const int base = tails_only ? M : 0;
+  const int grid = M - base + (tsum ? T : 0);
   if (grid == 0) return hipSuccess;
+  const char* nm = tails_only ? "tail_sums" : "block_sums";
   if (fp8)
-    return cx.launch("block_sums", k_block_sums<true>, dim3(grid), dim3(256), 0, K, kscale, L, B, M,
-                     ksum, kbar, pos, tsum);
-  return cx.launch("block_sums", k_block_sums<false>, dim3(grid), dim3(256), 0, K, kscale, L, B, M,
-                   ksum, kbar, pos, tsum);
+    return cx.launch(nm, k_block_sums<true>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,
+                     kbar, pos, tsum, base);
+  return cx.launch(nm, k_block_sums<false>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,
+                   kbar, pos, tsum, base);
 }
 
 int route_chunks(int L, int B) {
@@ -387,9 +408,9 @@ int route_chunks(int L, int B) {
 }
 
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
-                        int T, int H, int L, int B, int A, const double* ksum, const double* tsum,
-                        double* pmax, int32_t* heads, float* r_out, float* beta, int beta_ld,
-                        uint16_t* qr, float* wr) {
+                        int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
+                        const double* tsum, double* pmax, int32_t* heads, float* r_out,
+                        float* beta, int beta_ld, uint16_t* qr, float* wr) {
   if (T == 0) return hipSuccess;
   const int nt = route_chunks(L, B);
   double* ptail = pmax + (size_t)T * nt * kWave;
@@ -400,16 +421,16 @@ hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, 
   const dim3 grid(nt, pair ? (T + 1) / 2 : T);
   if (beta && pair)
     e = cx.launch("route_mfma", k_route_mfma<true, 2>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, tsum, pmax, ptail, beta, beta_ld);
+                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
   else if (beta)
     e = cx.launch("route_mfma", k_route_mfma<true, 1>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, tsum, pmax, ptail, beta, beta_ld);
+                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
   else if (pair)
     e = cx.launch("route_mfma", k_route_mfma<false, 2>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, tsum, pmax, ptail, beta, beta_ld);
+                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
   else
     e = cx.launch("route_mfma", k_route_mfma<false, 1>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, tsum, pmax, ptail, beta, beta_ld);
+                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
   if (e != hipSuccess) return e;
   if (!heads && !r_out) return hipSuccess;  // block scores only
   return cx.launch("route_select", k_route_select, dim3(T), dim3(256), 0, q, w, pos, H, L, B, A, nt,

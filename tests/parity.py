@@ -37,11 +37,15 @@ def to_gpu(inp, device="cuda"):
 
 
 def oracle_problem(inp, B, rows=None):
+    """Oracle problem of an input dict; an optional inp["kbar"] (float32 cached
+    block means) is passed through."""
     kdt = O.KDT_FP8 if inp["k_scale"] is not None else O.KDT_BF16
+    kbar = inp.get("kbar")
     if rows is None:
-        return O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], B, kdt, inp["k_scale"])
+        return O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], B, kdt, inp["k_scale"], kbar=kbar)
     rows = np.asarray(rows)
-    return O.Problem(inp["q"][rows], inp["w"][rows], inp["K"], inp["pos"][rows], B, kdt, inp["k_scale"])
+    return O.Problem(inp["q"][rows], inp["w"][rows], inp["K"], inp["pos"][rows], B, kdt, inp["k_scale"],
+                     kbar=kbar)
 
 
 def kdtype(inp):

@@ -40,10 +40,11 @@ FAKE = 1 << 20  # an aligned, never-dereferenced address: validation must fail f
 
 
 def _problem(**kw):
-    base = dict(T=4, H=64, d=128, L=1024, B=128, k_dtype=0, q=FAKE, w=FAKE, K=FAKE, k_scale=None, pos=FAKE)
+    base = dict(T=4, H=64, d=128, L=1024, B=128, k_dtype=0, q=FAKE, w=FAKE, K=FAKE, k_scale=None, pos=FAKE,
+                kbar=None)
     base.update(kw)
     return S.Problem(base["T"], base["H"], base["d"], base["L"], base["B"], base["k_dtype"],
-                     base["q"], base["w"], base["K"], base["k_scale"], base["pos"])
+                     base["q"], base["w"], base["K"], base["k_scale"], base["pos"], base["kbar"])
 
 
 def _route(p, A=8, heads=FAKE, ws=FAKE, nbytes=1 << 40):
@@ -59,6 +60,7 @@ def _score(p, A=8, k=16, idx=FAKE, sc=FAKE, ws=FAKE, nbytes=1 << 40):
     (dict(k_dtype=3), -1), (dict(d=64), -2), (dict(H=65), -2), (dict(K=None), -1),
     (dict(q=None), -1), (dict(w=None), -1), (dict(pos=None), -1), (dict(q=FAKE + 2), -1),
     (dict(K=FAKE + 8), -1), (dict(k_dtype=1), -1), (dict(k_scale=FAKE), -1),
+    (dict(kbar=FAKE + 4), -1), (dict(L=(1 << 23) + 1), -2),
 ])
 def test_problem_validation(kw, status):
     assert _route(_problem(**kw)) == status

@@ -282,3 +282,40 @@ def test_rows_without_keys():
         assert (idx[:2] == -1).all() and np.isneginf(sc[:2]).all()
         assert idx[2, 0] == 0 and (idx[2, 1:] == -1).all()
         assert (idx[3] >= 0).all()
+
+
+# ----------------------------------------------------------------- cached block means
+
+KBAR_CASES = [
+    # seed, T, L, H, A, B, kdt
+    (61, 7, 3000, 64, 8, 128, O.KDT_BF16),
+    (62, 9, 20000, 32, 8, 128, O.KDT_FP8),
+    (63, 5, 700, 64, 4, 64, O.KDT_FP8),
+]
+
+
+@pytest.mark.parametrize("source", ["pooled", "arbitrary"])
+@pytest.mark.parametrize("case", KBAR_CASES, ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}B{c[5]}kd{c[6]}")
+def test_cached_block_means(case, source):
+    """Every entry point with cached means (the library's own, or arbitrary
+    rows, which must be used as given) against the oracle fed the same rows."""
+    seed, T, L, H, A, B, kdt = case
+    inp = _case(seed, T, L, H, kdt, positions="random")
+    q, w, K, ks, pos = to_gpu(inp)
+    M = -(-L // B)
+    if source == "pooled":
+        kbar = S.block_means(K, B, ks)
+    else:
+        rows = np.random.default_rng(seed).standard_normal((M, 128)).astype(np.float32) * 0.2
+        kbar = torch.from_numpy(rows).cuda()
+    inp = dict(inp, kbar=_np(kbar))
+    heads, r = S.route(q, w, K, pos, B, A, ks, with_r=True, kbar=kbar)
+    P = oracle_problem(inp, B)
+    heads_o, ill = check_heads(P, A, _np(heads), _np(r))
+    assert ill == 0
+    idx, sc = S.score_topk(q, w, K, pos, B, A, 64, ks, kbar=kbar)
+    _check_misa(inp, B, A, 64, _np(idx), _np(sc), heads_o, label="cached misa")
+    idx, sc = S.hier_topk(q, w, K, pos, B, A, 256, 64, ks, kbar=kbar)
+    check_hier(inp, B, A, 256, 64, _np(idx), _np(sc), label="cached hier")
+    idx, sc = S.hisa_topk(q, w, K, pos, B, 4, 64, ks, kbar=kbar)
+    check_hisa(inp, B, 4, 64, _np(idx), _np(sc), label="cached hisa")

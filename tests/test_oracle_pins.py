@@ -410,3 +410,70 @@ def test_rows_shorter_than_k_take_everything():
     P = _P(inp, 8)
     for t, (idx, sc) in enumerate(O.misa_topk(P, 3, 32)[0]):
         assert sorted(idx) == list(range(P.n(t)))
+
+
+# ------------------------------------------------------- cached block means
+
+def _exact_block_means_f32(P):
+    """Means of every block of the whole key array, from an explicit loop; on a
+    dyadic grid with power-of-two blocks they are exact in float32."""
+    M = -(-P.L // P.B)
+    out = np.zeros((M, P.d), dtype=np.float32)
+    for b in range(M):
+        s0, s1 = b * P.B, min((b + 1) * P.B, P.L)
+        acc = np.zeros(P.d)
+        for s in range(s0, s1):
+            acc += P.K[s]
+        out[b] = acc / (s1 - s0)
+        assert np.array_equal(out[b].astype(np.float64), acc / (s1 - s0))  # exact in fp32
+    return out
+
+
+@pytest.mark.parametrize("B", [2, 4, 8])
+def test_cached_exact_means_change_nothing(B):
+    """Cached means equal to the pooled ones give the same routes, block scores
+    and selections, bit for bit."""
+    inp = synth.random_small(11, T=5, L=60, H=6, d=16, int_grid=True, positions="random")
+    P = _P(inp, B)
+    kbar = _exact_block_means_f32(P)
+    Pc = O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], B, O.KDT_BF16, None, kbar=kbar)
+    h1, r1 = O.route(P, 3)
+    h2, r2 = O.route(Pc, 3)
+    assert np.array_equal(h1, h2) and np.array_equal(r1, r2)
+    for t in range(P.T):
+        assert np.array_equal(O.hisa_block_scores(P, t), O.hisa_block_scores(Pc, t))
+    _same(O.misa_topk(P, 3, 9)[0], O.misa_topk(Pc, 3, 9)[0])
+    _same(O.hisa_topk(P, 2, 9)[0], O.hisa_topk(Pc, 2, 9)[0])
+
+
+def test_cached_means_closed_form():
+    """With arbitrary cached rows, r(t,h) = w * max(0, max over the complete
+    earlier blocks of q.kbar_b, q.mean(last block)) -- written out per head
+    here -- and the cached row of the query's own last block is never read."""
+    inp = synth.random_small(12, T=6, L=90, H=5, d=8, positions="random")
+    B = 16
+    P = _P(inp, B)
+    M = -(-P.L // B)
+    rng = np.random.default_rng(3)
+    kbar = rng.standard_normal((M, P.d)).astype(np.float32)
+    Pc = O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], B, O.KDT_BF16, None, kbar=kbar)
+    _, r = O.route(Pc, 2)
+    for t in range(P.T):
+        n = P.n(t)
+        Mt = -(-n // B)
+        for h in range(P.H):
+            best = 0.0
+            for b in range(Mt - 1):
+                best = max(best, float(np.dot(P.q[t, h], kbar[b].astype(np.float64))))
+            if Mt > 0:
+                s0 = (Mt - 1) * B
+                tail = P.K[s0:n].sum(axis=0) / (n - s0)
+                best = max(best, float(np.dot(P.q[t, h], tail)))
+            assert np.isclose(r[t, h], P.w[t, h] * best, rtol=1e-12, atol=1e-14)
+        # poisoning the row of the query's own last block changes nothing
+        if Mt > 0:
+            k2 = kbar.copy()
+            k2[Mt - 1] = 1e6
+            P2 = O.Problem(inp["q"][t:t + 1], inp["w"][t:t + 1], inp["K"], inp["pos"][t:t + 1], B,
+                           O.KDT_BF16, None, kbar=k2)
+            assert np.array_equal(O.route(P2, 2)[1][0], r[t])
