@@ -234,6 +234,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scale for HBM byte counters)")
+    ap.add_argument("--only", default=None, metavar="PATH:WORKLOAD",
+                    help="time one secondary line only (e.g. misa:c3_causal_prefill) and print it; "
+                         "for profiling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         _fail_multi_gpu(max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))))
@@ -253,6 +256,15 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return
     S.lib()
+    if args.only:
+        path, nm = args.only.split(":")
+        w1, i1, t1 = load_inputs(nm)
+        m1, k1, pc1 = time_path(S, path, w1, t1, args.steps, args.warmup, use_graphs=not args.eager,
+                                kernel=["score", "route", "block_sums", "topk"])
+        print(json.dumps({"only": args.only, "pairs_per_s": pairs_of(i1) / (m1 * 1e-3), "ms_per_step": m1,
+                          "step_ms_percentiles": pc1, "kernels_avg_ms": {k: v[0] for k, v in k1.items()}}),
+              flush=True)
+        return
 
     name = "c4_hier_decode_128k"
     wl, inp, tensors = load_inputs(name)

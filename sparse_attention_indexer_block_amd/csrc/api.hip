@@ -74,10 +74,10 @@ struct Bump {
 struct Plan {
   size_t ksum = 0, tsum = 0, pmax = 0, heads = 0, beta = 0, qr = 0, wr = 0;
   size_t S = 0;
-  size_t rmm = 0, ghist = 0, bcount = 0, rec = 0, gcnt = 0, bkeys = 0, bpos = 0;
+  size_t rmm = 0, ghist = 0, rec = 0, gcnt = 0, bcnt = 0, bkeys = 0;
   size_t cand = 0, ncand = 0, S2 = 0, blocks = 0, nblocks = 0;
   long long S_ld = 0, cand_ld = 0, S2_ld = 0, beta_ld = 0;
-  long long zero_words = 0;  // ghist + bcount, cleared by the first kernel that needs them
+  long long zero_words = 0;  // ghist, cleared by the first kernel that needs it
   int Mmax = 0, mm = 0;
   size_t total = 0;
 };
@@ -92,13 +92,12 @@ static void plan_long(Bump& bp, Plan& pl, int rows, int max_n) {
   const size_t nmm = nch > (size_t)score_max_splits() ? nch : (size_t)score_max_splits();
   // one set of scratch serves every selection of a call (they run in order)
   pl.rmm = bp.take(nmm * rows * 2 * 4);
-  pl.zero_words = (long long)rows * topk_coarse_bins() + rows;
+  pl.zero_words = (long long)rows * topk_coarse_bins();
   pl.ghist = bp.take((size_t)pl.zero_words * 4);
-  pl.bcount = pl.ghist + (size_t)rows * topk_coarse_bins() * 4;
   pl.rec = bp.take((size_t)rows * topk_long_rec_bytes());
   pl.gcnt = bp.take((size_t)rows * nch * 4);
+  pl.bcnt = bp.take((size_t)rows * nch * 4);
   pl.bkeys = bp.take((size_t)rows * rld * 4);
-  pl.bpos = bp.take((size_t)rows * rld * 4);
 }
 
 static void plan_route(Bump& bp, Plan& pl, const misa_problem* p) {
@@ -256,10 +255,9 @@ static TopkLongWs long_ws(const Plan& pl, void* ws, int nmm) {
   lw.nmm = nmm;
   lw.ghist = at<uint32_t>(ws, pl.ghist);
   lw.rec = at<void>(ws, pl.rec);
-  lw.bcount = at<uint32_t>(ws, pl.bcount);
   lw.gcnt = at<int32_t>(ws, pl.gcnt);
+  lw.bcnt = at<int32_t>(ws, pl.bcnt);
   lw.bkeys = at<uint32_t>(ws, pl.bkeys);
-  lw.bpos = at<int32_t>(ws, pl.bpos);
   return lw;
 }
 

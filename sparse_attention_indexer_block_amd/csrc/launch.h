@@ -131,11 +131,10 @@ struct TopkLongWs {
   const uint32_t* rmm; // [nmm, rows, 2] row key ranges written by the scoring kernel
   int nmm;
   uint32_t* ghist;     // [rows, topk_coarse_bins()] (zero on entry)
-  uint32_t* bcount;    // [rows] boundary list lengths (zero on entry)
   void* rec;           // [rows] per-row records of topk_long_rec_bytes()
   int32_t* gcnt;       // [rows, nchunk] items above the threshold bin
-  uint32_t* bkeys;     // [rows, stride] threshold-bin keys
-  int32_t* bpos;       // [rows, stride] their positions
+  int32_t* bcnt;       // [rows, nchunk] threshold-bin items of each chunk
+  uint32_t* bkeys;     // [rows, stride] threshold-bin keys, one region per chunk
 };
 int topk_long_chunks(int max_n);
 int topk_long_chunk();

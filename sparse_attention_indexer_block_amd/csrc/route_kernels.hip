@@ -174,18 +174,24 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
   const int b0 = tile * kRouteTile;
   const int blk = b0 + col;
   const int h_a = kRouteTile * wv + col;  // head fed by this lane's A operand
-  // per query of the group: visible blocks and the A operand (32 bf16 dims)
-  int n_q[kRouteQG], mt_q[kRouteQG];
-  u32x4 qv[kRouteQG][4];
+  // per query of the group: visible blocks, and the A operand (32 bf16 dims)
+  // in a two-slot ring so the next query's rows load during this one's products
+  int n_q[kRouteQG];
 #pragma unroll
   for (int i = 0; i < kRouteQG; ++i) {
     const int t = tq0 + i;
     n_q[i] = t < T ? visible_len(pos[t], L) : 0;
-    const bool ok = t < T && h_a < H;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)(ok ? t : 0) * H + (ok ? h_a : 0)) * kHeadDim + 32 * g);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) qv[i][v] = ok ? src[v] : u32x4{0u, 0u, 0u, 0u};
   }
+  u32x4 qv[2][4];
+#define MISA_LOAD_Q(i, slot)                                                                     \
+  do {                                                                                           \
+    const int t_ = tq0 + (i);                                                                    \
+    const bool ok_ = t_ < T && h_a < H;                                                          \
+    const u32x4* src_ = reinterpret_cast<const u32x4*>(                                          \
+        q + ((size_t)(ok_ ? t_ : 0) * H + (ok_ ? h_a : 0)) * kHeadDim + 32 * g);                 \
+    _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) qv[slot][v_] = ok_ ? src_[v_] : u32x4{0u, 0u, 0u, 0u}; \
+  } while (0)
+  MISA_LOAD_Q(0, 0);
   if (kbar) {
     // stage the tile's cached block means (8 KB): two 16-byte loads per thread
     f32x4 x[2];
@@ -226,6 +232,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
   for (int i = 0; i < kRouteQG; ++i) {
     const int t = tq0 + i;
     if (t >= T) break;  // uniform
+    if (i + 1 < kRouteQG) MISA_LOAD_Q(i + 1, (i + 1) & 1);
     const int n = n_q[i];
     const int Mt = (int)(((long long)n + B - 1) / B);
     double* pm = pmax + ((size_t)t * ntiles + tile) * kWave;
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < 32; s += 2) {
-      const uint32_t word = qv[i][s >> 3][(s >> 1) & 3];
+      const uint32_t word = qv[i & 1][s >> 3][(s >> 1) & 3];
       const double a0 = (double)bf16_bits_to_f32(word & 0xffffu);
       const double a1 = (double)bf16_bits_to_f32(word >> 16);
       acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, kb[s >> 1][0], acc0, 0, 0, 0);
@@ -286,6 +293,8 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     }
   }
 }
+
+#undef MISA_LOAD_Q
 
 // Final router step, 256 threads per query: r(t,h) = w[t,h] * max_b ReLU(rho)
 // over the tile maxima and the last block, then the first A heads under
@@ -415,22 +424,19 @@ hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, 
   const int nt = route_chunks(L, B);
   double* ptail = pmax + (size_t)T * nt * kWave;
   hipError_t e;
-  // one query per workgroup while that still leaves few workgroups per CU;
-  // past that, pairs of queries share each staged tile
-  const bool pair = (long long)nt * T > 2048;
-  const dim3 grid(nt, pair ? (T + 1) / 2 : T);
-  if (beta && pair)
-    e = cx.launch("route_mfma", k_route_mfma<true, 2>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
-  else if (beta)
-    e = cx.launch("route_mfma", k_route_mfma<true, 1>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
-  else if (pair)
-    e = cx.launch("route_mfma", k_route_mfma<false, 2>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
+  // one query per workgroup while that leaves few workgroups per CU; past
+  // that, groups of queries share each staged tile
+  const long long work = (long long)nt * T;
+  const int qg = work > 16384 ? 8 : (work > 2048 ? 2 : 1);
+  const dim3 grid(nt, (T + qg - 1) / qg);
+#define MISA_ROUTE_LAUNCH(BETA, QG)                                                                \
+  cx.launch("route_mfma", k_route_mfma<BETA, QG>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt, ksum, \
+            kbar, tsum, pmax, ptail, beta, beta_ld)
+  if (beta)
+    e = qg == 8 ? MISA_ROUTE_LAUNCH(true, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(true, 2) : MISA_ROUTE_LAUNCH(true, 1));
   else
-    e = cx.launch("route_mfma", k_route_mfma<false, 1>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt,
-                  ksum, kbar, tsum, pmax, ptail, beta, beta_ld);
+    e = qg == 8 ? MISA_ROUTE_LAUNCH(false, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(false, 2) : MISA_ROUTE_LAUNCH(false, 1));
+#undef MISA_ROUTE_LAUNCH
   if (e != hipSuccess) return e;
   if (!heads && !r_out) return hipSuccess;  // block scores only
   return cx.launch("route_select", k_route_select, dim3(T), dim3(256), 0, q, w, pos, H, L, B, A, nt,

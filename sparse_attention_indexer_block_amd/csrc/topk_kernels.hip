@@ -488,8 +488,8 @@ __device__ __forceinline__ void row_range(const uint32_t* rmm, int nmm, int rows
 // Long rows: three passes, each spread over (chunk, row) workgroups.
 //   hist  : coarse histogram of the row (bins linear in the score) into ghist
 //   count : threshold bin b* (the bin holding the k-th largest) from ghist;
-//           per chunk, the items above b*; the items inside b* appended to the
-//           row's boundary list (key, position)
+//           per chunk, the items above b*, and the items inside b* written in
+//           position order to the chunk's own region of the boundary list
 //   emit  : tau (k-th largest key) and need_eq (items equal to tau that are
 //           kept, lowest positions first) from the boundary list; kept items
 //           before the chunk; the chunk's kept items in position order
@@ -567,13 +567,15 @@ __global__ __launch_bounds__(NT) void k_long_hist(TopkArgs a, const uint32_t* rm
 
 // grid (nchunk, rows): every workgroup finds the row's threshold bin from the
 // finished histogram (the same answer in each), counts its chunk's items above
-// that bin, and appends the items inside it to the row's boundary list (in no
-// particular order). Chunk 0 records the rank rem of the k-th item in the bin.
+// that bin, and writes the items inside it, in position order, to the chunk's
+// own region of the boundary list. Chunk 0 records the rank rem of the k-th
+// item in the bin.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* rmm, int nmm,
-                                                   const uint32_t* ghist, uint32_t* bcount,
-                                                   LongRec* rec, int32_t* gcnt, int nch,
-                                                   uint32_t* bkeys, int32_t* bpos, long long rld) {
+                                                   const uint32_t* ghist, LongRec* rec, int32_t* gcnt,
+                                                   int32_t* bcnt, int nch, uint32_t* bkeys,
+                                                   long long rld) {
+  constexpr int NW = NT / kWave;
   __shared__ TopkShared<NT> sm;
   const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* r
   const int s0 = chunk * kChunk, s1 = min(n, s0 + kChunk);
   if (s0 >= s1 || a.k >= n) return;  // uniform
   const float* src = a.S + (size_t)row * a.S_ld;
-  const int ws0 = s0 + w * (kChunk / (NT / kWave));
+  const int ws0 = s0 + w * (kChunk / NW);
   uint32_t u[kGroups][4];
   bool in[kGroups][4];
 #pragma unroll
@@ -598,44 +600,50 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* r
     r.rem = (uint32_t)sm.rem;
     rec[row] = r;
   }
-  int above = 0, nb = 0;
-  uint64_t bm[kGroups][4];
+  // per lane and group: items above the bin (low half) and inside it (high half)
+  int cnt[kGroups];
+  int tot = 0;
+  bool inb[kGroups][4];
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g)
+  for (int g = 0; g < kGroups; ++g) {
+    int c = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t b = coarse_bin(u[g][e], xlo, scale);
-      above += (in[g][e] && b > bstar) ? 1 : 0;
-      bm[g][e] = wave_ballot(in[g][e] && b == bstar);
-      nb += __popcll(bm[g][e]);
+      inb[g][e] = in[g][e] && b == bstar;
+      c += (in[g][e] && b > bstar) ? 1 : 0;
+      c += inb[g][e] ? (1 << 16) : 0;
     }
-  if (nb) {
-    // one list reservation per wave
-    uint32_t base = 0u;
-    if (lane == 0) base = atomicAdd(&bcount[row], (uint32_t)nb);
-    base = __shfl(base, 0, kWave);
-    uint32_t* kd = bkeys + (size_t)row * rld;
-    int32_t* pd = bpos + (size_t)row * rld;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if ((bm[g][e] >> lane) & 1ull) {
-          const uint32_t at = base + (uint32_t)lanes_below(bm[g][e]);
-          kd[at] = u[g][e];
-          pd[at] = ws0 + 4 * (lane + kWave * g) + e;
-        }
-        base += (uint32_t)__popcll(bm[g][e]);
-      }
+    cnt[g] = c;
+    tot += c;
   }
-  above = (int)wave_total_u32((uint32_t)above);
-  if (lane == 0) sm.wgt[w] = above;
+  tot = (int)wave_total_u32((uint32_t)tot);
+  if (lane == 0) {
+    sm.wgt[w] = tot & 0xffff;
+    sm.weq[w] = tot >> 16;
+  }
   __syncthreads();
-  if (tid == 0) {
-    int s = 0;
+  int above = 0, nb = 0, run = 0;
 #pragma unroll
-    for (int i = 0; i < NT / kWave; ++i) s += sm.wgt[i];
-    gcnt[(size_t)row * nch + chunk] = s;
+  for (int i = 0; i < NW; ++i) {
+    above += sm.wgt[i];
+    nb += sm.weq[i];
+    run += i < w ? sm.weq[i] : 0;
+  }
+  if (tid == 0) {
+    gcnt[(size_t)row * nch + chunk] = above;
+    bcnt[(size_t)row * nch + chunk] = nb;
+  }
+  if (nb == 0) return;  // uniform
+  uint32_t* kd = bkeys + (size_t)row * rld + (size_t)chunk * kChunk;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int inc = wave_inclusive_scan(cnt[g] >> 16);
+    int at = run + inc - (cnt[g] >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (inb[g][e]) kd[at++] = u[g][e];
+    run += __builtin_amdgcn_readlane(inc, kWave - 1);
   }
 }
 
@@ -644,12 +652,13 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* r
 // boundary list, counts the kept items of the chunks before its own, and
 // writes its chunk's kept items in position order.
 template <int NT>
-__global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const uint32_t* bcount,
-                                                  const int32_t* gcnt, int nch, const uint32_t* bkeys,
-                                                  const int32_t* bpos, long long rld) {
+__global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
+                                                  const int32_t* bcnt, int nch, const uint32_t* bkeys,
+                                                  long long rld) {
   constexpr int NW = NT / kWave;
   __shared__ TopkShared<NT> sm;
   __shared__ __attribute__((aligned(16))) uint32_t blist[kBoundaryCap];
+  __shared__ int boff[kMaxChunks + 1];  // region offsets of the concatenated list
   const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int n = row_length(a, row);
@@ -685,18 +694,46 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
         }
     return;
   }
-  // ---- tau and need_eq from the boundary list
-  const int cb = (int)bcount[row];
+  // ---- per-chunk counts (all issued together), then the region offsets
+  const int nc = (n + kChunk - 1) / kChunk;
   const int rem = (int)rec[row].rem;
+  int gt_before = 0;
+  for (int c0 = 0; c0 < nc; c0 += NT) {
+    const int c = c0 + tid;
+    const int bc = c < nc ? bcnt[(size_t)row * nch + c] : 0;
+    if (c < chunk) gt_before += gcnt[(size_t)row * nch + c];
+    int tot_c;
+    const int inc = block_scan<NT>(bc, sm, &tot_c);
+    if (c < nc) boff[c + 1] = (c0 > 0 ? boff[c0] : 0) + inc;
+    if (c0 == 0 && tid == 0) boff[0] = 0;
+    __syncthreads();
+  }
+  const int cb = boff[nc];
   const uint32_t* gk = bkeys + (size_t)row * rld;
-  const int32_t* gp = bpos + (size_t)row * rld;
+  // list item i lives in region c = the last with boff[c] <= i
+  auto item = [=](int i) -> uint32_t {
+    int lo = 0, hi = nc - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (boff[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    return gk[(size_t)lo * kChunk + (i - boff[lo])];
+  };
   const bool in_lds = cb <= kBoundaryCap;
   uint32_t lo = 0xffffffffu, hi = 0u;
-  for (int i = tid; i < cb; i += NT) {
-    const uint32_t x = gk[i];
-    if (in_lds) blist[i] = x;
-    lo = min(lo, x);
-    hi = max(hi, x);
+  if (in_lds) {
+    for (int i = tid; i < cb; i += NT) {
+      const uint32_t x = item(i);
+      blist[i] = x;
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
+  } else {
+    for (int i = tid; i < cb; i += NT) {
+      const uint32_t x = item(i);
+      lo = min(lo, x);
+      hi = max(hi, x);
+    }
   }
   block_minmax<NT>(lo, hi, sm);  // synchronises
   uint32_t tau;
@@ -709,22 +746,19 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
     __syncthreads();
     rank_in_list<NT>(cb, rem, sm, tau, need_eq);
   } else if (in_lds) {
-    auto key_at = [&](int i) { return blist[i]; };
+    auto key_at = [=](int i) { return blist[i]; };
     radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
   } else {
-    auto key_at = [=](int i) { return gk[i]; };
-    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
+    radix_threshold<NT>(item, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
   }
-  // ---- kept items before this chunk: above-bin counts of earlier chunks, plus
-  // the boundary items before s0 that are > tau or == tau
-  int gt_before = 0, eq_before = 0;
-  for (int c = tid; c < chunk; c += NT) gt_before += gcnt[(size_t)row * nch + c];
-  for (int i = tid; i < cb; i += NT) {
-    if (gp[i] < s0) {
-      const uint32_t x = in_lds ? blist[i] : gk[i];
-      gt_before += x > tau ? 1 : 0;
-      eq_before += x == tau ? 1 : 0;
-    }
+  // ---- kept items before this chunk: above-bin counts of earlier chunks,
+  // plus the boundary items of earlier regions that are > tau or == tau
+  int eq_before = 0;
+  const int before = boff[chunk];
+  for (int i = tid; i < before; i += NT) {
+    const uint32_t x = in_lds ? blist[i] : item(i);
+    gt_before += x > tau ? 1 : 0;
+    eq_before += x == tau ? 1 : 0;
   }
   gt_before = (int)wave_total_u32((uint32_t)gt_before);
   eq_before = (int)wave_total_u32((uint32_t)eq_before);
@@ -1139,11 +1173,10 @@ hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLo
                            ws.nmm, ws.ghist);
   if (e != hipSuccess) return e;
   e = cx.launch("topk_count", k_long_count<kLongNT>, grid, dim3(kLongNT), 0, a, ws.rmm, ws.nmm,
-                (const uint32_t*)ws.ghist, ws.bcount, rec, ws.gcnt, nch, ws.bkeys, ws.bpos, rld);
+                (const uint32_t*)ws.ghist, rec, ws.gcnt, ws.bcnt, nch, ws.bkeys, rld);
   if (e != hipSuccess) return e;
   return cx.launch("topk_emit", k_long_emit<kLongNT>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,
-                   (const uint32_t*)ws.bcount, (const int32_t*)ws.gcnt, nch, (const uint32_t*)ws.bkeys,
-                   (const int32_t*)ws.bpos, rld);
+                   (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch, (const uint32_t*)ws.bkeys, rld);
 }
 
 hipError_t launch_topk_range(const LaunchCtx& cx, const TopkArgs& a, uint32_t* rmm_out,
