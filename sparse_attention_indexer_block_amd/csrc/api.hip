@@ -497,14 +497,16 @@ misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx,
   int32_t* cand = at<int32_t>(ws, pl.cand);
   int32_t* ncand = at<int32_t>(ws, pl.ncand);
   const int ncmax = (long long)pl.mm * p->B < p->L ? pl.mm * p->B : p->L;  // candidate bound
-  HIP_TRY(launch_expand_blocks(cx, blocks, nblocks, pl.mm, p->pos, p->L, p->B, p->T, cand,
-                               pl.cand_ld, ncand),
-          "block expansion");
+  // the refine pass forms the candidate list (indices and counts) from the blocks
   ScoreArgs sa = score_args(p);
-  sa.cand = cand;
+  sa.blocks = blocks;
+  sa.blocks_ld = pl.mm;
+  sa.nblocks = nblocks;
+  sa.B = p->B;
+  sa.cand_out = cand;
+  sa.ncand_out = ncand;
   sa.cand_ld = pl.cand_ld;
   sa.cand_max = ncmax;
-  sa.ncand = ncand;
   sa.S = at<float>(ws, pl.S2);
   sa.S_ld = pl.S2_ld;
   HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "refine scoring");

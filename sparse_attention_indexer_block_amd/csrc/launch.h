@@ -82,6 +82,15 @@ struct ScoreArgs {
   long long cand_ld;
   int cand_max;          // gather mode: bound on ncand[t]
   const int32_t* ncand;  // gather mode: [T] candidate counts
+  // gather mode with a block list instead of cand/ncand: the candidates are the
+  // visible keys of blocks[t, 0:nblocks[t]] (ascending, size B); their indices
+  // and counts are written to cand_out [T, cand_ld] and ncand_out [T]
+  const int32_t* blocks;
+  long long blocks_ld;
+  const int32_t* nblocks;
+  int B;
+  int32_t* cand_out;
+  int32_t* ncand_out;
   float* S;              // output rows
   long long S_ld;
   uint32_t* rmm;         // optional [nsplit, T, 2] per-split {min, max} score key of each row
@@ -99,7 +108,8 @@ struct ScoreArgs {
 // key splits (rows of rmm) is returned in *nsplit_out.
 int score_max_splits();
 hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* nsplit_out);
-// Dense scores of gathered keys: S[t, j] = I_all(t, cand[t, j]) for j < ncand[t].
+// Dense scores of gathered keys: S[t, j] = I_all(t, cand[t, j]) for j < ncand[t]
+// (cand either given, or formed from a block list).
 hipError_t launch_score_gather(const LaunchCtx& cx, ScoreArgs a, bool fp8);
 
 // ---- selection (topk_kernels.hip)
@@ -149,8 +159,6 @@ hipError_t launch_topk_range(const LaunchCtx& cx, const TopkArgs& a, uint32_t* r
                              uint32_t* zero, long long zero_n, int max_n);
 
 hipError_t launch_fill_u32(const LaunchCtx& cx, uint32_t* p, size_t n, uint32_t v);
-hipError_t launch_expand_blocks(const LaunchCtx& cx, const int32_t* blocks, const int32_t* nblocks,
-                                int m, const int32_t* pos, int L, int B, int T, int32_t* cand,
-                                long long cand_ld, int32_t* ncand);
+
 
 }  // namespace misa

@@ -282,23 +282,27 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
 // each wave loads its own B fragments straight from global memory: no LDS, no
 // barriers, D groups of 16 keys in flight per wave. Lane l covers key
 // (l mod 16) of a group and head dims [32*(l/16), 32*(l/16) + 32).
-template <int AP, int RPW, bool FP8, bool GATHER>
+template <int AP, int RPW, int WR, bool FP8, bool GATHER>
 __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
-  constexpr int ROWS = RPW * 16;
+  constexpr int WC = 4 / WR;                        // key groups per tile (waves sharing rows)
+  constexpr int ROWS = WR * RPW * 16;               // rows per workgroup
   constexpr int QW = ROWS / AP;                     // queries per workgroup
   constexpr int TPQ = AP >= 16 ? AP / 16 : 1;       // row tiles per query
   constexpr int NQ = RPW / TPQ;                     // query slots per lane
   constexpr int D = (RPW >= 8 && !FP8) ? 2 : 4;     // key groups in flight per wave
   constexpr int NV = FP8 ? 2 : 4;                   // 16-byte loads per lane per group
-  constexpr int KT = 64;                            // keys per tile (4 waves x 16)
+  constexpr int KT = 16 * WC;                       // keys per tile
+  static_assert(WR == 1 || WR == 2 || WR == 4, "WR must divide the four waves");
   static_assert(AP >= 4 && (AP & (AP - 1)) == 0, "AP must be a power of two >= 4");
   static_assert(ROWS % AP == 0 && QW >= 1, "row tiles must hold whole queries");
   static_assert(AP < 16 || RPW % TPQ == 0, "a wave must hold whole queries");
+  static_assert(WR == 1 || RPW * 16 % AP == 0, "row waves must hold whole queries");
   static_assert(!GATHER || QW == 1, "gather mode scores one query per workgroup");
 
   __shared__ int qn[QW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave / WC, wc = wave % WC;  // row group and key group of this wave
   const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
   const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
 
@@ -307,7 +311,21 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   if (tid < QW) {
     const int t = g * QW + tid;
     int nn = 0;
-    if (t < p.T) nn = GATHER ? p.ncand[t] : visible_len(p.pos[t], p.L);
+    if (t < p.T) {
+      if (GATHER && p.blocks) {
+        // candidates = the visible keys of the listed blocks (ascending); only
+        // the last listed block can be the query's partial last block
+        const int nb = p.nblocks[t];
+        if (nb > 0) {
+          const int last = p.blocks[(size_t)t * p.blocks_ld + nb - 1];
+          const long long tail = (long long)visible_len(p.pos[t], p.L) - (long long)last * p.B;
+          nn = (nb - 1) * p.B + (int)(tail < p.B ? tail : p.B);
+        }
+        if (split == 0) p.ncand_out[t] = nn;
+      } else {
+        nn = GATHER ? p.ncand[t] : visible_len(p.pos[t], p.L);
+      }
+    }
     qn[tid] = nn;
   }
   __syncthreads();
@@ -324,15 +342,21 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     }
     return;
   }
-  const int ngroups = tile1 - tile0;  // this wave's groups: one per tile, key offset 16*wave
+  const int ngroups = tile1 - tile0;  // this wave's groups: one per tile, key offset 16*wc
   const int qt0 = g * QW;
   const int kcol = lane & 15;
   const int slice = lane >> 4;
 
   auto key_of = [&](int gi) -> int {
-    const int col = (tile0 + gi) * KT + 16 * wave + kcol;
+    const int col = (tile0 + gi) * KT + 16 * wc + kcol;
     if constexpr (GATHER) {
-      return col < qn[0] ? p.cand[(size_t)qt0 * p.cand_ld + col] : -1;
+      if (col >= qn[0]) return -1;
+      if (p.blocks) {
+        const int key = p.blocks[(size_t)qt0 * p.blocks_ld + col / p.B] * p.B + col % p.B;
+        if (slice == 0) p.cand_out[(size_t)qt0 * p.cand_ld + col] = key;  // for the selection
+        return key;
+      }
+      return p.cand[(size_t)qt0 * p.cand_ld + col];
     } else {
       return col < p.L ? col : -1;
     }
@@ -366,7 +390,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     {
-      const int row = r * 16 + (lane & 15);
+      const int row = (wr * RPW + r) * 16 + (lane & 15);
       const int qi = row / AP, j = row % AP, t = g * QW + qi;
       if (t < p.T && j < p.A) {
         const bf16x8* src = reinterpret_cast<const bf16x8*>(
@@ -380,7 +404,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = r * 16 + 4 * slice + i;
+      const int row = (wr * RPW + r) * 16 + 4 * slice + i;
       const int qi = row / AP, j = row % AP, t = g * QW + qi;
       wv[r][i] = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
     }
@@ -396,7 +420,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   float smin[NQ], smax[NQ];
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
-    const int rt0 = s * TPQ;
+    const int rt0 = wr * RPW + s * TPQ;
     const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * slice) / AP;
     const int t = g * QW + qi;
     q_n[s] = writer ? qn[qi] : 0;
@@ -428,7 +452,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
       }
       float kscale = ksv[d];
       const int key = keyv[d];
-      const int col = (tile0 + gi) * KT + 16 * wave + kcol;
+      const int col = (tile0 + gi) * KT + 16 * wc + kcol;
       if (gi + D < ngroups) load_group(gi + D, d);
 
       f32x4 acc[RPW];
@@ -472,8 +496,8 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   }
 
   if (!GATHER && p.rmm) {
-    // per query: lanes of one wave reduce, then the four waves meet in LDS
-    __shared__ float rlo[4][QW], rhi[4][QW];
+    // per query: lanes of one wave reduce, then the key groups meet in LDS
+    __shared__ float rlo[WC][QW], rhi[WC][QW];
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
       float lo = smin[s], hi = smax[s];
@@ -482,18 +506,18 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
         lo = fminf(lo, __shfl_xor(lo, off, kWave));
         hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
       }
-      const int rt0 = s * TPQ;
+      const int rt0 = wr * RPW + s * TPQ;
       const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * slice) / AP;
       if (writer && (lane & 15) == 0) {
-        rlo[wave][qi] = lo;
-        rhi[wave][qi] = hi;
+        rlo[wc][qi] = lo;
+        rhi[wc][qi] = hi;
       }
     }
     __syncthreads();
     if (tid < QW && g * QW + tid < p.T) {
       float lo = rlo[0][tid], hi = rhi[0][tid];
 #pragma unroll
-      for (int w2 = 1; w2 < 4; ++w2) {
+      for (int w2 = 1; w2 < WC; ++w2) {
         lo = fminf(lo, rlo[w2][tid]);
         hi = fmaxf(hi, rhi[w2][tid]);
       }
@@ -548,17 +572,17 @@ static hipError_t run_score(const LaunchCtx& cx, ScoreArgs a, bool fp8, const ch
   return cx.launch(name, k_score<AP, WR, RPW, CPW, false, GATHER>, grid, dim3(256), 0, a);
 }
 
-template <int AP, int RPW, bool GATHER>
+template <int AP, int RPW, int WR, bool GATHER>
 static hipError_t run_direct(const LaunchCtx& cx, ScoreArgs a, bool fp8, const char* name,
                              int* nsplit_out) {
-  constexpr int QW = RPW * 16 / AP;
-  constexpr int KT = 64;
+  constexpr int QW = WR * RPW * 16 / AP;
+  constexpr int KT = 16 * (4 / WR);
   const long long max_cols = GATHER ? (long long)a.cand_max : (long long)a.L;
   const int tiles = (int)((max_cols + KT - 1) / KT);
   const int groups = GATHER ? a.T : (a.T + QW - 1) / QW;
   const int target = a.target_wgs > 0 ? a.target_wgs : 512;
   int splits = (target + groups - 1) / groups;
-  const int min_tiles = a.target_wgs > 0 ? 1 : 4;  // four 16-key groups per wave by default
+  const int min_tiles = a.target_wgs > 0 ? 1 : 4;  // four key groups per wave by default
   if (splits > (tiles + min_tiles - 1) / min_tiles) splits = (tiles + min_tiles - 1) / min_tiles;
   if (splits < 1) splits = 1;
   a.tiles_per_split = (tiles + splits - 1) / splits;
@@ -568,17 +592,31 @@ static hipError_t run_direct(const LaunchCtx& cx, ScoreArgs a, bool fp8, const c
   a.nsplit = splits;
   if (nsplit_out) *nsplit_out = splits;
   const dim3 grid = GATHER ? dim3(splits, groups) : dim3(groups, splits);
-  if (fp8) return cx.launch(name, k_score_direct<AP, RPW, true, GATHER>, grid, dim3(256), 0, a);
-  return cx.launch(name, k_score_direct<AP, RPW, false, GATHER>, grid, dim3(256), 0, a);
+  if (fp8) return cx.launch(name, k_score_direct<AP, RPW, WR, true, GATHER>, grid, dim3(256), 0, a);
+  return cx.launch(name, k_score_direct<AP, RPW, WR, false, GATHER>, grid, dim3(256), 0, a);
 }
 
-// Row tiles (of 16 rows) that cover every query of a decode batch in one wave.
-static int direct_rpw(long long rows) {
-  if (rows <= 16) return 1;
-  if (rows <= 32) return 2;
-  if (rows <= 64) return 4;
-  if (rows <= 128) return 8;
-  return 0;  // too many rows for one wave: use the LDS-tiled kernel
+// Decode batches: every routed row of the batch in one workgroup, up to four
+// row tiles (64 rows) per wave; the four waves split the rows (WR groups) and
+// the keys (4 / WR groups). Returns false when the batch is too large.
+template <int AP>
+static bool direct_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, long long rows, int* nsplit_out,
+                        hipError_t* err) {
+  const char* nm = "score_keys";
+  if (AP <= 16 && rows <= 16) {
+    *err = run_direct<AP <= 16 ? AP : 16, 1, 1, false>(cx, a, fp8, nm, nsplit_out);
+  } else if (AP <= 32 && rows <= 32) {
+    *err = run_direct<AP <= 32 ? AP : 32, 2, 1, false>(cx, a, fp8, nm, nsplit_out);
+  } else if (rows <= 64) {
+    *err = run_direct<AP, 4, 1, false>(cx, a, fp8, nm, nsplit_out);
+  } else if (rows <= 128) {
+    *err = run_direct<AP, 4, 2, false>(cx, a, fp8, nm, nsplit_out);
+  } else if (rows <= 256) {
+    *err = run_direct<AP, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
+  } else {
+    return false;
+  }
+  return true;
 }
 
 hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* nsplit_out) {
@@ -587,52 +625,24 @@ hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* ns
   const long long rows = (long long)a.T * ap;
   // Prefill-like batches (many queries whose prefixes grow) go heavy-first.
   a.reverse = 1;
-  const int rpw = direct_rpw(rows);
   const char* nm = "score_keys";
-  if (rpw > 0 && (ap < 16 || rpw * 16 >= ap)) {
-    switch (ap) {
-      case 4:
-        if (rpw == 1) return run_direct<4, 1, false>(cx, a, fp8, nm, nsplit_out);
-        if (rpw == 2) return run_direct<4, 2, false>(cx, a, fp8, nm, nsplit_out);
-        if (rpw == 4) return run_direct<4, 4, false>(cx, a, fp8, nm, nsplit_out);
-        return run_direct<4, 8, false>(cx, a, fp8, nm, nsplit_out);
-      case 8:
-        if (rpw == 1) return run_direct<8, 1, false>(cx, a, fp8, nm, nsplit_out);
-        if (rpw == 2) return run_direct<8, 2, false>(cx, a, fp8, nm, nsplit_out);
-        if (rpw == 4) return run_direct<8, 4, false>(cx, a, fp8, nm, nsplit_out);
-        return run_direct<8, 8, false>(cx, a, fp8, nm, nsplit_out);
-      case 16:
-        if (rpw == 1) return run_direct<16, 1, false>(cx, a, fp8, nm, nsplit_out);
-        if (rpw == 2) return run_direct<16, 2, false>(cx, a, fp8, nm, nsplit_out);
-        if (rpw == 4) return run_direct<16, 4, false>(cx, a, fp8, nm, nsplit_out);
-        return run_direct<16, 8, false>(cx, a, fp8, nm, nsplit_out);
-      case 32:
-        if (rpw <= 2) return run_direct<32, 2, false>(cx, a, fp8, nm, nsplit_out);
-        if (rpw == 4) return run_direct<32, 4, false>(cx, a, fp8, nm, nsplit_out);
-        return run_direct<32, 8, false>(cx, a, fp8, nm, nsplit_out);
-      default:
-        if (rpw <= 4) return run_direct<64, 4, false>(cx, a, fp8, nm, nsplit_out);
-        return run_direct<64, 8, false>(cx, a, fp8, nm, nsplit_out);
-    }
-  }
+  hipError_t err = hipSuccess;
+  bool done = false;
   switch (ap) {
-    case 4:
-      if (rows <= 64) return run_score<4, 4, 1, 4, false>(cx, a, fp8, nm, nsplit_out);
-      if (rows <= 128) return run_score<4, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
-      return run_score<4, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    case 8:
-      if (rows <= 64) return run_score<8, 4, 1, 4, false>(cx, a, fp8, nm, nsplit_out);
-      if (rows <= 128) return run_score<8, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
-      return run_score<8, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    case 16:
-      if (rows <= 64) return run_score<16, 4, 1, 4, false>(cx, a, fp8, nm, nsplit_out);
-      if (rows <= 128) return run_score<16, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
-      return run_score<16, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    case 32:
-      if (rows <= 128) return run_score<32, 4, 2, 4, false>(cx, a, fp8, nm, nsplit_out);
-      return run_score<32, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    default:
-      return run_score<64, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
+    case 4: done = direct_keys<4>(cx, a, fp8, rows, nsplit_out, &err); break;
+    case 8: done = direct_keys<8>(cx, a, fp8, rows, nsplit_out, &err); break;
+    case 16: done = direct_keys<16>(cx, a, fp8, rows, nsplit_out, &err); break;
+    case 32: done = direct_keys<32>(cx, a, fp8, rows, nsplit_out, &err); break;
+    default: done = direct_keys<64>(cx, a, fp8, rows, nsplit_out, &err); break;
+  }
+  if (done) return err;
+  // larger batches (prefill): LDS-staged key tiles shared by 256 rows
+  switch (ap) {
+    case 4: return run_score<4, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
+    case 8: return run_score<8, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
+    case 16: return run_score<16, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
+    case 32: return run_score<32, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
+    default: return run_score<64, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
   }
 }
 
@@ -647,11 +657,11 @@ hipError_t launch_score_gather(const LaunchCtx& cx, ScoreArgs a, bool fp8) {
     case 4:
     case 8:
     case 16:
-      return run_direct<16, 1, true>(cx, a, fp8, nm, nullptr);
+      return run_direct<16, 1, 1, true>(cx, a, fp8, nm, nullptr);
     case 32:
-      return run_direct<32, 2, true>(cx, a, fp8, nm, nullptr);
+      return run_direct<32, 2, 1, true>(cx, a, fp8, nm, nullptr);
     default:
-      return run_direct<64, 4, true>(cx, a, fp8, nm, nullptr);
+      return run_direct<64, 4, 1, true>(cx, a, fp8, nm, nullptr);
   }
 }
 

@@ -1106,42 +1106,6 @@ __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
     p[i] = v;
 }
 
-// HISA Stage 2 candidate list: the visible tokens of the chosen blocks, in
-// ascending order (blocks arrive ascending).
-__global__ __launch_bounds__(256) void k_expand_blocks(const int32_t* blocks, const int32_t* nblocks,
-                                                       int m, const int32_t* pos, int L, int B,
-                                                       int32_t* cand, long long cand_ld,
-                                                       int32_t* ncand) {
-  __shared__ int offs[1025];
-  const int t = blockIdx.x;
-  const int n = visible_len(pos[t], L);
-  const int nb = min(nblocks[t], 1024);
-  const int32_t* bl = blocks + (size_t)t * m;
-  auto size_of = [&](int j) {
-    const long long s0 = (long long)bl[j] * B;
-    return (int)(n - s0 < B ? n - s0 : B);
-  };
-  if (threadIdx.x == 0) {
-    int off = 0;
-    for (int j = 0; j < nb; ++j) {
-      offs[j] = off;
-      off += size_of(j);
-    }
-    offs[nb] = off;
-    ncand[t] = off;
-  }
-  __syncthreads();
-  const int total = offs[nb];
-  for (int i = threadIdx.x; i < total; i += 256) {
-    int lo = 0, hi = nb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (offs[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    cand[(size_t)t * cand_ld + i] = (int32_t)((long long)bl[lo] * B + (i - offs[lo]));
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Host launchers.
 
@@ -1194,13 +1158,5 @@ hipError_t launch_fill_u32(const LaunchCtx& cx, uint32_t* p, size_t n, uint32_t 
   return cx.launch("fill", k_fill_u32, dim3((unsigned)blocks), dim3(256), 0, p, n, v);
 }
 
-hipError_t launch_expand_blocks(const LaunchCtx& cx, const int32_t* blocks, const int32_t* nblocks,
-                                int m, const int32_t* pos, int L, int B, int T, int32_t* cand,
-                                long long cand_ld, int32_t* ncand) {
-  if (T == 0) return hipSuccess;
-  if (m > 1024) return hipErrorInvalidValue;
-  return cx.launch("expand_blocks", k_expand_blocks, dim3(T), dim3(256), 0, blocks, nblocks, m, pos,
-                   L, B, cand, cand_ld, ncand);
-}
 
 }  // namespace misa
