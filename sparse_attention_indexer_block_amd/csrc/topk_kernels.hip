@@ -1027,37 +1027,47 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
     const int rem = sm.rem;
     const int c = (int)sm.hist[bstar];
     if (c <= kListCap) {
-      // the threshold bin's keys, in no particular order
-      if (tid == 0) sm.nlist = 0;
-      __syncthreads();
+      // the threshold bin's keys (in item order): straight into sm.list when
+      // few enough to rank pairwise, else into cand for radix digits
+      uint32_t* dst = c <= kRankCap ? sm.list : cand;
+      uint64_t km[G][4];
+      int nw = 0;
       uint32_t clo = 0xffffffffu, chi = 0u;
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool keep = in[g][e] && lin_bin(u[g][e], xlo, scale, kFineBins) == bstar;
-          const uint64_t m = wave_ballot(keep);
-          if (m) {
-            int at = 0;
-            if (lane == 0) at = atomicAdd(&sm.nlist, __popcll(m));
-            at = __shfl(at, 0, kWave);
-            if (keep) cand[at + lanes_below(m)] = u[g][e];
-          }
+          km[g][e] = wave_ballot(keep);
+          nw += __popcll(km[g][e]);
           if (keep) {
             clo = min(clo, u[g][e]);
             chi = max(chi, u[g][e]);
           }
         }
-      block_minmax<NT>(clo, chi, sm);  // synchronises (cand complete)
+      if (lane == 0) sm.wgt[w] = nw;
+      __syncthreads();
+      int at = 0;
+      for (int i = 0; i < w; ++i) at += sm.wgt[i];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((km[g][e] >> lane) & 1ull) dst[at + lanes_below(km[g][e])] = u[g][e];
+          at += __popcll(km[g][e]);
+        }
+      if (rem >= c || c > kRankCap) {
+        block_minmax<NT>(clo, chi, sm);  // synchronises (the list is complete)
+      } else {
+        __syncthreads();
+      }
       if (rem >= c) {
         tau = sm.umin;  // the whole bin is kept
         need_eq = c;
       } else if (c <= kRankCap) {
-        for (int i = tid; i < c; i += NT) sm.list[i] = cand[i];
-        __syncthreads();
         rank_in_list<NT>(c, rem, sm, tau, need_eq);
       } else {
-        auto key_at = [&](int i) { return cand[i]; };
+        auto key_at = [=](int i) { return cand[i]; };
         radix_threshold<NT>(key_at, c, rem, sm.umin, sm.umax, sm, tau, need_eq);
       }
     } else {
