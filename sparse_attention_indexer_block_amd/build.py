@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmisa.so")
-SOURCES = ["route_kernels.hip", "score_kernels.hip", "topk_kernels.hip", "api.hip"]
+SOURCES = ["route_kernels.hip", "route_fast.hip", "score_kernels.hip", "topk_kernels.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

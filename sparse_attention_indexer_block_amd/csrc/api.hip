@@ -72,7 +72,7 @@ struct Bump {
 };
 
 struct Plan {
-  size_t ksum = 0, tsum = 0, pmax = 0, heads = 0, beta = 0, qr = 0, wr = 0;
+  size_t ksum = 0, tsum = 0, pmax = 0, kb16 = 0, part = 0, heads = 0, beta = 0, qr = 0, wr = 0;
   size_t S = 0;
   size_t rmm = 0, ghist = 0, rec = 0, gcnt = 0, bcnt = 0, bkeys = 0;
   size_t cand = 0, ncand = 0, S2 = 0, blocks = 0, nblocks = 0;
@@ -105,6 +105,10 @@ static void plan_route(Bump& bp, Plan& pl, const misa_problem* p) {
   pl.ksum = bp.take((size_t)M * 128 * 8);
   pl.tsum = bp.take((size_t)p->T * 128 * 8);
   pl.pmax = bp.take((size_t)p->T * (route_chunks(p->L, p->B) + 1) * 64 * 8);  // tile maxima + last block
+  if (route_fast_wins(p->L, p->B, p->T)) {
+    pl.kb16 = bp.take((size_t)M * 2 * 128 * 2);
+    pl.part = bp.take((size_t)p->T * route_fast_parts(p->L, p->B, p->T) * 64 * route_part_bytes());
+  }
 }
 
 static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, int m) {
@@ -239,13 +243,23 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   double* ksum = at<double>(ws, pl.ksum);
   double* tsum = at<double>(ws, pl.tsum);
   double* pmax = at<double>(ws, pl.pmax);
+  // many queries: a bf16 MFMA pass over hi/lo block means, settled in float64 where it is
+  // ambiguous; few queries: every block's rho in float64 directly
+  const bool fast = !beta && route_fast_wins(p->L, p->B, p->T);
+  uint16_t* kb16 = fast ? at<uint16_t>(ws, pl.kb16) : nullptr;
   // with cached block means only each query's last block is pooled here
   HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
-                            p->kbar != nullptr),
+                            p->kbar != nullptr, kb16),
           "block sums");
-  HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, pmax,
-                       heads, r, beta, beta_ld, qr, wr),
-          "router");
+  if (!fast) {
+    HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, pmax,
+                         heads, r, beta, beta_ld, qr, wr),
+            "router");
+  } else {
+    HIP_TRY(launch_route_heads(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, kb16, p->kbar,
+                               tsum, at<void>(ws, pl.part), heads, r, qr, wr),
+            "router");
+  }
   return MISA_OK;
 }
 

@@ -59,6 +59,19 @@ __device__ __forceinline__ float key_score(uint32_t u) {
   return __uint_as_float(b);
 }
 
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// A float64 value as bf16 hi + lo (hi = bf16(float(m)), lo = bf16(float(m - hi)));
+// |m - hi - lo| <= 2^-17.9 |m|.
+__device__ __forceinline__ void split_bf16(double m, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_rne((float)m);
+  lo = bf16_rne((float)(m - (double)bf16_bits_to_f32(hi)));
+}
+
 // Number of set bits of `mask` in lanes below the calling lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -54,7 +54,19 @@ inline long long padded_ld(long long n) { return ((n + 63) / 64) * 64; }
 // tsum is given, the sum of each query's last (possibly partial) block.
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum, bool tails_only = false);
+                             double* tsum, bool tails_only = false, uint16_t* kb16 = nullptr);
+// MISA head routing with an exact result (route_fast.hip): bf16 block scores
+// with proven error bounds, then float64 settling of every head's maximum.
+// part: T * route_fast_parts(L, B, T) * 64 records of route_part_bytes();
+// kb16 [M][2][128] bf16 hi / lo block means (from launch_block_sums), or kbar.
+int route_fast_parts(int L, int B, int T);
+// true when the two-pass router pays off (many queries times many block tiles)
+bool route_fast_wins(int L, int B, int T);
+size_t route_part_bytes();
+hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
+                              int T, int H, int L, int B, int A, const double* ksum, const uint16_t* kb16,
+                              const float* kbar, const double* tsum, void* part, int32_t* heads,
+                              float* r_out, uint16_t* qr, float* wr);
 // Router tiles of 16 blocks; the pmax workspace holds T * (route_chunks + 1) * 64 doubles.
 int route_chunks(int L, int B);
 // Router: heads[T,A] (ascending), optional r[T,H], optional HISA block scores

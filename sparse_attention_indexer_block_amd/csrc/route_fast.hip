@@ -1,0 +1,431 @@
+// MISA head routing (MISA technical summary, "Metodologia: MISA": the router
+// scores every indexer head against the mean-pooled key blocks and keeps the
+// best h heads) in two steps that give the same head set as an exact
+// evaluation:
+//
+//  1. k_route_fast: rho~(t,h,b) = q[t,h] . (hi_b + lo_b) with bf16 matrix
+//     products, where hi_b + lo_b is the block mean split into two bf16
+//     terms, plus a proven bound err(t,h,b) >= |rho~ - rho| from a third
+//     product |q| . |hi_b|. Per (query, head) it keeps, over the complete
+//     blocks before the query's last one, the largest and second-largest
+//     rho~, the block of the largest and the largest bound, per range of
+//     TPW block tiles.
+//  2. k_route_exact: per (query, head) the maximum of rho over those blocks is
+//     settled in float64: only blocks whose rho~ lies within twice the bound
+//     of the largest rho~ can hold the maximum, and only those are evaluated
+//     exactly (usually the leader alone); every rho~ is provably negative
+//     when the largest is below -bound (maximum 0 after the ReLU). The
+//     query's last block is always evaluated exactly.
+//     Then r(t,h) = w[t,h] * max(0, max_b rho) and the first A heads under
+//     (-r, h), as the float64 router would pick them.
+//
+// Bound: hi = bf16(float(m)) and lo = bf16(float(m - hi)) leave
+// |m - hi - lo| <= 2^-17.9 |m| per dim, and the float accumulation of the 256
+// exact bf16 products of a 16x16x32 chain errs by at most 256 * 2^-24 of
+// their absolute sum; both are below 2^-15 * sum_d |q_d| |m_d|, and the bound
+// used is 2^-14 * |q|.|hi| (|hi| within 2^-8 of |m|), leaving a factor of two.
+#include "device_common.h"
+#include "launch.h"
+
+namespace misa {
+
+constexpr int kFastTile = 16;  // blocks per MFMA column tile
+
+struct RoutePart {
+  float best;    // largest rho~ over the complete blocks seen
+  float second;  // second largest
+  float err;     // largest bound over those blocks
+  int arg;       // block of the largest (-1: none)
+};
+
+// Merge (best, second, err, arg) of another set of blocks into ours.
+__device__ __forceinline__ void merge_part(float& b, float& s, float& e, int& a, float b2, float s2,
+                                           float e2, int a2) {
+  const float lo = fminf(b, b2);
+  s = fmaxf(fmaxf(s, s2), lo);
+  if (b2 > b || (b2 == b && a2 >= 0 && (a < 0 || a2 < a))) a = a2;
+  b = fmaxf(b, b2);
+  e = fmaxf(e, e2);
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_merge(float& b, float& s, float& e, int& a) {
+  const float b2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), CTRL, 0xf, 0xf, false));
+  const float s2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), CTRL, 0xf, 0xf, false));
+  const float e2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e), CTRL, 0xf, 0xf, false));
+  const int a2 = __builtin_amdgcn_update_dpp(0, a, CTRL, 0xf, 0xf, false);
+  merge_part(b, s, e, a, b2, s2, e2, a2);
+}
+
+// grid (ntr, ceil(T / QG)), 256 threads: workgroup tr covers block tiles
+// [tr * TPW, tr * TPW + TPW) of QG queries; wave w takes heads [16w, 16w+16).
+// v_mfma_f32_16x16x32_bf16 with rows = heads, columns = blocks; lane l feeds
+// head / block l % 16 with dims [32(l/16), 32(l/16) + 32) over the four K
+// steps, and holds rows 4(l/16) + i of column l % 16 of the result.
+// kb16 [M][2][128] holds the hi / lo split of every block mean; without it
+// (cached means) the split is formed here from kbar.
+template <int QG, int TPW>
+__global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int32_t* pos, int T, int H,
+                                                    int L, int B, int ntr, const uint16_t* kb16,
+                                                    const float* kbar, RoutePart* part) {
+  const int tr = blockIdx.x, tq0 = blockIdx.y * QG;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g = lane >> 4;
+  const int M = (int)(((long long)L + B - 1) / B);
+  const int h_a = kFastTile * wv + col;
+  int nfull[QG];  // complete blocks before each query's last block
+  bf16x8 qa[QG][4];
+#pragma unroll
+  for (int i = 0; i < QG; ++i) {
+    const int t = tq0 + i;
+    const int n = t < T ? visible_len(pos[t], L) : 0;
+    const int Mt = (int)(((long long)n + B - 1) / B);
+    nfull[i] = Mt > 0 ? Mt - 1 : 0;
+    const bool ok = t < T && h_a < H;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)(ok ? t : 0) * H + (ok ? h_a : 0)) * kHeadDim + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[i][s] = __builtin_bit_cast(bf16x8, ok ? src[s] : u32x4{0u, 0u, 0u, 0u});
+  }
+  float best[QG][4], second[QG][4], err[QG][4];
+  int arg[QG][4];
+#pragma unroll
+  for (int i = 0; i < QG; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      best[i][e] = -__builtin_huge_valf();
+      second[i][e] = -__builtin_huge_valf();
+      err[i][e] = 0.f;
+      arg[i][e] = -1;
+    }
+
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int b0 = (tr * TPW + tt) * kFastTile;
+    if (b0 >= M) break;  // uniform
+    const int blk = b0 + col;
+    // B operands of this lane's block: hi, lo and |hi|, dims 32g .. 32g+31
+    bf16x8 bh[4], bl[4], ba[4];
+    if (blk < M) {
+      if (kb16) {
+        const u32x4* sh = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + 32 * g);
+        const u32x4* sl = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + kHeadDim + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 h4 = sh[s];
+          bh[s] = __builtin_bit_cast(bf16x8, h4);
+          bl[s] = __builtin_bit_cast(bf16x8, sl[s]);
+          ba[s] = __builtin_bit_cast(bf16x8, h4 & u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu});
+        }
+      } else {
+        const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)blk * kHeadDim + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const f32x4 x0 = src[2 * s], x1 = src[2 * s + 1];
+          u32x4 h4, l4;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            uint32_t ha, la, hb, lb;
+            split_bf16((double)(p < 2 ? x0[2 * p] : x1[2 * p - 4]), ha, la);
+            split_bf16((double)(p < 2 ? x0[2 * p + 1] : x1[2 * p - 3]), hb, lb);
+            h4[p] = ha | (hb << 16);
+            l4[p] = la | (lb << 16);
+          }
+          bh[s] = __builtin_bit_cast(bf16x8, h4);
+          bl[s] = __builtin_bit_cast(bf16x8, l4);
+          ba[s] = __builtin_bit_cast(bf16x8, h4 & u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu});
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bh[s] = bl[s] = ba[s] = bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+      if (b0 >= nfull[i]) continue;  // uniform: no complete block of this tile
+      f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = ah, aa = ah;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i][s], bh[s], ah, 0, 0, 0);
+        al = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i][s], bl[s], al, 0, 0, 0);
+        const u32x4 qabs = __builtin_bit_cast(u32x4, qa[i][s]) & u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
+        aa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qabs), ba[s], aa, 0, 0, 0);
+      }
+      if (blk < nfull[i]) {
+        // this lane's own block: running largest, second largest and bound
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = ah[e] + al[e];
+          second[i][e] = fmaxf(second[i][e], fminf(best[i][e], v));
+          if (v > best[i][e]) arg[i][e] = blk;
+          best[i][e] = fmaxf(best[i][e], v);
+          err[i][e] = fmaxf(err[i][e], ldexpf(aa[e], -14) + 1e-30f);
+        }
+      }
+    }
+  }
+  // the 16 lanes of a row group hold different blocks of the same heads
+#pragma unroll
+  for (int i = 0; i < QG; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dpp_merge<0x121>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:1
+      dpp_merge<0x122>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:2
+      dpp_merge<0x124>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:4
+      dpp_merge<0x128>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:8
+    }
+  if (col == 0) {
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+      const int t = tq0 + i;
+      if (t >= T) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        RoutePart r;
+        r.best = best[i][e];
+        r.second = second[i][e];
+        r.err = err[i][e];
+        r.arg = arg[i][e];
+        part[((size_t)t * ntr + tr) * kWave + kFastTile * wv + 4 * g + e] = r;
+      }
+    }
+  }
+}
+
+// Exact q . m_b in float64, q a 128-dim bf16 row in LDS (16-byte words) and
+// m_b the block mean ksum[b] / B or kbar[b]; the whole row of m_b is requested
+// at once.
+constexpr int kQStride = kHeadDim / 8 + 1;  // 16-byte words per q row in LDS (one pad word)
+
+// Dims [16 sub, 16 sub + 16) of rho(q, b) in float64; eight lanes (sub = 0..7) of one
+// group together cover the head dimension and their partials are summed by the caller.
+__device__ __forceinline__ double exact_rho_part(const u32x4* qrow, const double* ksum,
+                                                 const float* kbar, int b, int B, int sub) {
+  const u32x4 q0 = qrow[2 * sub], q1 = qrow[2 * sub + 1];
+  double acc = 0.0;
+  if (kbar) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)b * kHeadDim + 16 * sub);
+    f32x4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = src[i];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t qw = p < 4 ? q0[p] : q1[p - 4];
+      const f32x4 xx = x[p >> 1];
+      acc = fma((double)bf16_bits_to_f32(qw & 0xffffu), (double)xx[2 * (p & 1)], acc);
+      acc = fma((double)bf16_bits_to_f32(qw >> 16), (double)xx[2 * (p & 1) + 1], acc);
+    }
+    return acc;
+  }
+  const f64x2* src = reinterpret_cast<const f64x2*>(ksum + (size_t)b * kHeadDim + 16 * sub);
+  f64x2 k2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) k2[i] = src[i];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t qw = p < 4 ? q0[p] : q1[p - 4];
+    acc = fma((double)bf16_bits_to_f32(qw & 0xffffu), k2[p][0], acc);
+    acc = fma((double)bf16_bits_to_f32(qw >> 16), k2[p][1], acc);
+  }
+  return acc;
+}
+
+// Sum over the eight lanes of a group; every lane of the group receives the total.
+__device__ __forceinline__ double group8_sum(double v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  return v;
+}
+
+// Settles one candidate (head hh, block b) with the eight lanes of a group.
+__device__ __forceinline__ void settle_block(const u32x4* qs, const double* ksum, const float* kbar,
+                                             int hh, int b, int B, int sub,
+                                             unsigned long long* mbits) {
+  double rho = group8_sum(exact_rho_part(&qs[hh * kQStride], ksum, kbar, b, B, sub));
+  if (!kbar) rho = (B & (B - 1)) == 0 ? rho * (1.0 / (double)B) : rho / (double)B;
+  if (sub == 0 && rho > 0.0) atomicMax(&mbits[hh], (unsigned long long)__double_as_longlong(rho));
+}
+
+// One workgroup of 256 threads per query: settles max_b ReLU(rho) of every
+// head exactly, forms r(t,h) and keeps the first A heads under (-r, h).
+// A block can hold a head's maximum only if its rho~ is within twice the
+// head's bound of the largest rho~; such blocks are evaluated exactly: the
+// recorded leader of a block range, or the whole range when its runner-up
+// also comes that close. heads[t,:] is written in ascending order; with qr
+// the routed q rows and weights are packed in slot order for the scoring
+// kernel.
+constexpr int kWorkCap = 1024;              // exact-product work items held in LDS
+
+__global__ __launch_bounds__(256) void k_route_exact(const uint16_t* q, const float* w,
+                                                    const int32_t* pos, int H, int L, int B, int A,
+                                                    int ntr, int range_blocks, const RoutePart* part,
+                                                    const double* ksum, const float* kbar,
+                                                    const double* tsum, int32_t* heads,
+                                                    float* r_out, uint16_t* qr, float* wr) {
+  __shared__ u32x4 qs[kWave * kQStride];  // q[t, h, :] for every head
+  __shared__ float pb[4][kWave], pe[4][kWave];
+  __shared__ float gthr[kWave];           // per head: rho~ below this cannot be the maximum
+  __shared__ double ts[kHeadDim];
+  __shared__ double rs[kWave];
+  __shared__ unsigned long long mbits[kWave];  // settled max_b ReLU(rho) (bits of a double >= 0)
+  __shared__ int rank_part[4][kWave];
+  __shared__ int work_h[kWorkCap], work_b[kWorkCap];  // (head, block) pairs to evaluate exactly
+  __shared__ int n_work;
+  const int t = blockIdx.x, tid = threadIdx.x, h = tid & 63, j = tid >> 6;
+  const int n = visible_len(pos[t], L);
+  const int Mt = (int)(((long long)n + B - 1) / B);
+  const int nfull = Mt > 0 ? Mt - 1 : 0;
+  const bool active = h < H;
+  // everything independent of the partial results is requested first
+  const float wt = active ? w[(size_t)t * H + h] : 0.f;
+  if (tid < kHeadDim / 2)
+    reinterpret_cast<f64x2*>(ts)[tid] = reinterpret_cast<const f64x2*>(tsum + (size_t)t * kHeadDim)[tid];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + (size_t)t * H * kHeadDim);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u, row = i >> 4, v = i & 15;  // 64 rows of 16 words
+      qs[row * kQStride + v] = row < H ? src[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // global largest rho~ and bound per head
+  float b = -__builtin_huge_valf(), e = 0.f;
+  for (int c = j; c < ntr; c += 4) {
+    const RoutePart p = part[((size_t)t * ntr + c) * kWave + h];
+    b = fmaxf(b, p.best);
+    e = fmaxf(e, p.err);
+  }
+  pb[j][h] = b;
+  pe[j][h] = e;
+  if (tid == 0) n_work = 0;
+  if (j == 0) mbits[h] = 0ull;
+  __syncthreads();
+  if (j == 0) {
+#pragma unroll
+    for (int jj = 1; jj < 4; ++jj) {
+      b = fmaxf(b, pb[jj][h]);
+      e = fmaxf(e, pe[jj][h]);
+    }
+    // b + e < 0: every complete block has rho < 0 (nothing to evaluate)
+    gthr[h] = (active && nfull > 0 && b + e >= 0.f) ? b - 2.f * e : __builtin_huge_valf();
+  }
+  __syncthreads();
+  // candidate blocks of each head (thread j of head h scans ranges j, j+4, ...)
+  const float thr = gthr[h];
+  for (int c = j; c < ntr; c += 4) {
+    const RoutePart p = part[((size_t)t * ntr + c) * kWave + h];
+    if (p.arg >= 0 && p.best >= thr) {
+      const bool whole = p.second >= thr;
+      const int first = whole ? c * range_blocks : p.arg;
+      const int cnt = whole ? min(range_blocks, nfull - c * range_blocks) : 1;
+      const int at = atomicAdd(&n_work, cnt);
+      for (int k = 0; k < cnt && at + k < kWorkCap; ++k) {
+        work_h[at + k] = h;
+        work_b[at + k] = first + k;
+      }
+    }
+  }
+  __syncthreads();
+  const int nw = n_work;
+  const int grp = tid >> 3, sub = tid & 7;  // 32 groups of eight lanes
+  if (nw <= kWorkCap) {
+    for (int it = grp; it < nw; it += 32) settle_block(qs, ksum, kbar, work_h[it], work_b[it], B, sub, mbits);
+  } else {
+    // too many candidates to list: every complete block of every head
+    for (int i = grp; i < H * nfull; i += 32) {
+      const int hh = i / nfull;
+      if (gthr[hh] != __builtin_huge_valf()) settle_block(qs, ksum, kbar, hh, i - hh * nfull, B, sub, mbits);
+    }
+  }
+  __syncthreads();
+  if (j == 0) {
+    double m = __longlong_as_double((long long)mbits[h]);
+    if (Mt > 0 && active) {
+      // the query's own last block, always exactly
+      double acc = 0.0;
+      const u32x4* qrow = &qs[h * kQStride];
+#pragma unroll 4
+      for (int v = 0; v < 16; ++v) {
+        const u32x4 qw = qrow[v];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          acc = fma((double)bf16_bits_to_f32(qw[p] & 0xffffu), ts[8 * v + 2 * p], acc);
+          acc = fma((double)bf16_bits_to_f32(qw[p] >> 16), ts[8 * v + 2 * p + 1], acc);
+        }
+      }
+      const double rho = acc / (double)(n - (Mt - 1) * B);
+      m = rho > m ? rho : m;
+    }
+    const double r = active ? (double)wt * m + 0.0 : -__builtin_huge_val();
+    if (r_out && active) r_out[(size_t)t * H + h] = (float)r;
+    rs[h] = r;
+  }
+  __syncthreads();
+  if (!heads) return;
+  {
+    // rank of head h: wave j compares it with heads [16j, 16j + 16)
+    const double rh = rs[h];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const double r2 = rs[16 * j + u];
+      c += (r2 > rh) || (r2 == rh && 16 * j + u < h);
+    }
+    rank_part[j][h] = c;
+  }
+  __syncthreads();
+  if (j != 0) return;
+  const int rank = rank_part[0][h] + rank_part[1][h] + rank_part[2][h] + rank_part[3][h];
+  const bool sel = active && rank < A;
+  const uint64_t mask = wave_ballot(sel);
+  if (sel) {
+    const int slot = lanes_below(mask);
+    heads[(size_t)t * A + slot] = h;
+    if (qr) {
+      wr[(size_t)t * A + slot] = wt;
+      u32x4* dst = reinterpret_cast<u32x4*>(qr + ((size_t)t * A + slot) * kHeadDim);
+#pragma unroll
+      for (int v = 0; v < kHeadDim / 8; ++v) dst[v] = qs[h * kQStride + v];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+int route_fast_parts(int L, int B, int T) {
+  const int M = (int)(((long long)L + B - 1) / B);
+  const int tiles = (M + kFastTile - 1) / kFastTile;
+  const int tpw = (long long)tiles * T > 4096 ? 8 : 1;
+  return (tiles + tpw - 1) / tpw;
+}
+
+size_t route_part_bytes() { return sizeof(RoutePart); }
+
+bool route_fast_wins(int L, int B, int T) {
+  const int M = (int)(((long long)L + B - 1) / B);
+  const int tiles = (M + kFastTile - 1) / kFastTile;
+  return (long long)tiles * T > 4096;
+}
+
+hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
+                              int T, int H, int L, int B, int A, const double* ksum, const uint16_t* kb16,
+                              const float* kbar, const double* tsum, void* part, int32_t* heads,
+                              float* r_out, uint16_t* qr, float* wr) {
+  if (T == 0) return hipSuccess;
+  const bool wide = route_fast_wins(L, B, T);  // many queries: 8 tiles and 2 queries per workgroup
+  const int ntr = route_fast_parts(L, B, T);
+  RoutePart* pp = reinterpret_cast<RoutePart*>(part);
+  const uint16_t* kb = kbar ? nullptr : kb16;
+  hipError_t e;
+  if (wide)
+    e = cx.launch("route_fast", k_route_fast<2, 8>, dim3(ntr, (T + 1) / 2), dim3(256), 0, q, pos, T, H, L,
+                  B, ntr, kb, kbar, pp);
+  else
+    e = cx.launch("route_fast", k_route_fast<1, 1>, dim3(ntr, T), dim3(256), 0, q, pos, T, H, L, B, ntr,
+                  kb, kbar, pp);
+  if (e != hipSuccess) return e;
+  return cx.launch("route_exact", k_route_exact, dim3(T), dim3(256), 0, q, w, pos, H, L, B, A, ntr,
+                   (wide ? 8 : 1) * kFastTile, (const RoutePart*)pp, ksum, kbar, tsum, heads, r_out, qr, wr);
+}
+
+}  // namespace misa

@@ -97,7 +97,8 @@ struct RowSum {
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* kscale, int L,
                                                     int B, int M, double* ksum, float* kbar,
-                                                    const int32_t* pos, double* tsum, int b_base) {
+                                                    uint16_t* kb16, const int32_t* pos, double* tsum,
+                                                    int b_base) {
   constexpr int RL = RowSum<FP8>::RL;
   __shared__ double red[RL][kHeadDim];
   const int b = (int)blockIdx.x + b_base;
@@ -119,7 +120,15 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
     for (int r = 0; r < RL; ++r) s += red[r][tid];
     if (b < M) {
       ksum[(size_t)b * kHeadDim + tid] = s;
-      if (kbar) kbar[(size_t)b * kHeadDim + tid] = (float)(s / (double)(s1 - s0));
+      const double mean = s / (double)(s1 - s0);
+      if (kbar) kbar[(size_t)b * kHeadDim + tid] = (float)mean;
+      if (kb16) {
+        // bf16 hi / lo split of the mean for the router's fast pass
+        uint32_t hi, lo;
+        split_bf16(mean, hi, lo);
+        kb16[(size_t)b * 2 * kHeadDim + tid] = (uint16_t)hi;
+        kb16[(size_t)b * 2 * kHeadDim + kHeadDim + tid] = (uint16_t)lo;
+      }
     } else {
       tsum[(size_t)(b - M) * kHeadDim + tid] = s;
     }
@@ -397,7 +406,7 @@ __global__ __launch_bounds__(64) void k_gather_heads(const uint16_t* q, const fl
 
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum, bool tails_only) {
+                             double* tsum, bool tails_only, uint16_t* kb16) {
   const int M = (int)(((long long)L + B - 1) / B);
   const int base = tails_only ? M : 0;
   const int grid = M - base + (tsum ? T : 0);
@@ -405,9 +414,9 @@ hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* ks
   const char* nm = tails_only ? "tail_sums" : "block_sums";
   if (fp8)
     return cx.launch(nm, k_block_sums<true>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,
-                     kbar, pos, tsum, base);
+                     kbar, kb16, pos, tsum, base);
   return cx.launch(nm, k_block_sums<false>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,
-                   kbar, pos, tsum, base);
+                   kbar, kb16, pos, tsum, base);
 }
 
 int route_chunks(int L, int B) {

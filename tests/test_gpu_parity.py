@@ -70,6 +70,10 @@ ROUTE_CASES = [
     (4, 40, 2100, 64, 64, 128, O.KDT_BF16),
     (5, 6, 257, 7, 1, 1, O.KDT_FP8),
     (6, 8, 4096, 64, 8, 4096, O.KDT_BF16),
+    # many queries times many blocks: the two-pass router (bf16 pass, float64 settling)
+    (7, 1100, 1100, 64, 8, 16, O.KDT_BF16),
+    (8, 2200, 2200, 32, 8, 128, O.KDT_FP8),
+    (9, 4500, 600, 64, 8, 5, O.KDT_BF16),
 ]
 
 
@@ -77,6 +81,22 @@ ROUTE_CASES = [
 def test_route(case):
     seed, T, L, H, A, B, kdt = case
     inp = _case(seed, T, L, H, kdt, neg_scales=True)
+    q, w, K, ks, pos = to_gpu(inp)
+    heads, r = S.route(q, w, K, pos, B, A, ks, with_r=True)
+    P = oracle_problem(inp, B)
+    _, ill = check_heads(P, A, _np(heads), _np(r))
+    assert ill == 0
+
+
+@pytest.mark.parametrize("kdt", [O.KDT_BF16, O.KDT_FP8])
+def test_route_equal_blocks(kdt):
+    # every key is the same vector, so all complete blocks of a query have the same mean
+    # and no block can be ruled out before the exact products
+    T, L, H, A, B = 1500, 1500, 64, 8, 16
+    inp = _case(31, T, L, H, kdt, positions="prefill")
+    inp["K"][:] = inp["K"][0]
+    if inp["k_scale"] is not None:
+        inp["k_scale"][:] = inp["k_scale"][0]
     q, w, K, ks, pos = to_gpu(inp)
     heads, r = S.route(q, w, K, pos, B, A, ks, with_r=True)
     P = oracle_problem(inp, B)
@@ -97,6 +117,7 @@ MISA_CASES = [
     (17, 9, 1200, 40, 13, 100, 1200, O.KDT_BF16, "random"),
     (18, 300, 300, 64, 8, 128, 20, O.KDT_FP8, "prefill"),
     (19, 5, 20000, 32, 8, 128, 700, O.KDT_BF16, "decode"),
+    (20, 1100, 1100, 64, 8, 16, 64, O.KDT_FP8, "prefill"),
 ]
 
 
