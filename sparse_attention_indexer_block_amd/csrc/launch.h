@@ -106,7 +106,7 @@ struct ScoreArgs {
   float* S;              // output rows
   long long S_ld;
   uint32_t* rmm;         // optional [nsplit, T, 2] per-split {min, max} score key of each row
-  uint32_t* zero;        // optional buffer the first workgroup clears ...
+  uint32_t* zero;        // optional buffer the workgroups clear (each a share) ...
   long long zero_n;      // ... (zero_n 32-bit words)
   int tiles_per_split;
   int ngroups;
@@ -126,14 +126,15 @@ hipError_t launch_score_gather(const LaunchCtx& cx, ScoreArgs a, bool fp8);
 
 // ---- selection (topk_kernels.hip)
 struct TopkArgs {
-  const float* S;          // score rows
-  long long S_ld;
+  const float* S;          // score rows (16-byte aligned)
+  long long S_ld;          // multiple of 4 and >= every row length: the kernels read whole
+                           // 16-byte groups up to the one holding a row's last item
   const int32_t* row_n;    // [rows] explicit lengths, or null: n from pos
   const int32_t* pos;      // used when row_n == null: n = ceil(visible_len / n_div)
   int L;
   int n_div;
   const int32_t* row_idx;  // [rows, idx_ld] explicit key indices, or null (index = position)
-  long long idx_ld;
+  long long idx_ld;        // same rule as S_ld
   int rows;
   int k;
   int32_t* out_idx;        // [rows, out_ld]

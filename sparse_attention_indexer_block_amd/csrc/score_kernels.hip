@@ -49,8 +49,11 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
   const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
 
-  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (long long i = tid; i < p.zero_n; i += 256) p.zero[i] = 0u;
+  if (p.zero) {  // every workgroup clears its share
+    const long long nthreads = 256ll * gridDim.x * gridDim.y;
+    for (long long i = ((long long)blockIdx.y * gridDim.x + blockIdx.x) * 256 + tid; i < p.zero_n; i += nthreads)
+      p.zero[i] = 0u;
+  }
   if (tid < QW) {
     const int t = g * QW + tid;
     int nn = 0;
@@ -306,43 +309,32 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
   const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
 
-  if (p.zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (long long i = tid; i < p.zero_n; i += 256) p.zero[i] = 0u;
-  if (tid < QW) {
-    const int t = g * QW + tid;
-    int nn = 0;
-    if (t < p.T) {
-      if (GATHER && p.blocks) {
-        // candidates = the visible keys of the listed blocks (ascending); only
-        // the last listed block can be the query's partial last block
-        const int nb = p.nblocks[t];
-        if (nb > 0) {
-          const int last = p.blocks[(size_t)t * p.blocks_ld + nb - 1];
-          const long long tail = (long long)visible_len(p.pos[t], p.L) - (long long)last * p.B;
-          nn = (nb - 1) * p.B + (int)(tail < p.B ? tail : p.B);
-        }
-        if (split == 0) p.ncand_out[t] = nn;
-      } else {
-        nn = GATHER ? p.ncand[t] : visible_len(p.pos[t], p.L);
-      }
-    }
-    qn[tid] = nn;
-  }
-  __syncthreads();
-  int nmax = 0;
+  // With several key waves per row group (WC > 1) the workgroup's q rows and
+  // weights are loaded once into LDS (one pad word per row keeps the 16-byte
+  // row reads conflict-free) instead of once per wave.
+  constexpr bool STAGE = WC > 1;
+  constexpr int QSTR = kHeadDim / 8 + 1;
+  constexpr int SQ = STAGE ? ROWS * 16 / 256 : 0;  // 16-byte q words per thread
+  __shared__ u32x4 qsh[STAGE ? ROWS * QSTR : 1];
+  __shared__ float wsh[STAGE ? ROWS : 1];
+  u32x4 qstage[SQ > 0 ? SQ : 1];
+  float wstage = 0.f;
+  if constexpr (STAGE) {
 #pragma unroll
-  for (int i = 0; i < QW; ++i) nmax = qn[i] > nmax ? qn[i] : nmax;
-  const int ntiles = (nmax + KT - 1) / KT;
-  const int tile0 = split * p.tiles_per_split;
-  const int tile1 = min(ntiles, tile0 + p.tiles_per_split);
-  if (tile0 >= tile1) {  // uniform over the workgroup
-    if (!GATHER && p.rmm && tid < QW && g * QW + tid < p.T) {
-      p.rmm[((size_t)split * p.T + g * QW + tid) * 2] = 0xffffffffu;  // empty range
-      p.rmm[((size_t)split * p.T + g * QW + tid) * 2 + 1] = 0u;
+    for (int u = 0; u < SQ; ++u) {
+      const int i = tid + 256 * u, row = i >> 4, v = i & 15;
+      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      qstage[u] = (t < p.T && j < p.A)
+                      ? reinterpret_cast<const u32x4*>(p.q + ((size_t)t * p.H + j) * kHeadDim)[v]
+                      : u32x4{0u, 0u, 0u, 0u};
     }
-    return;
+    if (tid < ROWS) {
+      const int qi = tid / AP, j = tid % AP, t = g * QW + qi;
+      wstage = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
+    }
   }
-  const int ngroups = tile1 - tile0;  // this wave's groups: one per tile, key offset 16*wc
+
+  const int tile0 = split * p.tiles_per_split;
   const int qt0 = g * QW;
   const int kcol = lane & 15;
   const int slice = lane >> 4;
@@ -382,13 +374,81 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     }
   };
 
+  // Plain key ranges: the keys a split may touch are known from L alone, so the
+  // first groups are requested before the query lengths arrive (keys past a
+  // query's visible length are masked below).
+  int issued = 0;
+  if constexpr (!GATHER) {
+    const int ntl = (int)(((long long)p.L + KT - 1) / KT);
+    issued = max(0, min(D, min(ntl, tile0 + p.tiles_per_split) - tile0));
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < issued) load_group(d, d);
+  }
+
+  if (p.zero) {  // every workgroup clears its share
+    const long long nthreads = 256ll * gridDim.x * gridDim.y;
+    for (long long i = ((long long)blockIdx.y * gridDim.x + blockIdx.x) * 256 + tid; i < p.zero_n; i += nthreads)
+      p.zero[i] = 0u;
+  }
+  if (tid < QW) {
+    const int t = g * QW + tid;
+    int nn = 0;
+    if (t < p.T) {
+      if (GATHER && p.blocks) {
+        // candidates = the visible keys of the listed blocks (ascending); only
+        // the last listed block can be the query's partial last block
+        const int nb = p.nblocks[t];
+        if (nb > 0) {
+          const int last = p.blocks[(size_t)t * p.blocks_ld + nb - 1];
+          const long long tail = (long long)visible_len(p.pos[t], p.L) - (long long)last * p.B;
+          nn = (nb - 1) * p.B + (int)(tail < p.B ? tail : p.B);
+        }
+        if (split == 0) p.ncand_out[t] = nn;
+      } else {
+        nn = GATHER ? p.ncand[t] : visible_len(p.pos[t], p.L);
+      }
+    }
+    qn[tid] = nn;
+  }
+  if constexpr (STAGE) {
+#pragma unroll
+    for (int u = 0; u < SQ; ++u) {
+      const int i = tid + 256 * u;
+      qsh[(i >> 4) * QSTR + (i & 15)] = qstage[u];
+    }
+    if (tid < ROWS) wsh[tid] = wstage;
+  }
+  __syncthreads();
+  int nmax = 0;
+#pragma unroll
+  for (int i = 0; i < QW; ++i) nmax = qn[i] > nmax ? qn[i] : nmax;
+  const int ntiles = (nmax + KT - 1) / KT;
+  const int tile1 = min(ntiles, tile0 + p.tiles_per_split);
+  if (tile0 >= tile1) {  // uniform over the workgroup
+    if (!GATHER && p.rmm && tid < QW && g * QW + tid < p.T) {
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2] = 0xffffffffu;  // empty range
+      p.rmm[((size_t)split * p.T + g * QW + tid) * 2 + 1] = 0u;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // early key loads land before the wave ends
+    return;
+  }
+  const int ngroups = tile1 - tile0;  // this wave's groups: one per tile, key offset 16*wc
   // ---- A operand (q rows of the scored heads) and epilogue weights, kept in
   // registers; issued before the key stream so the first MFMA waits on one
   // round trip only.
   bf16x8 afrag[RPW][4];
   float wv[RPW][4];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
+  for (int r = 0; r < RPW && STAGE; ++r) {
+    const int row = (wr * RPW + r) * 16 + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = __builtin_bit_cast(bf16x8, qsh[row * QSTR + 4 * slice + ks]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[r][i] = wsh[(wr * RPW + r) * 16 + 4 * slice + i];
+  }
+#pragma unroll
+  for (int r = 0; r < RPW && !STAGE; ++r) {
     {
       const int row = (wr * RPW + r) * 16 + (lane & 15);
       const int qi = row / AP, j = row % AP, t = g * QW + qi;
@@ -412,7 +472,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
 
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (d < ngroups) load_group(d, d);
+    if (d >= issued && d < ngroups) load_group(d, d);
 
   const bool writer = AP >= 16 ? (lane < 16) : (AP == 8 ? ((lane & 16) == 0) : true);
   int q_n[NQ];
@@ -495,6 +555,8 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     }
   }
 
+  if constexpr (!GATHER)
+    if (issued > ngroups) __builtin_amdgcn_s_waitcnt(0);  // unused early loads land first
   if (!GATHER && p.rmm) {
     // per query: lanes of one wave reduce, then the key groups meet in LDS
     __shared__ float rlo[WC][QW], rhi[WC][QW];

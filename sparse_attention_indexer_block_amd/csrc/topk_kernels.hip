@@ -507,23 +507,32 @@ __device__ __forceinline__ uint32_t coarse_bin(uint32_t u, float xlo, float scal
   return lin_bin(u, xlo, scale, kCoarseBins);
 }
 
-// Keys of items [s0 + 4*j, s0 + 4*j + 4) of a row (j-th group of four), with
-// positions past s1 marked absent. Row starts are 16-byte aligned.
-__device__ __forceinline__ void load_group4(const float* row, int s0, int s1, int j, uint32_t u[4],
-                                            bool in[4]) {
-  const int s = s0 + 4 * j;
-  if (s + 4 <= s1) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(row + s);
+// Keys of items [s0 + 4 (j0 + dj g), ... + 4) of a row for g < G (groups of
+// four), with positions past s1 marked absent. Row starts are 16-byte aligned
+// and every score row is stored with a stride that is a multiple of 64 items,
+// so the aligned group holding item s1 - 1 lies inside the row's storage: each
+// group is one 16-byte load from a clamped address, with no branch per group
+// (all G loads are in flight together).
+template <int G>
+__device__ __forceinline__ void load_groups4(const float* row, int s0, int s1, int j0, int dj,
+                                             uint32_t (&u)[G][4], bool (&in)[G][4]) {
+  f32x4 v[G];
+  if (s1 > s0) {
+    const int last = (s1 - 1) & ~3;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      u[e] = score_key(v[e]);
-      in[e] = true;
-    }
+    for (int g = 0; g < G; ++g)
+      v[g] = *reinterpret_cast<const f32x4*>(row + min(s0 + 4 * (j0 + dj * g), last));
   } else {
 #pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int s = s0 + 4 * (j0 + dj * g);
+#pragma unroll
     for (int e = 0; e < 4; ++e) {
-      in[e] = s + e < s1;
-      u[e] = in[e] ? score_key(row[s + e]) : 0u;
+      in[g][e] = s + e < s1;
+      u[g][e] = in[g][e] ? score_key(v[g][e]) : 0u;
     }
   }
 }
@@ -547,8 +556,7 @@ __global__ __launch_bounds__(NT) void k_long_hist(TopkArgs a, const uint32_t* rm
   const float* src = a.S + (size_t)row * a.S_ld;
   uint32_t u[kGroups][4];
   bool in[kGroups][4];
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) load_group4(src, s0, s1, g * NT + tid, u[g], in[g]);
+  load_groups4<kGroups>(src, s0, s1, tid, NT, u, in);
   for (int b = tid; b < kCoarseBins; b += NT) lh[b] = 0u;
   row_range<NT>(rmm, nmm, a.rows, row, sm);
   const float xlo = key_score(sm.umin), scale = lin_scale(xlo, key_score(sm.umax), kCoarseBins);
@@ -586,8 +594,7 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* r
   const int ws0 = s0 + w * (kChunk / NW);
   uint32_t u[kGroups][4];
   bool in[kGroups][4];
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) load_group4(src, ws0, s1, lane + kWave * g, u[g], in[g]);
+  load_groups4<kGroups>(src, ws0, s1, lane, kWave, u, in);
   row_range<NT>(rmm, nmm, a.rows, row, sm);
   const float xlo = key_score(sm.umin), scale = lin_scale(xlo, key_score(sm.umax), kCoarseBins);
   find_bin<NT>(ghist + (size_t)row * kCoarseBins, kCoarseBins, a.k, sm);
@@ -680,8 +687,7 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
   const int ws0 = s0 + w * (kChunk / NW);
   uint32_t u[kGroups][4];
   bool in[kGroups][4];
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) load_group4(src, ws0, s1, lane + kWave * g, u[g], in[g]);
+  load_groups4<kGroups>(src, ws0, s1, lane, kWave, u, in);
   if (take_all) {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
@@ -985,16 +991,18 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
   uint32_t u[G][4];
   bool in[G][4];
   i32x4 ix[G];
+  load_groups4<G>(src, seg0, n, lane, kWave, u, in);
+  if (ri && n > seg0) {
+    // index rows share the score rows' padded stride: same clamped 16-byte loads
+    const int last = (n - 1) & ~3;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    load_group4(src, seg0, n, lane + kWave * g, u[g], in[g]);
-    const int s = seg0 + 4 * (lane + kWave * g);
-    if (ri && s + 4 <= n) {
-      ix[g] = *reinterpret_cast<const i32x4*>(ri + s);
-    } else {
+    for (int g = 0; g < G; ++g)
+      ix[g] = *reinterpret_cast<const i32x4*>(ri + min(seg0 + 4 * (lane + kWave * g), last));
+  } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ix[g][e] = (ri && s + e < n) ? ri[s + e] : s + e;
-    }
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ix[g][e] = seg0 + 4 * (lane + kWave * g) + e;
   }
   int32_t* oi = a.out_idx + (size_t)row * a.out_ld;
   float* os = a.out_score ? a.out_score + (size_t)row * a.out_ld : nullptr;
@@ -1087,14 +1095,18 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
 }
 
 // grid (nchunk, rows): {min, max} score key of each chunk into rmm[chunk, row];
-// workgroup (0, 0) also clears `zero`.
+// the workgroups also clear `zero`, each a share.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_topk_range(TopkArgs a, uint32_t* rmm, uint32_t* zero,
                                                    long long zero_n) {
   __shared__ TopkShared<NT> sm;
   const int row = blockIdx.y, chunk = blockIdx.x;
-  if (zero && row == 0 && chunk == 0)
-    for (long long i = threadIdx.x; i < zero_n; i += NT) zero[i] = 0u;
+  if (zero) {
+    const long long nthreads = (long long)NT * gridDim.x * gridDim.y;
+    for (long long i = ((long long)blockIdx.y * gridDim.x + blockIdx.x) * NT + threadIdx.x; i < zero_n;
+         i += nthreads)
+      zero[i] = 0u;
+  }
   const int n = row_length(a, row);
   const int s0 = chunk * kChunk, s1 = min(n, s0 + kChunk);
   uint32_t lo = 0xffffffffu, hi = 0u;
