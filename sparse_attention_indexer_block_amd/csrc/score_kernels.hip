@@ -339,16 +339,20 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   const int kcol = lane & 15;
   const int slice = lane >> 4;
 
+  // Every request reads from a valid address (a column past the end reads key
+  // 0 and carries key -1, so it is never written): a load issued under a lane
+  // mask beside a register fill for the other lanes would make the compiler
+  // wait for it before it could request the next group.
   auto key_of = [&](int gi) -> int {
     const int col = (tile0 + gi) * KT + 16 * wc + kcol;
     if constexpr (GATHER) {
-      if (col >= qn[0]) return -1;
-      if (p.blocks) {
-        const int key = p.blocks[(size_t)qt0 * p.blocks_ld + col / p.B] * p.B + col % p.B;
-        if (slice == 0) p.cand_out[(size_t)qt0 * p.cand_ld + col] = key;  // for the selection
-        return key;
-      }
-      return p.cand[(size_t)qt0 * p.cand_ld + col];
+      // one load per group either way (no branch between the request and its use)
+      const int cc = min(col, qn[0] - 1);  // qn[0] >= 1 whenever groups are loaded
+      const int bsz = p.blocks ? p.B : 1;
+      const int* src = p.blocks ? p.blocks + (size_t)qt0 * p.blocks_ld : p.cand + (size_t)qt0 * p.cand_ld;
+      const int blk = cc / bsz;
+      const int key = src[blk] * bsz + (cc - blk * bsz);
+      return col < qn[0] ? key : -1;
     } else {
       return col < p.L ? col : -1;
     }
@@ -357,33 +361,25 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   u32x4 kv[D][NV];
   float ksv[D];
   int keyv[D];
-  auto load_group = [&](int gi, int slot) {
-    const int s = key_of(gi);
+  auto load_key = [&](int s, int slot) {
     keyv[slot] = s;
-    if (s >= 0) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(
-          reinterpret_cast<const uint8_t*>(p.K) + (size_t)s * (FP8 ? kHeadDim : 2 * kHeadDim) +
-          slice * NV * 16);
+    const int r = s >= 0 ? s : 0;
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        reinterpret_cast<const uint8_t*>(p.K) + (size_t)r * (FP8 ? kHeadDim : 2 * kHeadDim) + slice * NV * 16);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) kv[slot][v] = src[v];
-      ksv[slot] = FP8 ? p.kscale[s] : 1.f;
-    } else {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) kv[slot][v] = u32x4{0u, 0u, 0u, 0u};
-      ksv[slot] = 1.f;
-    }
+    for (int v = 0; v < NV; ++v) kv[slot][v] = src[v];
+    ksv[slot] = FP8 ? p.kscale[r] : 1.f;
   };
+  auto load_group = [&](int gi, int slot) { load_key(key_of(gi), slot); };
 
   // Plain key ranges: the keys a split may touch are known from L alone, so the
-  // first groups are requested before the query lengths arrive (keys past a
-  // query's visible length are masked below).
-  int issued = 0;
+  // first D groups are requested before the query lengths arrive (keys past a
+  // query's visible length are masked below). All D are requested whether or
+  // not the split has that many: a request under a uniform branch makes the
+  // compiler's wait counting conservative for every later group.
   if constexpr (!GATHER) {
-    const int ntl = (int)(((long long)p.L + KT - 1) / KT);
-    issued = max(0, min(D, min(ntl, tile0 + p.tiles_per_split) - tile0));
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (d < issued) load_group(d, d);
+    for (int d = 0; d < D; ++d) load_group(d, d);
   }
 
   if (p.zero) {  // every workgroup clears its share
@@ -430,7 +426,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
       p.rmm[((size_t)split * p.T + g * QW + tid) * 2] = 0xffffffffu;  // empty range
       p.rmm[((size_t)split * p.T + g * QW + tid) * 2 + 1] = 0u;
     }
-    __builtin_amdgcn_s_waitcnt(0);  // early key loads land before the wave ends
+    if constexpr (!GATHER) __builtin_amdgcn_s_waitcnt(0);  // early key requests land first
     return;
   }
   const int ngroups = tile1 - tile0;  // this wave's groups: one per tile, key offset 16*wc
@@ -470,9 +466,14 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     }
   }
 
+  if constexpr (GATHER) {
+    // key indices of the first D groups, all requested before any key row
+    int k0[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d >= issued && d < ngroups) load_group(d, d);
+    for (int d = 0; d < D; ++d) k0[d] = key_of(d);  // in bounds for any d (clamped)
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_key(k0[d], d);
+  }
 
   const bool writer = AP >= 16 ? (lane < 16) : (AP == 8 ? ((lane & 16) == 0) : true);
   int q_n[NQ];
@@ -513,6 +514,8 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
       float kscale = ksv[d];
       const int key = keyv[d];
       const int col = (tile0 + gi) * KT + 16 * wc + kcol;
+      if constexpr (GATHER)  // block-list candidates are recorded for the selection
+        if (p.blocks && slice == 0 && key >= 0) p.cand_out[(size_t)qt0 * p.cand_ld + col] = key;
       if (gi + D < ngroups) load_group(gi + D, d);
 
       f32x4 acc[RPW];
@@ -555,8 +558,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     }
   }
 
-  if constexpr (!GATHER)
-    if (issued > ngroups) __builtin_amdgcn_s_waitcnt(0);  // unused early loads land first
+  if (ngroups < D) __builtin_amdgcn_s_waitcnt(0);  // unused requests land before the wave ends
   if (!GATHER && p.rmm) {
     // per query: lanes of one wave reduce, then the key groups meet in LDS
     __shared__ float rlo[WC][QW], rhi[WC][QW];
