@@ -111,6 +111,19 @@ def test_workspace_sizes():
         assert ws(op) % 256 == 0
 
 
+@pytest.mark.parametrize("T,L,B,H", [(8, 4096, 4096, 64), (3, 1, 1, 7), (5, 1, 128, 64), (6, 257, 1, 7),
+                                     (16, 131072, 128, 32), (8, 131200, 128, 64), (1, 1 << 23, 128, 64),
+                                     (16384, 16384, 128, 64), (2, 300, 7, 48)])
+def test_workspace_sizes_for_edge_shapes(T, L, B, H):
+    # host-side planning only (no device call): single-block arrays, one-key blocks,
+    # the largest supported L and router shapes on both sides of every path switch
+    Lb = S.lib()
+    p = _problem(T=T, L=L, B=B, H=H)
+    for op in range(5):
+        n = Lb.misa_workspace_bytes(ctypes.byref(p), op, min(8, H), min(8192, L), min(2048, L), 64)
+        assert n > 0 and n % 256 == 0, (op, n)
+
+
 def test_profile_api_without_gpu():
     assert S.lib().misa_profile_reset() == 0
     ms, n = S.profile_read("")
