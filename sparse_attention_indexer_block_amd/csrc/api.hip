@@ -129,7 +129,7 @@ static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, i
       pl.qr = bp.take((size_t)T * A * 128 * 2);
       pl.wr = bp.take((size_t)T * A * 4);
       pl.S_ld = padded_ld(L);
-      pl.S = bp.take((size_t)T * pl.S_ld * 4);
+      pl.S = bp.take((size_t)(T + 1) * pl.S_ld * 4);  // + the scoring kernel's dump row
       plan_long(bp, pl, T, L);
       break;
     case MISA_OP_HIER_TOPK: {
@@ -138,7 +138,7 @@ static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, i
       pl.qr = bp.take((size_t)T * A * 128 * 2);
       pl.wr = bp.take((size_t)T * A * 4);
       pl.S_ld = padded_ld(L);
-      pl.S = bp.take((size_t)T * pl.S_ld * 4);
+      pl.S = bp.take((size_t)(T + 1) * pl.S_ld * 4);  // + the scoring kernel's dump row
       pl.cand_ld = padded_ld(kprime < L ? kprime : L);
       pl.cand = bp.take((size_t)T * pl.cand_ld * 4);
       pl.ncand = bp.take((size_t)T * 4);

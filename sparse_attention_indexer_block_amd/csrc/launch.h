@@ -103,7 +103,8 @@ struct ScoreArgs {
   int B;
   int32_t* cand_out;
   int32_t* ncand_out;
-  float* S;              // output rows
+  float* S;              // output rows; launch_score_keys needs T + 1 rows (row T takes
+                         // the writes of lanes without a query) and S_ld a multiple of 64
   long long S_ld;
   uint32_t* rmm;         // optional [nsplit, T, 2] per-split {min, max} score key of each row
   uint32_t* zero;        // optional buffer the workgroups clear (each a share) ...
@@ -116,8 +117,9 @@ struct ScoreArgs {
 };
 // Scores of every visible key over the first A rows of each query's q and w
 // (the routed rows packed by the router, or all H heads for the dense indexer):
-// S[t, s] = sum_{j<A} w[t,j] ReLU(q[t,j] . k[s]) for s < n_t. The number of
-// key splits (rows of rmm) is returned in *nsplit_out.
+// S[t, s] = sum_{j<A} w[t,j] ReLU(q[t,j] . k[s]) for s < n_t; entries of a
+// row past n_t (below S_ld) and row T may be overwritten. The number of key
+// splits (rows of rmm) is returned in *nsplit_out.
 int score_max_splits();
 hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* nsplit_out);
 // Dense scores of gathered keys: S[t, j] = I_all(t, cand[t, j]) for j < ncand[t]

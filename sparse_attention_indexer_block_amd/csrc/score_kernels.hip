@@ -20,34 +20,60 @@ namespace misa {
 
 constexpr int kLdsStride = kHeadDim + 8;  // bf16 per key row in LDS (16 B pad)
 
-template <int AP, int WR, int RPW, int CPW, bool FP8, bool GATHER>
+// Row layout of the A operand. With AP <= 16 head slots, G = AP / 4 row tiles
+// form a "quad" of four queries: row r of tile k in the quad is query r / 4,
+// head slot 4 k + r % 4, so the four MFMA result rows a lane holds are four
+// heads of one query in every tile of the quad and the head sum needs no
+// cross-lane step. With AP >= 32 a query fills AP / 16 whole tiles (row r =
+// head slot) and the sum adds the lane groups with two exchanges.
+template <int AP>
+struct RowMap {
+  static constexpr bool QUAD = AP <= 16;
+  static constexpr int G = QUAD ? AP / 4 : AP / 16;  // tiles per quad / per query
+  // (query index inside the workgroup, head slot) of row r of row tile rt
+  static __device__ __forceinline__ void at(int rt, int r, int& qi, int& j) {
+    if constexpr (QUAD) {
+      qi = (rt / G) * 4 + (r >> 2);
+      j = 4 * (rt % G) + (r & 3);
+    } else {
+      qi = rt / G;
+      j = (rt % G) * 16 + r;
+    }
+  }
+};
+
+// Prefill-shaped batches: 256 rows per workgroup (WR row-wave groups of RPW
+// tiles), key tiles of KT keys staged through LDS and shared by the waves.
+// Scores go to S[t, col] for every col below the tile end (a key past the
+// query's visible length gets an unused value inside the padded row; rows of
+// lanes without a query go to the dump row S[T]), so the epilogue has no
+// branch. RMM: also the per-split {min, max} score key of each query.
+template <int AP, int WR, int RPW, int CPW, bool FP8, bool RMM>
 __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
+  using RM = RowMap<AP>;
   // key tiles in flight per workgroup (fewer when the row tiles use many registers)
   constexpr int R = (RPW >= 4 && !FP8) ? 2 : 4;
   constexpr int WC = 4 / WR;
   constexpr int ROWS = WR * RPW * 16;
   constexpr int QW = ROWS / AP;                     // queries per workgroup
   constexpr int KT = WC * CPW * 16;                 // keys per LDS tile
-  constexpr int TPQ = AP >= 16 ? AP / 16 : 1;       // row tiles per query
-  constexpr int NQ = RPW / TPQ;                     // query slots per lane
+  constexpr int NQ = RM::QUAD ? RPW / RM::G : RPW / RM::G;  // quads / queries per wave
   constexpr int CH_PER_ROW = FP8 ? 8 : 16;          // 16-byte global chunks per key row
   constexpr int CHUNKS = KT * CH_PER_ROW / 256;     // chunks per thread per tile
   static_assert(AP >= 4 && (AP & (AP - 1)) == 0, "AP must be a power of two >= 4");
   static_assert(ROWS % AP == 0 && QW >= 1, "row tiles must hold whole queries");
-  static_assert(AP < 16 || RPW % TPQ == 0, "a wave must hold whole queries");
-  static_assert(!GATHER || QW == 1, "gather mode scores one query per workgroup");
+  static_assert(RPW % RM::G == 0, "a wave must hold whole quads or queries");
   static_assert(CHUNKS >= 1 && KT * CH_PER_ROW % 256 == 0, "tile must split evenly");
 
   __shared__ __attribute__((aligned(16))) uint16_t ktile[2][KT * kLdsStride];
   __shared__ float ksc[2][KT];
-  __shared__ int kkey[2][KT];
   __shared__ int qn[QW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / WC, wc = wave % WC;
-  const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
-  const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
+  const int g = p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int split = (int)blockIdx.y;
 
   if (p.zero) {  // every workgroup clears its share
     const long long nthreads = 256ll * gridDim.x * gridDim.y;
@@ -56,9 +82,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   }
   if (tid < QW) {
     const int t = g * QW + tid;
-    int nn = 0;
-    if (t < p.T) nn = GATHER ? p.ncand[t] : visible_len(p.pos[t], p.L);
-    qn[tid] = nn;
+    qn[tid] = t < p.T ? visible_len(p.pos[t], p.L) : 0;
   }
   __syncthreads();
   int nmax = 0;
@@ -68,7 +92,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   const int tile0 = split * p.tiles_per_split;
   const int tile1 = min(ntiles, tile0 + p.tiles_per_split);
   if (tile0 >= tile1) {  // uniform over the workgroup
-    if (!GATHER && p.rmm && tid < QW && g * QW + tid < p.T) {
+    if (RMM && tid < QW && g * QW + tid < p.T) {
       p.rmm[((size_t)split * p.T + g * QW + tid) * 2] = 0xffffffffu;  // empty range
       p.rmm[((size_t)split * p.T + g * QW + tid) * 2 + 1] = 0u;
     }
@@ -78,36 +102,18 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   // ---- staging of key tiles: global -> registers (R tiles in flight) -> LDS
   u32x4 stage[R][CHUNKS];
   float stage_sc[R];
-  int stage_key[R];
-  const int qt0 = g * QW;  // gather: the single query
-
-  auto key_of = [&](int tile, int kr) -> int {
-    const int col = tile * KT + kr;
-    if constexpr (GATHER) {
-      return col < qn[0] ? p.cand[(size_t)qt0 * p.cand_ld + col] : -1;
-    } else {
-      return col < p.L ? col : -1;
-    }
-  };
 
   auto load_tile = [&](int tile, int rr) {
 #pragma unroll
     for (int u = 0; u < CHUNKS; ++u) {
       const int c = tid + 256 * u;
       const int kr = c / CH_PER_ROW, part = c % CH_PER_ROW;
-      const int s = key_of(tile, kr);
-      if (s >= 0) {
-        const uint8_t* base = reinterpret_cast<const uint8_t*>(p.K) +
-                              (size_t)s * (FP8 ? kHeadDim : 2 * kHeadDim) + 16 * part;
-        stage[rr][u] = *reinterpret_cast<const u32x4*>(base);
-      } else {
-        stage[rr][u] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int s = min(tile * KT + kr, p.L - 1);  // past the end: any valid key (never stored)
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(p.K) + (size_t)s * (FP8 ? kHeadDim : 2 * kHeadDim) +
+                            16 * part;
+      stage[rr][u] = *reinterpret_cast<const u32x4*>(base);
     }
-    if (tid < KT) {
-      stage_key[rr] = key_of(tile, tid);
-      stage_sc[rr] = (FP8 && stage_key[rr] >= 0) ? p.kscale[stage_key[rr]] : 1.f;
-    }
+    if (FP8 && tid < KT) stage_sc[rr] = p.kscale[min(tile * KT + tid, p.L - 1)];
   };
 
   auto store_tile = [&](int buf, int rr) {
@@ -132,10 +138,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
         *reinterpret_cast<u32x4*>(&ktile[buf][kr * kLdsStride + 8 * part]) = stage[rr][u];
       }
     }
-    if (tid < KT) {
-      ksc[buf][tid] = stage_sc[rr];
-      kkey[buf][tid] = stage_key[rr];
-    }
+    if (FP8 && tid < KT) ksc[buf][tid] = stage_sc[rr];
   };
 
   // ---- A operand (q rows of the scored heads) and epilogue weights, kept in
@@ -146,8 +149,9 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   for (int r = 0; r < RPW; ++r) {
     const int rt = wr * RPW + r;
     {
-      const int row = rt * 16 + (lane & 15);
-      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      int qi, j;
+      RM::at(rt, lane & 15, qi, j);
+      const int t = g * QW + qi;
       if (t < p.T && j < p.A) {
         const bf16x8* src = reinterpret_cast<const bf16x8*>(
             p.q + ((size_t)t * p.H + j) * kHeadDim + 32 * (lane >> 4));
@@ -160,8 +164,9 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = rt * 16 + 4 * (lane >> 4) + i;
-      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      int qi, j;
+      RM::at(rt, 4 * (lane >> 4) + i, qi, j);
+      const int t = g * QW + qi;
       wv[r][i] = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
     }
   }
@@ -170,18 +175,19 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   for (int rr = 0; rr < R; ++rr)
     if (tile0 + rr < tile1) load_tile(tile0 + rr, rr);
 
-  // per query slot of this lane: visible length, output row and score range
-  const bool writer = AP >= 16 ? (lane < 16) : (AP == 8 ? ((lane & 16) == 0) : true);
+  // per quad (or query) of this lane: visible length, output row, score range
   int q_n[NQ];
   float* q_row[NQ];
   float smin[NQ], smax[NQ];
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
-    const int rt0 = wr * RPW + s * TPQ;
-    const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * (lane >> 4)) / AP;
+    const int rt0 = wr * RPW + s * RM::G;
+    int qi, j;
+    RM::at(rt0, 4 * (lane >> 4), qi, j);
     const int t = g * QW + qi;
-    q_n[s] = writer ? qn[qi] : 0;
-    q_row[s] = p.S + (size_t)(t < p.T ? t : 0) * p.S_ld;
+    const bool writer = RM::QUAD || lane < 16;  // AP >= 32: lane group 0 holds the sums
+    q_n[s] = qn[qi];
+    q_row[s] = p.S + (size_t)(writer && t < p.T ? t : p.T) * p.S_ld;
     smin[s] = __builtin_huge_valf();
     smax[s] = -__builtin_huge_valf();
   }
@@ -196,67 +202,63 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
       __syncthreads();
       if (tile + R < tile1) load_tile(tile + R, rr);
 
-      // ---- MFMA: acc[r][c] = q rows (r) x 16 keys (c), K = 128 in 4 steps
-      f32x4 acc[RPW][CPW];
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
-        const int col = (wc * CPW + c) * 16 + (lane & 15);
+        // ---- MFMA: acc[r] = q rows (r) x 16 keys, K = 128 in 4 steps
+        const int colt = (wc * CPW + c) * 16 + (lane & 15);
         const bf16x8* bsrc =
-            reinterpret_cast<const bf16x8*>(&ktile[cur][col * kLdsStride + 32 * (lane >> 4)]);
+            reinterpret_cast<const bf16x8*>(&ktile[cur][colt * kLdsStride + 32 * (lane >> 4)]);
         bf16x8 bfrag[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) bfrag[ks] = bsrc[ks];
+        f32x4 acc[RPW];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
           f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks)
             a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[r][ks], bfrag[ks], a4, 0, 0, 0);
-          acc[r][c] = a4;
+          acc[r] = a4;
         }
-      }
-
-      // ---- epilogue: ReLU, times w, sum over the query's head slots, times |scale|
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        const int colt = (wc * CPW + c) * 16 + (lane & 15);
+        // ---- epilogue: ReLU, times w, sum over the query's head slots, times |scale|
         float kscale = 1.f;
         if constexpr (FP8) {
           kscale = ksc[cur][colt];
           // a negative scale flips the key's sign inside the ReLU (rare: uniform branch)
-          if (__builtin_amdgcn_read_exec() & wave_ballot(kscale < 0.f)) {
+          if (wave_ballot(kscale < 0.f)) {
             const float sgn = kscale < 0.f ? -1.f : 1.f;
 #pragma unroll
             for (int r = 0; r < RPW; ++r)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[r][c][i] *= sgn;
+              for (int i = 0; i < 4; ++i) acc[r][i] *= sgn;
             kscale = fabsf(kscale);
           }
         }
-        const bool valid_key = !GATHER || kkey[cur][colt] >= 0;
         const int col = tile * KT + colt;
 #pragma unroll
         for (int s = 0; s < NQ; ++s) {
-          const int r0 = s * TPQ;
           float part = 0.f;
 #pragma unroll
-          for (int tq = 0; tq < TPQ; ++tq)
+          for (int k = 0; k < RM::G; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part += wv[r0 + tq][i] * fmaxf(acc[r0 + tq][c][i], 0.f);
-          if constexpr (AP >= 8) part += __shfl_xor(part, 16, kWave);
-          if constexpr (AP >= 16) part += __shfl_xor(part, 32, kWave);
-          if (col < q_n[s] && valid_key) {
-            const float v = part * kscale;
-            q_row[s][col] = v;
-            smin[s] = fminf(smin[s], v);
-            smax[s] = fmaxf(smax[s], v);
+            for (int i = 0; i < 4; ++i) part += wv[s * RM::G + k][i] * fmaxf(acc[s * RM::G + k][i], 0.f);
+          if constexpr (!RM::QUAD) {
+            part += __shfl_xor(part, 16, kWave);
+            part += __shfl_xor(part, 32, kWave);
+          }
+          const float v = part * kscale;
+          q_row[s][col] = v;
+          if constexpr (RMM) {
+            const bool vis = col < q_n[s];
+            smin[s] = fminf(smin[s], vis ? v : __builtin_huge_valf());
+            smax[s] = fmaxf(smax[s], vis ? v : -__builtin_huge_valf());
           }
         }
       }
     }
   }
 
-  if (!GATHER && p.rmm) {
+  if constexpr (RMM) {
     // lanes that share a query sit in one 16-lane group: reduce there
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
@@ -266,9 +268,11 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
         lo = fminf(lo, __shfl_xor(lo, off, kWave));
         hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
       }
-      const int rt0 = wr * RPW + s * TPQ;
-      const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * (lane >> 4)) / AP;
+      const int rt0 = wr * RPW + s * RM::G;
+      int qi, j;
+      RM::at(rt0, 4 * (lane >> 4), qi, j);
       const int t = g * QW + qi;
+      const bool writer = RM::QUAD || lane < 16;
       if (writer && (lane & 15) == 0 && t < p.T) {
         // an empty range (no visible key here) stays {max key, 0}
         const bool any = lo <= hi;
@@ -603,27 +607,18 @@ static int pad_heads(int A) {
   return ap;
 }
 
-template <int AP, int WR, int RPW, int CPW, bool GATHER>
+template <int AP, int WR, int RPW, int CPW>
 static hipError_t run_score(const LaunchCtx& cx, ScoreArgs a, bool fp8, const char* name,
                             int* nsplit_out) {
   constexpr int WC = 4 / WR;
   constexpr int QW = WR * RPW * 16 / AP;
   constexpr int KT = WC * CPW * 16;
-  const long long max_cols = GATHER ? (long long)a.cand_max : (long long)a.L;
-  const int tiles = (int)((max_cols + KT - 1) / KT);
-  int groups, splits;
+  const int tiles = (int)(((long long)a.L + KT - 1) / KT);
   const int target = a.target_wgs > 0 ? a.target_wgs : 2048;
-  if (GATHER) {
-    groups = a.T;
-    // aim for `target` workgroups in total, at least 2 tiles each
-    splits = (target + groups - 1) / groups;
-    splits = splits > (tiles + 1) / 2 ? (tiles + 1) / 2 : splits;
-  } else {
-    groups = (a.T + QW - 1) / QW;
-    const int min_tiles = a.target_wgs > 0 ? 1 : 4;
-    splits = (target + groups - 1) / groups;
-    splits = splits > (tiles + min_tiles - 1) / min_tiles ? (tiles + min_tiles - 1) / min_tiles : splits;
-  }
+  const int groups = (a.T + QW - 1) / QW;
+  const int min_tiles = a.target_wgs > 0 ? 1 : 4;
+  int splits = (target + groups - 1) / groups;
+  splits = splits > (tiles + min_tiles - 1) / min_tiles ? (tiles + min_tiles - 1) / min_tiles : splits;
   if (splits < 1) splits = 1;
   a.tiles_per_split = (tiles + splits - 1) / splits;
   splits = (tiles + a.tiles_per_split - 1) / a.tiles_per_split;
@@ -631,9 +626,11 @@ static hipError_t run_score(const LaunchCtx& cx, ScoreArgs a, bool fp8, const ch
   a.ngroups = groups;
   a.nsplit = splits;
   if (nsplit_out) *nsplit_out = splits;
-  dim3 grid = GATHER ? dim3(splits, groups) : dim3(groups, splits);
-  if (fp8) return cx.launch(name, k_score<AP, WR, RPW, CPW, true, GATHER>, grid, dim3(256), 0, a);
-  return cx.launch(name, k_score<AP, WR, RPW, CPW, false, GATHER>, grid, dim3(256), 0, a);
+  const dim3 grid(groups, splits);
+#define MISA_SCORE_LAUNCH(F8, RM) cx.launch(name, k_score<AP, WR, RPW, CPW, F8, RM>, grid, dim3(256), 0, a)
+  if (a.rmm) return fp8 ? MISA_SCORE_LAUNCH(true, true) : MISA_SCORE_LAUNCH(false, true);
+  return fp8 ? MISA_SCORE_LAUNCH(true, false) : MISA_SCORE_LAUNCH(false, false);
+#undef MISA_SCORE_LAUNCH
 }
 
 template <int AP, int RPW, int WR, bool GATHER>
@@ -702,11 +699,11 @@ hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* ns
   if (done) return err;
   // larger batches (prefill): LDS-staged key tiles shared by 256 rows
   switch (ap) {
-    case 4: return run_score<4, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    case 8: return run_score<8, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    case 16: return run_score<16, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    case 32: return run_score<32, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
-    default: return run_score<64, 4, 4, 4, false>(cx, a, fp8, nm, nsplit_out);
+    case 4: return run_score<4, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
+    case 8: return run_score<8, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
+    case 16: return run_score<16, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
+    case 32: return run_score<32, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
+    default: return run_score<64, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
   }
 }
 

@@ -121,6 +121,11 @@ MISA_CASES = [
     (18, 300, 300, 64, 8, 128, 20, O.KDT_FP8, "prefill"),
     (19, 5, 20000, 32, 8, 128, 700, O.KDT_BF16, "decode"),
     (20, 1100, 1100, 64, 8, 16, 64, O.KDT_FP8, "prefill"),
+    # LDS-tiled scoring (more than 256 rows) with 16 and 32 padded head slots, and
+    # with rows long enough for the split selection (per-split score ranges)
+    (21, 40, 900, 64, 12, 128, 77, O.KDT_FP8, "random"),
+    (22, 20, 700, 48, 20, 64, 50, O.KDT_BF16, "random"),
+    (23, 40, 17000, 32, 8, 128, 300, O.KDT_FP8, "random"),
 ]
 
 
