@@ -143,7 +143,7 @@ static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, i
       pl.cand = bp.take((size_t)T * pl.cand_ld * 4);
       pl.ncand = bp.take((size_t)T * 4);
       pl.S2_ld = pl.cand_ld;
-      pl.S2 = bp.take((size_t)T * pl.S2_ld * 4);
+      pl.S2 = bp.take((size_t)(T + 1) * pl.S2_ld * 4);  // + the scoring kernel's dump row
       plan_long(bp, pl, T, L);  // covers the k' stage and the final stage (k' <= L)
       break;
     }
@@ -160,7 +160,7 @@ static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, i
       pl.cand = bp.take((size_t)T * pl.cand_ld * 4);
       pl.ncand = bp.take((size_t)T * 4);
       pl.S2_ld = pl.cand_ld;
-      pl.S2 = bp.take((size_t)T * pl.S2_ld * 4);
+      pl.S2 = bp.take((size_t)(T + 1) * pl.S2_ld * 4);  // + the scoring kernel's dump row
       const int mx = pl.Mmax > (int)pl.cand_ld ? pl.Mmax : (int)pl.cand_ld;
       plan_long(bp, pl, T, mx);
       break;

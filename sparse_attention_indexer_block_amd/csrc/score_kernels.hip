@@ -20,25 +20,46 @@ namespace misa {
 
 constexpr int kLdsStride = kHeadDim + 8;  // bf16 per key row in LDS (16 B pad)
 
-// Row layout of the A operand. With AP <= 16 head slots, G = AP / 4 row tiles
-// form a "quad" of four queries: row r of tile k in the quad is query r / 4,
-// head slot 4 k + r % 4, so the four MFMA result rows a lane holds are four
-// heads of one query in every tile of the quad and the head sum needs no
-// cross-lane step. With AP >= 32 a query fills AP / 16 whole tiles (row r =
-// head slot) and the sum adds the lane groups with two exchanges.
-template <int AP>
+// Row layout of the A operand. With AP <= 16 head slots and RPW a multiple of
+// G = AP / 4, G row tiles form a "quad" of four queries: row r of tile k in the
+// quad is query r / 4, head slot 4 k + r % 4, so the four MFMA result rows a
+// lane holds are four heads of one query in every tile of the quad; the head
+// sum needs no cross-lane step and every lane stores its own query's score.
+// Otherwise rows are linear (row = tile * 16 + r, query row / AP): a query
+// fills AP / 16 whole tiles, or a tile holds 16 / AP queries, and the sum adds
+// the lane groups with one or two exchanges.
+template <int AP, int RPW>
 struct RowMap {
-  static constexpr bool QUAD = AP <= 16;
-  static constexpr int G = QUAD ? AP / 4 : AP / 16;  // tiles per quad / per query
+  static constexpr bool QUAD = AP <= 16 && RPW % (AP / 4) == 0;
+  static constexpr int G = QUAD ? AP / 4 : (AP >= 16 ? AP / 16 : 1);  // row tiles per slot
+  static constexpr int NQ = RPW / G;  // slots (quads or queries) per wave
   // (query index inside the workgroup, head slot) of row r of row tile rt
   static __device__ __forceinline__ void at(int rt, int r, int& qi, int& j) {
     if constexpr (QUAD) {
       qi = (rt / G) * 4 + (r >> 2);
       j = 4 * (rt % G) + (r & 3);
     } else {
-      qi = rt / G;
-      j = (rt % G) * 16 + r;
+      const int row = rt * 16 + r;
+      qi = row / AP;
+      j = row % AP;
     }
+  }
+  // query whose sums this lane holds for the slot that starts at row tile rt0
+  static __device__ __forceinline__ int slot_query(int rt0, int lane) {
+    int qi, j;
+    at(rt0, 4 * (lane >> 4), qi, j);
+    return qi;
+  }
+  // lanes that store a slot's sums (after the exchange the others hold copies)
+  static __device__ __forceinline__ bool writer(int lane) {
+    return QUAD || (AP >= 16 ? lane < 16 : (lane & 16) == 0);
+  }
+  static __device__ __forceinline__ float finish(float part) {
+    if constexpr (!QUAD) {
+      if constexpr (AP >= 8) part += __shfl_xor(part, 16, kWave);
+      if constexpr (AP >= 16) part += __shfl_xor(part, 32, kWave);
+    }
+    return part;
   }
 };
 
@@ -50,14 +71,14 @@ struct RowMap {
 // branch. RMM: also the per-split {min, max} score key of each query.
 template <int AP, int WR, int RPW, int CPW, bool FP8, bool RMM>
 __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
-  using RM = RowMap<AP>;
+  using RM = RowMap<AP, RPW>;
   // key tiles in flight per workgroup (fewer when the row tiles use many registers)
   constexpr int R = (RPW >= 4 && !FP8) ? 2 : 4;
   constexpr int WC = 4 / WR;
   constexpr int ROWS = WR * RPW * 16;
   constexpr int QW = ROWS / AP;                     // queries per workgroup
   constexpr int KT = WC * CPW * 16;                 // keys per LDS tile
-  constexpr int NQ = RM::QUAD ? RPW / RM::G : RPW / RM::G;  // quads / queries per wave
+  constexpr int NQ = RM::NQ;                        // quads / queries per wave
   constexpr int CH_PER_ROW = FP8 ? 8 : 16;          // 16-byte global chunks per key row
   constexpr int CHUNKS = KT * CH_PER_ROW / 256;     // chunks per thread per tile
   static_assert(AP >= 4 && (AP & (AP - 1)) == 0, "AP must be a power of two >= 4");
@@ -181,13 +202,10 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   float smin[NQ], smax[NQ];
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
-    const int rt0 = wr * RPW + s * RM::G;
-    int qi, j;
-    RM::at(rt0, 4 * (lane >> 4), qi, j);
+    const int qi = RM::slot_query(wr * RPW + s * RM::G, lane);
     const int t = g * QW + qi;
-    const bool writer = RM::QUAD || lane < 16;  // AP >= 32: lane group 0 holds the sums
     q_n[s] = qn[qi];
-    q_row[s] = p.S + (size_t)(writer && t < p.T ? t : p.T) * p.S_ld;
+    q_row[s] = p.S + (size_t)(RM::writer(lane) && t < p.T ? t : p.T) * p.S_ld;
     smin[s] = __builtin_huge_valf();
     smax[s] = -__builtin_huge_valf();
   }
@@ -242,11 +260,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
           for (int k = 0; k < RM::G; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) part += wv[s * RM::G + k][i] * fmaxf(acc[s * RM::G + k][i], 0.f);
-          if constexpr (!RM::QUAD) {
-            part += __shfl_xor(part, 16, kWave);
-            part += __shfl_xor(part, 32, kWave);
-          }
-          const float v = part * kscale;
+          const float v = RM::finish(part) * kscale;
           q_row[s][col] = v;
           if constexpr (RMM) {
             const bool vis = col < q_n[s];
@@ -268,12 +282,8 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
         lo = fminf(lo, __shfl_xor(lo, off, kWave));
         hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
       }
-      const int rt0 = wr * RPW + s * RM::G;
-      int qi, j;
-      RM::at(rt0, 4 * (lane >> 4), qi, j);
-      const int t = g * QW + qi;
-      const bool writer = RM::QUAD || lane < 16;
-      if (writer && (lane & 15) == 0 && t < p.T) {
+      const int t = g * QW + RM::slot_query(wr * RPW + s * RM::G, lane);
+      if (RM::writer(lane) && (lane & 15) == 0 && t < p.T) {
         // an empty range (no visible key here) stays {max key, 0}
         const bool any = lo <= hi;
         p.rmm[((size_t)split * p.T + t) * 2] = any ? score_key(lo) : 0xffffffffu;
@@ -294,15 +304,15 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   constexpr int WC = 4 / WR;                        // key groups per tile (waves sharing rows)
   constexpr int ROWS = WR * RPW * 16;               // rows per workgroup
   constexpr int QW = ROWS / AP;                     // queries per workgroup
-  constexpr int TPQ = AP >= 16 ? AP / 16 : 1;       // row tiles per query
-  constexpr int NQ = RPW / TPQ;                     // query slots per lane
+  using RM = RowMap<AP, RPW>;
+  constexpr int NQ = RM::NQ;                        // quads / queries per wave
   constexpr int D = (RPW >= 8 && !FP8) ? 2 : 4;     // key groups in flight per wave
   constexpr int NV = FP8 ? 2 : 4;                   // 16-byte loads per lane per group
   constexpr int KT = 16 * WC;                       // keys per tile
   static_assert(WR == 1 || WR == 2 || WR == 4, "WR must divide the four waves");
   static_assert(AP >= 4 && (AP & (AP - 1)) == 0, "AP must be a power of two >= 4");
   static_assert(ROWS % AP == 0 && QW >= 1, "row tiles must hold whole queries");
-  static_assert(AP < 16 || RPW % TPQ == 0, "a wave must hold whole queries");
+  static_assert(RPW % RM::G == 0, "a wave must hold whole quads or queries");
   static_assert(WR == 1 || RPW * 16 % AP == 0, "row waves must hold whole queries");
   static_assert(!GATHER || QW == 1, "gather mode scores one query per workgroup");
 
@@ -441,17 +451,24 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   float wv[RPW][4];
 #pragma unroll
   for (int r = 0; r < RPW && STAGE; ++r) {
-    const int row = (wr * RPW + r) * 16 + (lane & 15);
+    // staged rows are in (query, slot) order: row qi * AP + j
+    int qi, j;
+    RM::at(wr * RPW + r, lane & 15, qi, j);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = __builtin_bit_cast(bf16x8, qsh[row * QSTR + 4 * slice + ks]);
+    for (int ks = 0; ks < 4; ++ks)
+      afrag[r][ks] = __builtin_bit_cast(bf16x8, qsh[(qi * AP + j) * QSTR + 4 * slice + ks]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[r][i] = wsh[(wr * RPW + r) * 16 + 4 * slice + i];
+    for (int i = 0; i < 4; ++i) {
+      RM::at(wr * RPW + r, 4 * slice + i, qi, j);
+      wv[r][i] = wsh[qi * AP + j];
+    }
   }
 #pragma unroll
   for (int r = 0; r < RPW && !STAGE; ++r) {
     {
-      const int row = (wr * RPW + r) * 16 + (lane & 15);
-      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      int qi, j;
+      RM::at(wr * RPW + r, lane & 15, qi, j);
+      const int t = g * QW + qi;
       if (t < p.T && j < p.A) {
         const bf16x8* src = reinterpret_cast<const bf16x8*>(
             p.q + ((size_t)t * p.H + j) * kHeadDim + 32 * slice);
@@ -464,8 +481,9 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = (wr * RPW + r) * 16 + 4 * slice + i;
-      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      int qi, j;
+      RM::at(wr * RPW + r, 4 * slice + i, qi, j);
+      const int t = g * QW + qi;
       wv[r][i] = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
     }
   }
@@ -479,17 +497,18 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     for (int d = 0; d < D; ++d) load_key(k0[d], d);
   }
 
-  const bool writer = AP >= 16 ? (lane < 16) : (AP == 8 ? ((lane & 16) == 0) : true);
+  // stores need no mask: a key past the query's candidates or visible length
+  // lands inside the padded row, and lanes without a query (or holding copies)
+  // write to the dump row S[T]
   int q_n[NQ];
   float* q_row[NQ];
   float smin[NQ], smax[NQ];
 #pragma unroll
   for (int s = 0; s < NQ; ++s) {
-    const int rt0 = wr * RPW + s * TPQ;
-    const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * slice) / AP;
+    const int qi = RM::slot_query(wr * RPW + s * RM::G, lane);
     const int t = g * QW + qi;
-    q_n[s] = writer ? qn[qi] : 0;
-    q_row[s] = p.S + (size_t)(t < p.T ? t : 0) * p.S_ld;
+    q_n[s] = qn[qi];
+    q_row[s] = p.S + (size_t)(RM::writer(lane) && t < p.T ? t : p.T) * p.S_ld;
     smin[s] = __builtin_huge_valf();
     smax[s] = -__builtin_huge_valf();
   }
@@ -544,20 +563,16 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
       }
 #pragma unroll
       for (int s = 0; s < NQ; ++s) {
-        const int r0 = s * TPQ;
         float part = 0.f;
 #pragma unroll
-        for (int tq = 0; tq < TPQ; ++tq)
+        for (int k = 0; k < RM::G; ++k)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part += wv[r0 + tq][i] * fmaxf(acc[r0 + tq][i], 0.f);
-        if constexpr (AP >= 8) part += __shfl_xor(part, 16, kWave);
-        if constexpr (AP >= 16) part += __shfl_xor(part, 32, kWave);
-        if (col < q_n[s] && (!GATHER || key >= 0)) {
-          const float v = part * kscale;
-          q_row[s][col] = v;
-          smin[s] = fminf(smin[s], v);
-          smax[s] = fmaxf(smax[s], v);
-        }
+          for (int i = 0; i < 4; ++i) part += wv[s * RM::G + k][i] * fmaxf(acc[s * RM::G + k][i], 0.f);
+        const float v = RM::finish(part) * kscale;
+        q_row[s][col] = v;
+        const bool vis = col < q_n[s];  // (a gathered column past the candidates has key -1)
+        smin[s] = fminf(smin[s], vis ? v : __builtin_huge_valf());
+        smax[s] = fmaxf(smax[s], vis ? v : -__builtin_huge_valf());
       }
     }
   }
@@ -574,9 +589,8 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
         lo = fminf(lo, __shfl_xor(lo, off, kWave));
         hi = fmaxf(hi, __shfl_xor(hi, off, kWave));
       }
-      const int rt0 = wr * RPW + s * TPQ;
-      const int qi = AP >= 16 ? (rt0 * 16) / AP : (rt0 * 16 + 4 * slice) / AP;
-      if (writer && (lane & 15) == 0) {
+      const int qi = RM::slot_query(wr * RPW + s * RM::G, lane);
+      if (RM::writer(lane) && (lane & 15) == 0) {
         rlo[wc][qi] = lo;
         rhi[wc][qi] = hi;
       }
