@@ -45,9 +45,10 @@ struct LaunchCtx {
   }
 };
 
-// Row stride (in elements) of internal [rows, n] buffers: a multiple of 64 so
-// rows start 256-byte aligned and can be read with 16-byte vector loads.
-inline long long padded_ld(long long n) { return ((n + 63) / 64) * 64; }
+// Row stride (in elements) of internal [rows, n] buffers: a multiple of 128 so
+// rows start 512-byte aligned, can be read with 16-byte vector loads, and hold
+// whole 128-key score tiles (the scoring kernels write every column of a tile).
+inline long long padded_ld(long long n) { return ((n + 127) / 128) * 128; }
 
 // ---- router side (route_kernels.hip)
 // Full-block key sums ksum[ceil(L/B), 128] (and optional means kbar) and, when
@@ -104,7 +105,7 @@ struct ScoreArgs {
   int32_t* cand_out;
   int32_t* ncand_out;
   float* S;              // output rows; launch_score_keys needs T + 1 rows (row T takes
-                         // the writes of lanes without a query) and S_ld a multiple of 64
+                         // the writes of lanes without a query) and S_ld a multiple of 128
   long long S_ld;
   uint32_t* rmm;         // optional [nsplit, T, 2] per-split {min, max} score key of each row
   uint32_t* zero;        // optional buffer the workgroups clear (each a share) ...

@@ -696,6 +696,7 @@ static bool direct_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, long long ro
 
 hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* nsplit_out) {
   if (a.T == 0) return hipSuccess;
+  if (a.S_ld % 128 != 0 || a.S_ld < a.L) return hipErrorInvalidValue;  // whole tiles per row
   const int ap = pad_heads(a.A);
   const long long rows = (long long)a.T * ap;
   // Prefill-like batches (many queries whose prefixes grow) go heavy-first.
@@ -713,16 +714,17 @@ hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* ns
   if (done) return err;
   // larger batches (prefill): LDS-staged key tiles shared by 256 rows
   switch (ap) {
-    case 4: return run_score<4, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
-    case 8: return run_score<8, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
-    case 16: return run_score<16, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
-    case 32: return run_score<32, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
-    default: return run_score<64, 4, 4, 4>(cx, a, fp8, nm, nsplit_out);
+    case 4: return run_score<4, 4, 4, 8>(cx, a, fp8, nm, nsplit_out);
+    case 8: return run_score<8, 4, 4, 8>(cx, a, fp8, nm, nsplit_out);
+    case 16: return run_score<16, 4, 4, 8>(cx, a, fp8, nm, nsplit_out);
+    case 32: return run_score<32, 4, 4, 8>(cx, a, fp8, nm, nsplit_out);
+    default: return run_score<64, 4, 4, 8>(cx, a, fp8, nm, nsplit_out);
   }
 }
 
 hipError_t launch_score_gather(const LaunchCtx& cx, ScoreArgs a, bool fp8) {
   if (a.T == 0) return hipSuccess;
+  if (a.S_ld % 128 != 0 || a.S_ld < a.cand_max) return hipErrorInvalidValue;  // whole tiles per row
   a.reverse = 0;
   a.rmm = nullptr;
   a.A = a.H;
