@@ -87,6 +87,50 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
 #pragma unroll
     for (int s = 0; s < 4; ++s) qa[i][s] = __builtin_bit_cast(bf16x8, ok ? src[s] : u32x4{0u, 0u, 0u, 0u});
   }
+  // hi / lo bf16 parts of the workgroup's block means, staged once in LDS for
+  // the four waves (rows padded by 16 bytes: conflict-free 16-byte reads)
+  constexpr int NB = TPW * kFastTile;
+  constexpr int RS = kHeadDim + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t smh[NB * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t sml[NB * RS];
+  {
+    const int bstart = tr * NB;
+    constexpr int NC = NB * 16 / 256;  // 16-byte chunks (8 dims) per thread
+    u32x4 hv[NC], lv[NC];
+    if (kb16) {
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        const int c = tid + 256 * u, r = c >> 4, v = c & 15;
+        const int blk = min(bstart + r, M - 1);  // past the end: any valid block, zeroed below
+        hv[u] = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim)[v];
+        lv[u] = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + kHeadDim)[v];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        const int c = tid + 256 * u, r = c >> 4, v = c & 15;
+        const int blk = min(bstart + r, M - 1);
+        const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)blk * kHeadDim + 8 * v);
+        const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          uint32_t ha, la, hb, lb;
+          split_bf16((double)(p < 2 ? x0[2 * p] : x1[2 * p - 4]), ha, la);
+          split_bf16((double)(p < 2 ? x0[2 * p + 1] : x1[2 * p - 3]), hb, lb);
+          hv[u][p] = ha | (hb << 16);
+          lv[u][p] = la | (lb << 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int c = tid + 256 * u, r = c >> 4, v = c & 15;
+      const bool ok = bstart + r < M;
+      *reinterpret_cast<u32x4*>(&smh[r * RS + 8 * v]) = ok ? hv[u] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(&sml[r * RS + 8 * v]) = ok ? lv[u] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
   float best[QG][4], second[QG][4], err[QG][4];
   int arg[QG][4];
 #pragma unroll
@@ -105,39 +149,13 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
     const int blk = b0 + col;
     // B operands of this lane's block: hi, lo and |hi|, dims 32g .. 32g+31
     bf16x8 bh[4], bl[4], ba[4];
-    if (blk < M) {
-      if (kb16) {
-        const u32x4* sh = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + 32 * g);
-        const u32x4* sl = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + kHeadDim + 32 * g);
+    const int rl = (tt * kFastTile + col) * RS + 32 * g;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 h4 = sh[s];
-          bh[s] = __builtin_bit_cast(bf16x8, h4);
-          bl[s] = __builtin_bit_cast(bf16x8, sl[s]);
-          ba[s] = __builtin_bit_cast(bf16x8, h4 & u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu});
-        }
-      } else {
-        const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)blk * kHeadDim + 32 * g);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const f32x4 x0 = src[2 * s], x1 = src[2 * s + 1];
-          u32x4 h4, l4;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            uint32_t ha, la, hb, lb;
-            split_bf16((double)(p < 2 ? x0[2 * p] : x1[2 * p - 4]), ha, la);
-            split_bf16((double)(p < 2 ? x0[2 * p + 1] : x1[2 * p - 3]), hb, lb);
-            h4[p] = ha | (hb << 16);
-            l4[p] = la | (lb << 16);
-          }
-          bh[s] = __builtin_bit_cast(bf16x8, h4);
-          bl[s] = __builtin_bit_cast(bf16x8, l4);
-          ba[s] = __builtin_bit_cast(bf16x8, h4 & u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu});
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) bh[s] = bl[s] = ba[s] = bf16x8{};
+    for (int s = 0; s < 4; ++s) {
+      const u32x4 h4 = *reinterpret_cast<const u32x4*>(&smh[rl + 8 * s]);
+      bh[s] = __builtin_bit_cast(bf16x8, h4);
+      bl[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&sml[rl + 8 * s]));
+      ba[s] = __builtin_bit_cast(bf16x8, h4 & u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu});
     }
 #pragma unroll
     for (int i = 0; i < QG; ++i) {
