@@ -64,10 +64,66 @@ __device__ __forceinline__ void dpp_merge(float& b, float& s, float& e, int& a) 
 // steps, and holds rows 4(l/16) + i of column l % 16 of the result.
 // kb16 [M][2][128] holds the hi / lo split of every block mean; without it
 // (cached means) the split is formed here from kbar.
-template <int QG, int TPW>
+// Settling and selection outputs of the single-pass form (see below).
+struct RouteSettle {
+  const float* w;
+  const double* ksum;  // block sums (used when kbar is null)
+  const double* tsum;  // each query's last-block sum
+  int A;
+  int32_t* heads;
+  float* r_out;
+  uint16_t* qr;
+  float* wr;
+};
+
+// Exact q . m_b over this lane's 32 dims (32 g .. 32 g + 31) in float64; qa
+// holds those dims of the head's q row, m_b = src[b] / div (block sums) or the
+// cached mean, src rows of 128 values.
+__device__ __forceinline__ double exact_part32(const bf16x8 (&qa)[4], const double* sum_row,
+                                               const float* mean_row, int g) {
+  double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const u32x4 qw = __builtin_bit_cast(u32x4, qa[s]);
+    if (mean_row) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(mean_row + 32 * g + 8 * s);
+      const f32x4 x0 = src[0], x1 = src[1];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float a = p < 2 ? x0[2 * p] : x1[2 * p - 4], b = p < 2 ? x0[2 * p + 1] : x1[2 * p - 3];
+        acc0 = fma((double)bf16_bits_to_f32(qw[p] & 0xffffu), (double)a, acc0);
+        acc1 = fma((double)bf16_bits_to_f32(qw[p] >> 16), (double)b, acc1);
+      }
+    } else {
+      const f64x2* src = reinterpret_cast<const f64x2*>(sum_row + 32 * g + 8 * s);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const f64x2 k2 = src[p];
+        acc0 = fma((double)bf16_bits_to_f32(qw[p] & 0xffffu), k2[0], acc0);
+        acc1 = fma((double)bf16_bits_to_f32(qw[p] >> 16), k2[1], acc1);
+      }
+    }
+  }
+  return acc0 + acc1;
+}
+
+// Sum over the four lanes col, col + 16, col + 32, col + 48 (every one receives it).
+__device__ __forceinline__ double sum_groups(double v) {
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+// FUSED (every complete block of each query inside this workgroup's range,
+// ntr == 1): instead of writing partial records, the workgroup settles each
+// head's maximum in float64 (the candidate block of every head, all blocks
+// for the rare head whose second-best bf16 score reaches the leader's bound,
+// and the query's last block), then ranks the heads and writes heads, r and
+// the packed q rows and weights of the chosen heads, as k_route_exact does.
+template <int QG, int TPW, bool FUSED>
 __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int32_t* pos, int T, int H,
                                                     int L, int B, int ntr, const uint16_t* kb16,
-                                                    const float* kbar, RoutePart* part) {
+                                                    const float* kbar, RoutePart* part, RouteSettle st) {
   const int tr = blockIdx.x, tq0 = blockIdx.y * QG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,6 +184,16 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
       const bool ok = bstart + r < M;
       *reinterpret_cast<u32x4*>(&smh[r * RS + 8 * v]) = ok ? hv[u] : u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&sml[r * RS + 8 * v]) = ok ? lv[u] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // (single-pass form) the queries' last-block sums, for the settling below
+  static_assert(!FUSED || QG <= 2, "two staged last-block rows per workgroup");
+  __shared__ double tsh[FUSED ? QG : 1][kHeadDim];
+  if constexpr (FUSED) {
+    const int i = tid >> 7, d = tid & 127;  // 256 threads: two rows of 128
+    if (i < QG) {
+      const int t = min(tq0 + i, T - 1);
+      tsh[i][d] = st.tsum[(size_t)t * kHeadDim + d];
     }
   }
   __syncthreads();
@@ -191,19 +257,164 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
       dpp_merge<0x124>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:4
       dpp_merge<0x128>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:8
     }
-  if (col == 0) {
+  if constexpr (!FUSED) {
+    if (col == 0) {
+#pragma unroll
+      for (int i = 0; i < QG; ++i) {
+        const int t = tq0 + i;
+        if (t >= T) break;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          RoutePart r;
+          r.best = best[i][e];
+          r.second = second[i][e];
+          r.err = err[i][e];
+          r.arg = arg[i][e];
+          part[((size_t)t * ntr + tr) * kWave + kFastTile * wv + 4 * g + e] = r;
+        }
+      }
+    }
+    return;
+  } else {
+    __shared__ double rsh[QG][kWave];
+    __shared__ __attribute__((aligned(16))) uint16_t qrow[4][kHeadDim];  // per wave: one q row
+    __shared__ int rank_part[QG][4][kWave];
+    __shared__ int slot_of[QG][kWave];
+    const double divb = kbar ? 1.0 : (double)B;
 #pragma unroll
     for (int i = 0; i < QG; ++i) {
       const int t = tq0 + i;
-      if (t >= T) break;
+      const int tc = t < T ? t : T - 1;  // (rows past T compute on a valid query, never written)
+      // the row group of head 16 wv + 4 g + e holds its merged record; code it as
+      // -1 (no block can be positive), the leader block, or the leader + 2^30 when
+      // the second best reaches the leader's bound (every block evaluated)
+      int code[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        RoutePart r;
-        r.best = best[i][e];
-        r.second = second[i][e];
-        r.err = err[i][e];
-        r.arg = arg[i][e];
-        part[((size_t)t * ntr + tr) * kWave + kFastTile * wv + 4 * g + e] = r;
+        const float thr = best[i][e] - 2.f * err[i][e];
+        const bool use = arg[i][e] >= 0 && best[i][e] + err[i][e] >= 0.f;
+        code[e] = use ? (arg[i][e] | (second[i][e] >= thr ? (1 << 30) : 0)) : -1;
+      }
+      // this lane's A-operand head h_a = 16 wv + col sits in row group col / 4, element col % 4
+      const int srcl = 16 * (col >> 2) + col;
+      int c = -1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = __shfl(code[e], srcl, kWave);
+        c = (col & 3) == e ? v : c;
+      }
+      double m = 0.0;  // max over the candidates of ReLU(rho)
+      if (c >= 0) {
+        const int b = c & ((1 << 30) - 1);
+        const double rho = sum_groups(exact_part32(qa[i], st.ksum + (size_t)b * kHeadDim,
+                                                   kbar ? kbar + (size_t)b * kHeadDim : nullptr, g)) / divb;
+        m = rho > m ? rho : m;
+      }
+      uint64_t ambm = wave_ballot(g == 0 && c >= 0 && (c >> 30) != 0);
+      while (ambm) {
+        // a head whose bf16 scores cannot separate its blocks: every complete block
+        // in float64, the wave's 16 columns taking 16 blocks at a time
+        const int hc = __builtin_ctzll(ambm);  // column (head 16 wv + hc) of the lane group 0 bit
+        ambm &= ambm - 1;
+        if (col == hc) {
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            *reinterpret_cast<u32x4*>(&qrow[wv][32 * g + 8 * s2]) = __builtin_bit_cast(u32x4, qa[i][s2]);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the row is in LDS for the whole wave
+        __builtin_amdgcn_wave_barrier();
+        bf16x8 qh[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) qh[s2] = *reinterpret_cast<const bf16x8*>(&qrow[wv][32 * g + 8 * s2]);
+        double mb = 0.0;
+        for (int b0 = 0; b0 < nfull[i]; b0 += 2 * kFastTile) {  // uniform over the query
+          const int b1 = b0 + col, b2 = b0 + kFastTile + col;
+          const int c1 = min(b1, nfull[i] - 1), c2 = min(b2, nfull[i] - 1);
+          const double r1 = sum_groups(exact_part32(qh, st.ksum + (size_t)c1 * kHeadDim,
+                                                    kbar ? kbar + (size_t)c1 * kHeadDim : nullptr, g)) / divb;
+          const double r2 = sum_groups(exact_part32(qh, st.ksum + (size_t)c2 * kHeadDim,
+                                                    kbar ? kbar + (size_t)c2 * kHeadDim : nullptr, g)) / divb;
+          mb = r1 > mb ? r1 : mb;  // (c1, c2 are complete blocks of this query)
+          mb = r2 > mb ? r2 : mb;
+        }
+        // largest over the 16 columns
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const double o = __shfl_xor(mb, off, kWave);
+          mb = o > mb ? o : mb;
+        }
+        if (col == hc) m = mb > m ? mb : m;
+        __builtin_amdgcn_wave_barrier();
+      }
+      const int n = visible_len(pos[tc], L);
+      const int Mt = (int)(((long long)n + B - 1) / B);
+      if (Mt > 0) {
+        // the query's own last block, always exactly (its sum staged in LDS)
+        double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const u32x4 qw = __builtin_bit_cast(u32x4, qa[i][s2]);
+#pragma unroll
+          for (int p2 = 0; p2 < 4; ++p2) {
+            const int d = 32 * g + 8 * s2 + 2 * p2;
+            a0 = fma((double)bf16_bits_to_f32(qw[p2] & 0xffffu), tsh[i][d], a0);
+            a1 = fma((double)bf16_bits_to_f32(qw[p2] >> 16), tsh[i][d + 1], a1);
+          }
+        }
+        const double rho = sum_groups(a0 + a1) / (double)(n - (Mt - 1) * B);
+        m = rho > m ? rho : m;
+      }
+      const bool active = t < T && h_a < H;
+      const double r = active ? (double)st.w[(size_t)t * H + h_a] * m + 0.0 : -__builtin_huge_val();
+      if (g == 0) {
+        rsh[i][h_a] = r;
+        if (st.r_out && active) st.r_out[(size_t)t * H + h_a] = (float)r;
+      }
+    }
+    __syncthreads();
+    {
+      // rank of head h: wave j compares it with heads [16j, 16j + 16)
+      const int h = tid & 63, j = tid >> 6;
+#pragma unroll
+      for (int i = 0; i < QG; ++i) {
+        const double rh = rsh[i][h];
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const double r2 = rsh[i][16 * j + u];
+          cnt += (r2 > rh) || (r2 == rh && 16 * j + u < h);
+        }
+        rank_part[i][j][h] = cnt;
+      }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      const int h = tid;
+#pragma unroll
+      for (int i = 0; i < QG; ++i) {
+        const int t = tq0 + i;
+        const int rank = rank_part[i][0][h] + rank_part[i][1][h] + rank_part[i][2][h] + rank_part[i][3][h];
+        const bool sel = t < T && h < H && rank < st.A;
+        const uint64_t mask = wave_ballot(sel);
+        const int slot = sel ? lanes_below(mask) : -1;
+        slot_of[i][h] = slot;
+        if (sel) {
+          if (st.heads) st.heads[(size_t)t * st.A + slot] = h;
+          if (st.wr) st.wr[(size_t)t * st.A + slot] = st.w[(size_t)t * H + h];
+        }
+      }
+    }
+    if (st.qr) {
+      __syncthreads();
+      // the lanes that hold a chosen head's q row write it to its slot
+#pragma unroll
+      for (int i = 0; i < QG; ++i) {
+        const int slot = slot_of[i][h_a];
+        if (slot >= 0) {
+          u32x4* dst = reinterpret_cast<u32x4*>(st.qr + ((size_t)(tq0 + i) * st.A + slot) * kHeadDim + 32 * g);
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) dst[s2] = __builtin_bit_cast(u32x4, qa[i][s2]);
+        }
       }
     }
   }
@@ -411,10 +622,10 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* q, const fl
 // ---------------------------------------------------------------------------
 
 int route_fast_parts(int L, int B, int T) {
+  (void)T;
   const int M = (int)(((long long)L + B - 1) / B);
   const int tiles = (M + kFastTile - 1) / kFastTile;
-  const int tpw = (long long)tiles * T > 4096 ? 8 : 1;
-  return (tiles + tpw - 1) / tpw;
+  return (tiles + 7) / 8;  // ranges of eight block tiles
 }
 
 size_t route_part_bytes() { return sizeof(RoutePart); }
@@ -430,20 +641,19 @@ hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const floa
                               const float* kbar, const double* tsum, void* part, int32_t* heads,
                               float* r_out, uint16_t* qr, float* wr) {
   if (T == 0) return hipSuccess;
-  const bool wide = route_fast_wins(L, B, T);  // many queries: 8 tiles and 2 queries per workgroup
   const int ntr = route_fast_parts(L, B, T);
   RoutePart* pp = reinterpret_cast<RoutePart*>(part);
   const uint16_t* kb = kbar ? nullptr : kb16;
-  hipError_t e;
-  if (wide)
-    e = cx.launch("route_fast", k_route_fast<2, 8>, dim3(ntr, (T + 1) / 2), dim3(256), 0, q, pos, T, H, L,
-                  B, ntr, kb, kbar, pp);
-  else
-    e = cx.launch("route_fast", k_route_fast<1, 1>, dim3(ntr, T), dim3(256), 0, q, pos, T, H, L, B, ntr,
-                  kb, kbar, pp);
+  const RouteSettle st{w, ksum, tsum, A, heads, r_out, qr, wr};
+  const dim3 grid(ntr, (T + 1) / 2);  // two queries and eight block tiles per workgroup
+  if (ntr == 1)  // every block in one range: settle and select in the same launch
+    return cx.launch("route_fast", k_route_fast<2, 8, true>, grid, dim3(256), 0, q, pos, T, H, L, B, ntr, kb,
+                     kbar, pp, st);
+  hipError_t e = cx.launch("route_fast", k_route_fast<2, 8, false>, grid, dim3(256), 0, q, pos, T, H, L, B,
+                           ntr, kb, kbar, pp, st);
   if (e != hipSuccess) return e;
   return cx.launch("route_exact", k_route_exact, dim3(T), dim3(256), 0, q, w, pos, H, L, B, A, ntr,
-                   (wide ? 8 : 1) * kFastTile, (const RoutePart*)pp, ksum, kbar, tsum, heads, r_out, qr, wr);
+                   8 * kFastTile, (const RoutePart*)pp, ksum, kbar, tsum, heads, r_out, qr, wr);
 }
 
 }  // namespace misa

@@ -74,7 +74,9 @@ ROUTE_CASES = [
     (7, 1100, 1100, 64, 8, 16, O.KDT_BF16),
     (8, 2200, 2200, 32, 8, 128, O.KDT_FP8),
     (9, 4500, 600, 64, 8, 5, O.KDT_BF16),
-    # few query-head rows and several blocks per pooling group (one-pass router)
+    # many queries and more than 128 blocks: bf16 pass over two ranges, separate settling
+    (12, 600, 20000, 64, 8, 128, O.KDT_FP8),
+    # few query-head rows and several blocks per pooling group
     (10, 6, 50000, 64, 8, 100, O.KDT_FP8),
     (11, 3, 30000, 48, 5, 64, O.KDT_BF16),
 ]
