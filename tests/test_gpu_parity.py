@@ -128,6 +128,8 @@ MISA_CASES = [
     (21, 40, 900, 64, 12, 128, 77, O.KDT_FP8, "random"),
     (22, 20, 700, 48, 20, 64, 50, O.KDT_BF16, "random"),
     (23, 40, 17000, 32, 8, 128, 300, O.KDT_FP8, "random"),
+    # many rows longer than 8192 keys: the row selection streams through the rows
+    (24, 1100, 9000, 16, 4, 128, 300, O.KDT_BF16, "random"),
 ]
 
 
