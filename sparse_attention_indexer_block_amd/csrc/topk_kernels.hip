@@ -101,27 +101,24 @@ __device__ __forceinline__ int block_scan(int v, TopkShared<NT>& sm, int* total)
 template <int NT>
 __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, TopkShared<NT>& sm) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t a = __shfl_xor(lo, off, kWave), b = __shfl_xor(hi, off, kWave);
-    lo = a < lo ? a : lo;
-    hi = b > hi ? b : hi;
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane == 0) {
     sm.wmin[w] = lo;
     sm.wmax[w] = hi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t a = sm.wmin[0], b = sm.wmax[0];
-    for (int i = 1; i < TopkShared<NT>::NW; ++i) {
-      a = sm.wmin[i] < a ? sm.wmin[i] : a;
-      b = sm.wmax[i] > b ? sm.wmax[i] : b;
-    }
-    sm.umin = a;
-    sm.umax = b;
+  // every thread folds the per-wave extremes itself and stores the same values
+  // (a thread reads back its own store: no second barrier; the next writer of
+  // wmin / umin is always behind another barrier)
+  uint32_t a = sm.wmin[0], b = sm.wmax[0];
+#pragma unroll
+  for (int i = 1; i < TopkShared<NT>::NW; ++i) {
+    a = sm.wmin[i] < a ? sm.wmin[i] : a;
+    b = sm.wmax[i] > b ? sm.wmax[i] : b;
   }
-  __syncthreads();
+  sm.umin = a;
+  sm.umax = b;
 }
 
 // Locate the bin holding the rem-th largest item of hist[0, nb) (nb a power of
