@@ -205,7 +205,15 @@ def cpu_baseline(inp, wl, budget_s=12.0):
         pairs += sum(P.n(t) for t in range(P.T))
         reps += 1
     dt = time.perf_counter() - t0
-    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(threads), "cpu_model": model, "kind": "oracle",
             "sample": f"{reps} full steps of {wl.name} (all {wl.T} queries: decode inputs, routing, "
                       f"routed scores, top-k', 64-head rerank, top-k) in {dt:.1f} s"}
 

@@ -2,8 +2,9 @@
 benchmark times (same entry points, same shapes).
 
 c1 (tiny decode) and the decode configurations are checked on every row; the
-causal prefill (16384 x 16384) is checked on sampled rows, edge rows included,
-with the router checked on a larger sample.
+causal prefill (16384 x 16384) has its routed heads checked on every query, the
+shape of every selection (counts, order, range, padding) checked on every row,
+and the selection itself checked on sampled rows, edge rows included.
 """
 import numpy as np
 import pytest
@@ -65,10 +66,22 @@ def test_c3_prefill_sampled():
     torch.cuda.synchronize()
     rng = np.random.default_rng(3)
     edge = [0, 1, 2, 126, 127, 128, 129, 255, 256, 2046, 2047, 2048, 2049, 8191, 8192, 16382, 16383]
-    rows_r = np.unique(np.concatenate([edge, rng.choice(wl.T, 400, replace=False)]))
-    Pr = oracle_problem(inp, wl.B, rows_r)
-    _, ill = check_heads(Pr, wl.A, _np(heads)[rows_r], _np(r)[rows_r])
+    # routed heads of every query, bit for bit
+    P = oracle_problem(inp, wl.B)
+    _, ill = check_heads(P, wl.A, _np(heads), _np(r))
     assert ill == 0
+    # every row: min(k, n_t) indices, ascending, inside the visible prefix, then padding
+    gi, gs = _np(idx), _np(sc)
+    n = np.minimum(np.maximum(inp["pos"].astype(np.int64) + 1, 0), wl.L)
+    kt = np.minimum(wl.k, n)
+    lead = np.arange(wl.k)[None, :] < kt[:, None]
+    assert np.array_equal(gi >= 0, lead), "selection counts or padding position"
+    assert np.all(gi[~lead] == -1) and np.all(np.isneginf(gs[~lead])), "padding values"
+    assert np.all(np.isfinite(gs[lead])), "selected scores"
+    assert np.all(gi[lead] < np.repeat(n, kt)), "index outside the visible prefix"
+    both = lead[:, 1:] & lead[:, :-1]
+    assert np.all(np.diff(gi, axis=1)[both] > 0), "indices not strictly ascending"
+    # the selection itself against the oracle on sampled rows, edge rows included
     rows = np.unique(np.concatenate([edge, rng.choice(wl.T, 24, replace=False)]))
     sub = {kk: (v[rows] if kk in ("q", "w", "pos") else v) for kk, v in inp.items()}
     _check_misa(sub, wl.B, wl.A, wl.k, _np(idx)[rows], _np(sc)[rows], label="c3")
