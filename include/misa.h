@@ -118,6 +118,18 @@ size_t misa_workspace_bytes(const misa_problem* p, int32_t op, int32_t A, int32_
 misa_status misa_block_means(const misa_problem* p, float* kbar, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* Incremental form of misa_block_means for a growing key array (the cached
+ * block statistics the MISA summary's "Metodologia: MISA" presumes when it
+ * calls the router's cost negligible): with p->L the new length, rows
+ * first_block .. ceil(L/B) - 1 of kbar are recomputed exactly as
+ * misa_block_means computes them, and only those blocks' keys are read; the
+ * rows before first_block are left as they are. After keys [L_old, L) were
+ * appended, first_block = L_old / B brings kbar up to date. first_block must
+ * lie in [0, ceil(L/B)] (MISA_ERR_INVALID_ARG otherwise; ceil(L/B) is a no-op);
+ * the workspace is that of misa_block_means. */
+misa_status misa_block_means_update(const misa_problem* p, int32_t first_block, float* kbar, void* ws,
+                                    size_t ws_bytes, void* stream);
+
 /* Router (MISA summary, "Metodologia: MISA", block-pooled router): heads[T,A]
  * int32 receives the routed heads of each query in ascending order; r[T,H]
  * float32 (may be NULL) receives r(t,h). The selection is taken in float64

@@ -7,6 +7,7 @@ loudly when the HIP library has not been built.
 
 Entry points (same names as the C ABI in include/misa.h):
     block_means(K, B, k_scale=None)                     -> kbar [ceil(L/B), 128] f32
+    block_means_update(K, B, kbar, first_block, k_scale=None) -> kbar (rows first_block.. recomputed)
     route(q, w, K, pos, B, A, k_scale=None, with_r=False) -> heads [T, A] i32 (, r [T, H] f32)
     score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None) -> (idx [T, k] i32, scores [T, k] f32)
     hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None) -> (idx, scores)
@@ -62,6 +63,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "misa_workspace_bytes": (sz, [P, i32, i32, i32, i32, i32]),
             "misa_block_means": (i32, [P, vp, vp, sz, vp]),
+            "misa_block_means_update": (i32, [P, i32, vp, vp, sz, vp]),
             "misa_route": (i32, [P, i32, vp, vp, vp, sz, vp]),
             "misa_score_topk": (i32, [P, i32, vp, i32, vp, vp, vp, sz, vp]),
             "misa_hier_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
@@ -159,6 +161,18 @@ def block_means(K, B, k_scale=None, ws=None):
     kbar = torch.empty((M, p.d), dtype=torch.float32, device=K.device)
     ws, n = _workspace(p, OP_BLOCK_MEANS, K.device, ws)
     _check(lib().misa_block_means(ctypes.byref(p), _ptr(kbar), _ptr(ws), n, _stream()))
+    return kbar
+
+
+def block_means_update(K, B, kbar, first_block, k_scale=None, ws=None):
+    """Recompute rows first_block.. of cached block means kbar in place for the
+    (grown) key array K; rows before first_block are kept."""
+    p = make_problem(None, None, K, None, B, k_scale)
+    M = -(-p.L // B)
+    if tuple(kbar.shape) != (M, p.d) or kbar.dtype != torch.float32 or not kbar.is_contiguous():
+        raise ValueError(f"kbar must be a contiguous float32 [{M}, {p.d}] tensor")
+    ws, n = _workspace(p, OP_BLOCK_MEANS, K.device, ws)
+    _check(lib().misa_block_means_update(ctypes.byref(p), int(first_block), _ptr(kbar), _ptr(ws), n, _stream()))
     return kbar
 
 

@@ -395,6 +395,23 @@ misa_status misa_block_means(const misa_problem* p, float* kbar, void* ws, size_
   return MISA_OK;
 }
 
+misa_status misa_block_means_update(const misa_problem* p, int32_t first_block, float* kbar, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, false));
+  MISA_TRY(check_out(kbar, "kbar"));
+  const int M = (int)(((long long)p->L + p->B - 1) / p->B);
+  if (first_block < 0 || first_block > M)
+    return fail(MISA_ERR_INVALID_ARG, "first_block = %d must lie in [0, ceil(L/B) = %d]", first_block, M);
+  if (first_block == M) return MISA_OK;
+  const Plan pl = make_plan(p, MISA_OP_BLOCK_MEANS, 1, 1, 1, 1);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, p->k_dtype == MISA_K_FP8_E4M3FN, p->L, p->B,
+                            at<double>(ws, pl.ksum), kbar, 0, nullptr, nullptr, false, nullptr, first_block),
+          "block means update");
+  return MISA_OK;
+}
+
 misa_status misa_route(const misa_problem* p, int32_t A, int32_t* heads, float* r, void* ws,
                        size_t ws_bytes, void* stream) {
   MISA_TRY(check_problem(p, true));

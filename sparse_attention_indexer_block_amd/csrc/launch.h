@@ -51,11 +51,13 @@ struct LaunchCtx {
 inline long long padded_ld(long long n) { return ((n + 127) / 128) * 128; }
 
 // ---- router side (route_kernels.hip)
-// Full-block key sums ksum[ceil(L/B), 128] (and optional means kbar) and, when
-// tsum is given, the sum of each query's last (possibly partial) block.
+// Full-block key sums ksum[ceil(L/B), 128] (and optional means kbar) of blocks
+// first_block .. ceil(L/B) - 1 and, when tsum is given, the sum of each query's
+// last (possibly partial) block.
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum, bool tails_only = false, uint16_t* kb16 = nullptr);
+                             double* tsum, bool tails_only = false, uint16_t* kb16 = nullptr,
+                             int first_block = 0);
 // MISA head routing with an exact result (route_fast.hip): bf16 block scores
 // with proven error bounds, then float64 settling of every head's maximum.
 // part: T * route_fast_parts(L, B, T) * 64 records of route_part_bytes();

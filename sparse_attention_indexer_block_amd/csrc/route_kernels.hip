@@ -406,9 +406,9 @@ __global__ __launch_bounds__(64) void k_gather_heads(const uint16_t* q, const fl
 
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum, bool tails_only, uint16_t* kb16) {
+                             double* tsum, bool tails_only, uint16_t* kb16, int first_block) {
   const int M = (int)(((long long)L + B - 1) / B);
-  const int base = tails_only ? M : 0;
+  const int base = tails_only ? M : (first_block < M ? first_block : M);
   const int grid = M - base + (tsum ? T : 0);
   if (grid == 0) return hipSuccess;
   const char* nm = tails_only ? "tail_sums" : "block_sums";

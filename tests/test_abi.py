@@ -95,6 +95,16 @@ def test_empty_batch_is_a_noop():
     assert _score(p, idx=None, sc=None, ws=None, nbytes=0) == 0
 
 
+def test_block_means_update_validation():
+    L = S.lib()
+    p = _problem(L=1000, B=128)  # 8 blocks
+    f = lambda fb, kbar=FAKE: L.misa_block_means_update(ctypes.byref(p), fb, kbar, FAKE, 1 << 40, None)
+    assert f(-1) == -1
+    assert f(9) == -1
+    assert f(3, kbar=None) == -1
+    assert f(8) == 0  # nothing to recompute: returns before any launch
+
+
 def test_workspace_sizes():
     L = S.lib()
     p = _problem(T=8, L=131072, k_dtype=1, k_scale=FAKE)

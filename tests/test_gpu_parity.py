@@ -60,6 +60,29 @@ def test_block_means(kdt):
         np.testing.assert_allclose(got, ref, rtol=2.5e-7, atol=1e-38)
 
 
+@pytest.mark.parametrize("kdt,B", [(O.KDT_BF16, 128), (O.KDT_FP8, 128), (O.KDT_FP8, 37)])
+def test_block_means_update(kdt, B):
+    """Cached means kept current while keys are appended: recomputing the rows
+    from the first touched block reproduces the full computation bit for bit,
+    and rows before it are left untouched."""
+    inp = synth.random_small(41, T=1, L=5000, H=8, k_dtype=kdt)
+    _, _, K, ks, _ = to_gpu(inp)
+    for L0, L1 in [(1000, 1001), (1023, 1024), (1024, 1300), (1, 5000), (4999, 5000)]:
+        K0, K1 = K[:L0], K[:L1]
+        s0 = ks[:L0] if ks is not None else None
+        s1 = ks[:L1] if ks is not None else None
+        M1 = -(-L1 // B)
+        kbar = torch.full((M1, 128), float("nan"), dtype=torch.float32, device=K.device)
+        M0 = -(-L0 // B)
+        kbar[:M0] = S.block_means(K0, B, s0)
+        keep = kbar[: L0 // B].clone()
+        S.block_means_update(K1, B, kbar, L0 // B, s1)
+        full = S.block_means(K1, B, s1)
+        torch.cuda.synchronize()
+        assert torch.equal(kbar, full), (L0, L1)
+        assert torch.equal(kbar[: L0 // B], keep)
+
+
 # ----------------------------------------------------------------- router
 
 ROUTE_CASES = [
