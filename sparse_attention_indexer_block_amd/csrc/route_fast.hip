@@ -281,10 +281,12 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
     __shared__ int rank_part[QG][4][kWave];
     __shared__ int slot_of[QG][kWave];
     const double divb = kbar ? 1.0 : (double)B;
+    // candidate of each head and its exact value, for every query of the group at
+    // once (no branch between the queries' requests)
+    int cq[QG];
+    double mq[QG];  // max over the candidates of ReLU(rho)
 #pragma unroll
     for (int i = 0; i < QG; ++i) {
-      const int t = tq0 + i;
-      const int tc = t < T ? t : T - 1;  // (rows past T compute on a valid query, never written)
       // the row group of head 16 wv + 4 g + e holds its merged record; code it as
       // -1 (no block can be positive), the leader block, or the leader + 2^30 when
       // the second best reaches the leader's bound (every block evaluated)
@@ -303,13 +305,18 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
         const int v = __shfl(code[e], srcl, kWave);
         c = (col & 3) == e ? v : c;
       }
-      double m = 0.0;  // max over the candidates of ReLU(rho)
-      if (c >= 0) {
-        const int b = c & ((1 << 30) - 1);
-        const double rho = sum_groups(exact_part32(qa[i], st.ksum + (size_t)b * kHeadDim,
-                                                   kbar ? kbar + (size_t)b * kHeadDim : nullptr, g)) / divb;
-        m = rho > m ? rho : m;
-      }
+      cq[i] = c;
+      const int b = c >= 0 ? (c & ((1 << 30) - 1)) : 0;  // (block 0 when there is none: unused)
+      const double rho = sum_groups(exact_part32(qa[i], st.ksum + (size_t)b * kHeadDim,
+                                                 kbar ? kbar + (size_t)b * kHeadDim : nullptr, g)) / divb;
+      mq[i] = c >= 0 && rho > 0.0 ? rho : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+      const int t = tq0 + i;
+      const int tc = t < T ? t : T - 1;  // (rows past T compute on a valid query, never written)
+      const int c = cq[i];
+      double m = mq[i];
       uint64_t ambm = wave_ballot(g == 0 && c >= 0 && (c >> 30) != 0);
       while (ambm) {
         // a head whose bf16 scores cannot separate its blocks: every complete block
