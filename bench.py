@@ -180,6 +180,28 @@ def time_path(S, path, wl, tensors, steps, warmup, use_graphs=True, A=None, kern
     return ms, kms, pct
 
 
+def quality(S, path, wl, inp, tensors, A=None):
+    """Selection quality beside speed (the pages report both): overlap (IoU) of
+    the selected token set with the dense indexer's top-k, and the fraction of
+    planted needles selected, for the method and for the dense indexer."""
+    import torch
+    q, w, K, ks, pos = tensors
+    idx = Step(S, path, wl, tensors, A=A)(tensors)[0]
+    dense = S.score_topk(q, w, K, pos, wl.B, wl.H, wl.k, ks)[0]
+    torch.cuda.synchronize()
+    X, D = idx.cpu().numpy(), dense.cpu().numpy()
+    ious, hit_x, hit_d, nn = [], 0, 0, 0
+    for t in range(wl.T):
+        xs, ds = set(X[t][X[t] >= 0].tolist()), set(D[t][D[t] >= 0].tolist())
+        ious.append(len(xs & ds) / max(1, len(xs | ds)))
+        for s_ in inp["needles"][t]:
+            nn += 1
+            hit_x += s_ in xs
+            hit_d += s_ in ds
+    return {"iou_vs_dense_topk": float(np.mean(ious)), "needle_recall": hit_x / nn if nn else None,
+            "dense_needle_recall": hit_d / nn if nn else None, "needles": nn}
+
+
 def pairs_of(inp):
     return int(np.sum(np.minimum(np.maximum(inp["pos"].astype(np.int64) + 1, 0), inp["wl"].L)))
 
@@ -350,6 +372,8 @@ def main():
                 flops = 2.0 * (A or w2.A) * 128 * p2
                 e["score_keys_tflops"] = flops / (k2["score_keys"][0] * 1e-3) / 1e12
                 e["score_keys_hbm_gbs"] = score_kernel_bytes(w2, A or w2.A) / (k2["score_keys"][0] * 1e-3) / 1e9
+            if not cached and "c3" not in nm and A is None:
+                e["quality"] = quality(S, path, w2, i2, t2)
             extra[label] = e
             del t2
         loaded.clear()
@@ -364,6 +388,7 @@ def main():
         extra["dense_over_routed_scoring_kernel_c4"] = ds / ms if ds and ms else None
         extra["context_pages_misa_vs_dsa_indexer_kernel_speedup"] = {"value": 3.82, "hardware": "NVIDIA H200"}
         rec["secondary"] = extra
+        rec["quality"] = quality(S, "hier", wl, inp, tensors)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         rec["cpu_baseline"] = cpu_baseline(inp, wl)
