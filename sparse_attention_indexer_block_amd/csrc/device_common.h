@@ -112,8 +112,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// Sum over the wave, returned in every lane: rows of 16 lanes reduce with
-// rotations, then the four row totals are read out as scalars.
 // Wave-wide minimum / maximum (every lane gets the result): DPP rotations inside
 // each row of 16 lanes, then the four row results through readlane.
 template <bool MAX>
@@ -130,6 +128,8 @@ __device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_ext_u32<false>(v); }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_ext_u32<true>(v); }
 
+// Sum over the wave, returned in every lane: rows of 16 lanes reduce with
+// rotations, then the four row totals are read out as scalars.
 __device__ __forceinline__ uint32_t wave_total_u32(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);  // row_ror:8
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);  // row_ror:4
