@@ -34,6 +34,11 @@ Where the pages leave a formula open, the fixed reading is:
   * router score r(t,h) = w[t,h] * max_b ReLU(q[t,h] . Kbar_{t,b}); the routed
     set is the first A heads under the key (-r, h).
   * HISA block score beta(t,b) = sum_h w[t,h] * ReLU(q[t,h] . Kbar_{t,b}).
+  * MISA inside HISA (the head axis and the token axis combined, as the MISA
+    summary's "Contribuciones Clave" and "Significado y Afirmaciones" call them
+    complementary): the routed heads R_t replace all H heads in both HISA
+    stages, beta_R(t,b) = sum_{h in R_t} w[t,h] * ReLU(q[t,h] . Kbar_{t,b}) and
+    I_R on the chosen blocks' tokens.
   * every selection keeps the first min(k, n) items under (-score, index);
     -0.0 compares equal to +0.0.
 """
@@ -272,3 +277,31 @@ def hisa_topk(P: Problem, m: int, k: int):
             else np.zeros(0, dtype=np.int64)
         out.append(first_k(dense_scores(P, t, cand), cand, k))
     return out, chosen
+
+
+def routed_block_scores(P: Problem, t: int, heads) -> np.ndarray:
+    """beta_R(t,b): the block score of HISA Stage 1 with only the routed heads
+    R_t [HISA Stage 1; MISA, the router's head subset]."""
+    heads = list(heads)
+    rho = block_logits(P, t)[heads]
+    return _canon((P.w[t, heads][:, None] * np.maximum(rho, 0.0)).sum(axis=0))
+
+
+def misa_hisa_topk(P: Problem, A: int, m: int, k: int, heads=None):
+    """MISA inside HISA: route A heads per query [MISA], keep the top-m blocks
+    by beta_R (lower block index first on ties) [HISA Stage 1], score the
+    visible tokens of those blocks with I_R and keep top-k [HISA Stage 2 with
+    the routed heads].  Returns (per-query results, chosen blocks, heads)."""
+    if heads is None:
+        heads, _ = route(P, A)
+    out, chosen = [], []
+    for t in range(P.T):
+        beta = routed_block_scores(P, t, heads[t])
+        blocks, _ = first_k(beta, np.arange(len(beta)), m)
+        blocks = np.sort(blocks)
+        chosen.append(blocks)
+        rng = block_ranges(P.n(t), P.B)
+        cand = np.concatenate([np.arange(*rng[b]) for b in blocks]) if len(blocks) \
+            else np.zeros(0, dtype=np.int64)
+        out.append(first_k(routed_scores(P, t, heads[t], cand), cand, k))
+    return out, chosen, heads

@@ -160,8 +160,9 @@ class Exact:
         return [self.w[t, h] * max([Fraction(0)] + [self.dot(self.q[t, h], c) for c in kb])
                 for h in range(self.H)]
 
-    def beta(self, t):
-        return [sum((self.w[t, h] * max(Fraction(0), self.dot(self.q[t, h], c)) for h in range(self.H)),
+    def beta(self, t, heads=None):
+        heads = range(self.H) if heads is None else heads
+        return [sum((self.w[t, h] * max(Fraction(0), self.dot(self.q[t, h], c)) for h in heads),
                     Fraction(0)) for c in self.kbar(t)]
 
 
@@ -209,6 +210,15 @@ def test_exact_brute_force_int_grid(seed, B):
         (si, _), bl = O.hisa_topk(P, m, k)[0][t], O.hisa_topk(P, m, k)[1][t]
         assert list(bl) == blocks
         assert sorted(si) == sorted(final)
+        # MISA inside HISA: the routed heads in both stages
+        blocks = _rank_select(X.beta(t, heads[t]), m)
+        cand = [s for b in blocks for s in range(b * B, min((b + 1) * B, n))]
+        final = [cand[j] for j in _rank_select([ir[s] for s in cand], k)]
+        res, mbl, _ = O.misa_hisa_topk(P, A, m, k, heads=heads)
+        mi, ms = res[t]
+        assert list(mbl[t]) == blocks
+        assert sorted(mi) == sorted(final)
+        assert [float(ir[s]) for s in mi] == list(ms)
 
 
 @pytest.mark.parametrize("seed", range(3))
@@ -301,6 +311,37 @@ def test_hisa_token_blocks_is_dense():
     inp = _medium(5, L=300)
     P = _P(inp, 1)
     _same(O.hisa_topk(P, 40, 25)[0], O.dense_topk(P, 25))
+
+
+def test_misa_hisa_all_heads_is_hisa():
+    """A = H routes every head, so both stages use all heads: HISA."""
+    inp = _medium(7)
+    for B, m in [(64, 3), (37, 5)]:
+        P = _P(inp, B)
+        res, blocks, heads = O.misa_hisa_topk(P, P.H, m, 30)
+        assert (heads == np.arange(P.H)).all()
+        ref, ref_blocks = O.hisa_topk(P, m, 30)
+        for t in range(P.T):
+            assert list(blocks[t]) == list(ref_blocks[t])
+            assert list(res[t][0]) == list(ref[t][0])
+            assert np.allclose(res[t][1], ref[t][1], rtol=1e-12, atol=1e-12)
+
+
+def test_misa_hisa_covering_prefix_is_misa():
+    """m * B >= n_t keeps every block, so the refine stage is MISA itself."""
+    inp = _medium(8)
+    for B, m in [(64, 11), (700, 1)]:
+        P = _P(inp, B)
+        res, _, heads = O.misa_hisa_topk(P, 4, m, 33)
+        _same(res, O.misa_topk(P, 4, 33, heads=heads)[0])
+
+
+def test_misa_hisa_token_blocks_is_misa():
+    """B = 1 makes beta_R the routed token score, so m >= k blocks give MISA's top-k."""
+    inp = _medium(9, L=300)
+    P = _P(inp, 1)
+    res, _, heads = O.misa_hisa_topk(P, 3, 40, 25)
+    _same(res, O.misa_topk(P, 3, 25, heads=heads)[0])
 
 
 def test_router_block_size_one_closed_form():
