@@ -14,6 +14,8 @@
  *   hisa_topk       top-m key blocks by their mean-pooled representative, then
  *                   the full indexer on the tokens of those blocks, then top-k
  *                   (HISA write-up, section 3, Stage 1 and Stage 2).
+ *   misa_hisa_topk  HISA with the routed heads in both stages: the head axis
+ *                   of MISA and the token axis of HISA combined.
  *   misa_block_means  the query-independent block means the router pools.
  *
  * Definitions (the pages give the structure; the exact formulas are fixed here):
@@ -77,7 +79,8 @@ typedef enum misa_op {
   MISA_OP_SCORE_TOPK = 1,
   MISA_OP_HIER_TOPK = 2,
   MISA_OP_HISA_TOPK = 3,
-  MISA_OP_BLOCK_MEANS = 4
+  MISA_OP_BLOCK_MEANS = 4,
+  MISA_OP_MISA_HISA_TOPK = 5
 } misa_op;
 
 /* One indexer problem. All pointers are device pointers. */
@@ -103,7 +106,8 @@ typedef struct misa_problem {
  * depends on pos[t]. The library trusts the values: results are those of the
  * definitions evaluated with these means, which is what misa_block_means
  * writes. Pointer must be 16-byte aligned. Used by misa_route,
- * misa_score_topk, misa_hier_topk and hisa_topk; misa_block_means ignores it. */
+ * misa_score_topk, misa_hier_topk, hisa_topk and misa_hisa_topk; misa_block_means
+ * ignores it. */
 
 /* Bytes of workspace entry point `op` needs for this problem and these
  * parameters (unused parameters are ignored). Returns 0 for an invalid request;
@@ -158,6 +162,20 @@ misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* head
  * those blocks with all H heads (I_all) and return the top-k. */
 misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* MISA inside HISA. The MISA technical summary presents head routing as an
+ * efficiency axis complementary to token-axis hierarchies such as HISA and
+ * combinable with them ("Contribuciones Clave", "Significado y Afirmaciones");
+ * the plain reading used here puts the A routed heads R_t (as misa_route picks
+ * them) in place of all H heads in both HISA stages:
+ *   beta_R(t,b) = sum_{h in R_t} w[t,h] * max(0, q[t,h] . Kbar_{t,b}),
+ * the top-m blocks by beta_R (ties to the lower block), I_R on the visible
+ * tokens of those blocks, and the top-k of those (scores hold I_R).
+ * `heads` [T,A] may supply the routed heads (distinct values in [0,H)); NULL
+ * routes inside the call. A == H with heads == NULL is hisa_topk. Errors as
+ * for misa_score_topk and hisa_topk. */
+misa_status misa_hisa_topk(const misa_problem* p, int32_t A, const int32_t* heads, int32_t m, int32_t k,
+                           int32_t* idx, float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /* Short static text for a status code. */
 const char* misa_status_str(int32_t status);

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI in include/misa.h):
     score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None) -> (idx [T, k] i32, scores [T, k] f32)
     hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None) -> (idx, scores)
     hisa_topk(q, w, K, pos, B, m, k, k_scale=None)      -> (idx, scores)
+    misa_hisa_topk(q, w, K, pos, B, A, m, k, k_scale=None, heads=None) -> (idx, scores)
 
 Inputs are CUDA (HIP) tensors: q [T,H,128] bfloat16 (or int16 bf16 bits),
 w [T,H] float32, K [L,128] bfloat16 / int16 bits, or uint8 / float8_e4m3fn
@@ -28,7 +29,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmisa.so")
 
-OP_ROUTE, OP_SCORE_TOPK, OP_HIER_TOPK, OP_HISA_TOPK, OP_BLOCK_MEANS = 0, 1, 2, 3, 4
+OP_ROUTE, OP_SCORE_TOPK, OP_HIER_TOPK, OP_HISA_TOPK, OP_BLOCK_MEANS, OP_MISA_HISA_TOPK = 0, 1, 2, 3, 4, 5
 KDT_BF16, KDT_FP8 = 0, 1
 STATUS = {0: "MISA_OK", -1: "MISA_ERR_INVALID_ARG", -2: "MISA_ERR_UNSUPPORTED",
           -3: "MISA_ERR_WORKSPACE", -4: "MISA_ERR_HIP"}
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "misa_score_topk": (i32, [P, i32, vp, i32, vp, vp, vp, sz, vp]),
             "misa_hier_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
             "hisa_topk": (i32, [P, i32, i32, vp, vp, vp, sz, vp]),
+            "misa_hisa_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
             "misa_status_str": (ctypes.c_char_p, [i32]),
             "misa_last_error": (ctypes.c_char_p, []),
             "misa_profile_enable": (i32, [i32]),
@@ -222,6 +224,19 @@ def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, kbar=None)
     idx, sc = out if out is not None else _outputs(p, k, q.device)
     ws, n = _workspace(p, OP_HISA_TOPK, q.device, ws, m=m, k=k)
     _check(lib().hisa_topk(ctypes.byref(p), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n, _stream()))
+    return idx, sc
+
+
+def misa_hisa_topk(q, w, K, pos, B, A, m, k, k_scale=None, heads=None, ws=None, out=None, kbar=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+    if heads is not None:
+        _dev(heads, "heads")
+        if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):
+            raise ValueError("heads must be int32 [T, A]")
+    idx, sc = out if out is not None else _outputs(p, k, q.device)
+    ws, n = _workspace(p, OP_MISA_HISA_TOPK, q.device, ws, A=A, m=m, k=k)
+    _check(lib().misa_hisa_topk(ctypes.byref(p), A, _ptr(heads), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n,
+                                _stream()))
     return idx, sc
 
 

@@ -147,8 +147,14 @@ static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, i
       plan_long(bp, pl, T, L);  // covers the k' stage and the final stage (k' <= L)
       break;
     }
-    case MISA_OP_HISA_TOPK: {
+    case MISA_OP_HISA_TOPK:
+    case MISA_OP_MISA_HISA_TOPK: {
       plan_route(bp, pl, p);
+      if (op == MISA_OP_MISA_HISA_TOPK) {  // the routed heads' packed rows
+        pl.heads = bp.take((size_t)T * A * 4);
+        pl.qr = bp.take((size_t)T * A * 128 * 2);
+        pl.wr = bp.take((size_t)T * A * 4);
+      }
       pl.Mmax = ceil_div(L, p->B);
       pl.mm = m < pl.Mmax ? m : pl.Mmax;
       pl.beta_ld = padded_ld(pl.Mmax);
@@ -236,9 +242,11 @@ static misa_status check_out(const void* ptr, const char* name) {
 
 // ---------------------------------------------------------------- pipelines
 
+// sums_ready: the block sums (ksum, or only the query tails with cached means)
+// and tsum are already in the workspace from an earlier router pass of this call.
 static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws,
                              int A, int32_t* heads, float* r, float* beta, int beta_ld,
-                             uint16_t* qr = nullptr, float* wr = nullptr) {
+                             uint16_t* qr = nullptr, float* wr = nullptr, bool sums_ready = false) {
   const bool fp8 = p->k_dtype == MISA_K_FP8_E4M3FN;
   double* ksum = at<double>(ws, pl.ksum);
   double* tsum = at<double>(ws, pl.tsum);
@@ -248,9 +256,10 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   const bool fast = !beta && route_fast_wins(p->L, p->B, p->T);
   uint16_t* kb16 = fast ? at<uint16_t>(ws, pl.kb16) : nullptr;
   // with cached block means only each query's last block is pooled here
-  HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
-                            p->kbar != nullptr, kb16),
-          "block sums");
+  if (!sums_ready)
+    HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
+                              p->kbar != nullptr, kb16),
+            "block sums");
   if (!fast) {
     HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, pmax,
                          heads, r, beta, beta_ld, qr, wr),
@@ -352,6 +361,54 @@ static misa_status run_routed_scores(const LaunchCtx& cx, const misa_problem* p,
   return MISA_OK;
 }
 
+// HISA Stage 1 and Stage 2 (HISA write-up, section 3) with the heads of p:
+// block scores of every visible block, the top-m blocks, the indexer on their
+// tokens, top-k. sums_ready: the block sums are already in the workspace.
+static misa_status run_hisa(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws, int k,
+                            int32_t* idx, float* scores, bool sums_ready) {
+  float* beta = at<float>(ws, pl.beta);
+  MISA_TRY(run_route(cx, p, pl, ws, 1, nullptr, nullptr, beta, (int)pl.beta_ld, nullptr, nullptr,
+                     sums_ready));
+  int32_t* blocks = at<int32_t>(ws, pl.blocks);
+  int32_t* nblocks = at<int32_t>(ws, pl.nblocks);
+  TopkArgs tb = topk_args(p);
+  tb.S = beta;
+  tb.S_ld = pl.beta_ld;
+  tb.n_div = p->B;
+  tb.k = pl.mm;
+  tb.out_idx = blocks;
+  tb.out_ld = pl.mm;
+  tb.out_count = nblocks;
+  MISA_TRY(run_topk(cx, tb, pl, ws, pl.Mmax));
+  int32_t* cand = at<int32_t>(ws, pl.cand);
+  int32_t* ncand = at<int32_t>(ws, pl.ncand);
+  const int ncmax = (long long)pl.mm * p->B < p->L ? pl.mm * p->B : p->L;  // candidate bound
+  // the refine pass forms the candidate list (indices and counts) from the blocks
+  ScoreArgs sa = score_args(p);
+  sa.blocks = blocks;
+  sa.blocks_ld = pl.mm;
+  sa.nblocks = nblocks;
+  sa.B = p->B;
+  sa.cand_out = cand;
+  sa.ncand_out = ncand;
+  sa.cand_ld = pl.cand_ld;
+  sa.cand_max = ncmax;
+  sa.S = at<float>(ws, pl.S2);
+  sa.S_ld = pl.S2_ld;
+  HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "refine scoring");
+  TopkArgs tf = topk_args(p);
+  tf.S = at<float>(ws, pl.S2);
+  tf.S_ld = pl.S2_ld;
+  tf.row_n = ncand;
+  tf.row_idx = cand;
+  tf.idx_ld = pl.cand_ld;
+  tf.k = k;
+  tf.out_idx = idx;
+  tf.out_score = scores;
+  tf.out_ld = k;
+  return run_topk(cx, tf, pl, ws, ncmax);
+}
+
 }  // namespace misa
 
 using namespace misa;
@@ -374,6 +431,9 @@ size_t misa_workspace_bytes(const misa_problem* p, int32_t op, int32_t A, int32_
       break;
     case MISA_OP_HISA_TOPK:
       if (m < 1 || k < 1) return 0;
+      break;
+    case MISA_OP_MISA_HISA_TOPK:
+      if (A < 1 || A > p->H || m < 1 || k < 1) return 0;
       break;
     case MISA_OP_BLOCK_MEANS:
       break;
@@ -510,48 +570,36 @@ misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx,
   const Plan pl = make_plan(p, MISA_OP_HISA_TOPK, 1, 1, k, m);
   MISA_TRY(check_ws(pl, ws, ws_bytes));
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
-  float* beta = at<float>(ws, pl.beta);
-  // Stage 1: block scores of every visible block, then the top-m blocks
-  MISA_TRY(run_route(cx, p, pl, ws, 1, nullptr, nullptr, beta, (int)pl.beta_ld));
-  int32_t* blocks = at<int32_t>(ws, pl.blocks);
-  int32_t* nblocks = at<int32_t>(ws, pl.nblocks);
-  TopkArgs tb = topk_args(p);
-  tb.S = beta;
-  tb.S_ld = pl.beta_ld;
-  tb.n_div = p->B;
-  tb.k = pl.mm;
-  tb.out_idx = blocks;
-  tb.out_ld = pl.mm;
-  tb.out_count = nblocks;
-  MISA_TRY(run_topk(cx, tb, pl, ws, pl.Mmax));
-  // Stage 2: the full indexer on the tokens of the chosen blocks, then top-k
-  int32_t* cand = at<int32_t>(ws, pl.cand);
-  int32_t* ncand = at<int32_t>(ws, pl.ncand);
-  const int ncmax = (long long)pl.mm * p->B < p->L ? pl.mm * p->B : p->L;  // candidate bound
-  // the refine pass forms the candidate list (indices and counts) from the blocks
-  ScoreArgs sa = score_args(p);
-  sa.blocks = blocks;
-  sa.blocks_ld = pl.mm;
-  sa.nblocks = nblocks;
-  sa.B = p->B;
-  sa.cand_out = cand;
-  sa.ncand_out = ncand;
-  sa.cand_ld = pl.cand_ld;
-  sa.cand_max = ncmax;
-  sa.S = at<float>(ws, pl.S2);
-  sa.S_ld = pl.S2_ld;
-  HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "refine scoring");
-  TopkArgs tf = topk_args(p);
-  tf.S = at<float>(ws, pl.S2);
-  tf.S_ld = pl.S2_ld;
-  tf.row_n = ncand;
-  tf.row_idx = cand;
-  tf.idx_ld = pl.cand_ld;
-  tf.k = k;
-  tf.out_idx = idx;
-  tf.out_score = scores;
-  tf.out_ld = k;
-  return run_topk(cx, tf, pl, ws, ncmax);
+  return run_hisa(cx, p, pl, ws, k, idx, scores, false);
+}
+
+misa_status misa_hisa_topk(const misa_problem* p, int32_t A, const int32_t* heads, int32_t m, int32_t k,
+                           int32_t* idx, float* scores, void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, true));
+  if (A < 1 || A > p->H) return fail(MISA_ERR_INVALID_ARG, "A = %d must lie in [1, H = %d]", A, p->H);
+  if (m < 1) return fail(MISA_ERR_INVALID_ARG, "m = %d must be >= 1", m);
+  if (k < 1) return fail(MISA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(idx, "idx"));
+  MISA_TRY(check_out(scores, "scores"));
+  if (heads && !aligned(heads, 4)) return fail(MISA_ERR_INVALID_ARG, "heads must be 4-byte aligned");
+  const Plan pl = make_plan(p, MISA_OP_MISA_HISA_TOPK, A, 1, k, m);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  if (!heads && A == p->H)  // every head is routed: HISA itself
+    return run_hisa(cx, p, pl, ws, k, idx, scores, false);
+  uint16_t* qr = at<uint16_t>(ws, pl.qr);
+  float* wr = at<float>(ws, pl.wr);
+  if (heads)
+    HIP_TRY(launch_gather_heads(cx, p->q, p->w, heads, p->T, p->H, A, qr, wr), "head gather");
+  else
+    MISA_TRY(run_route(cx, p, pl, ws, A, at<int32_t>(ws, pl.heads), nullptr, nullptr, 0, qr, wr));
+  // both HISA stages with the routed heads: their packed rows stand in for q and w
+  misa_problem pr = *p;
+  pr.q = qr;
+  pr.w = wr;
+  pr.H = A;
+  return run_hisa(cx, &pr, pl, ws, k, idx, scores, heads == nullptr);
 }
 
 const char* misa_status_str(int32_t status) {

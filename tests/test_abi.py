@@ -20,7 +20,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert {"misa_route", "misa_score_topk", "misa_hier_topk", "hisa_topk"} <= set(names)
+    assert {"misa_route", "misa_score_topk", "misa_hier_topk", "hisa_topk", "misa_hisa_topk"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in misa.h but not exported"
@@ -80,6 +80,13 @@ def test_parameter_validation():
     assert L.misa_hier_topk(ctypes.byref(p), 8, None, 15, 16, FAKE, FAKE, FAKE, 1 << 40, None) == -1
     assert L.hisa_topk(ctypes.byref(p), 0, 16, FAKE, FAKE, FAKE, 1 << 40, None) == -1
     assert L.hisa_topk(ctypes.byref(p), 4, 0, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+    mh = lambda A, m, k, heads=None: L.misa_hisa_topk(ctypes.byref(p), A, heads, m, k, FAKE, FAKE, FAKE,
+                                                       1 << 40, None)
+    assert mh(0, 4, 16) == -1
+    assert mh(65, 4, 16) == -1
+    assert mh(8, 0, 16) == -1
+    assert mh(8, 4, 0) == -1
+    assert mh(8, 4, 16, heads=FAKE + 2) == -1
     # workspace too small, missing or misaligned
     need = L.misa_workspace_bytes(ctypes.byref(p), S.OP_SCORE_TOPK, 8, 1, 16, 1)
     assert need >= 256
@@ -116,8 +123,10 @@ def test_workspace_sizes():
     assert ws(S.OP_HIER_TOPK, kp=100) == 0          # k' < k
     assert ws(S.OP_SCORE_TOPK, A=65) == 0
     assert ws(S.OP_HISA_TOPK, m=0) == 0
+    assert ws(S.OP_MISA_HISA_TOPK) > ws(S.OP_HISA_TOPK)  # + the routed heads' packed rows
+    assert ws(S.OP_MISA_HISA_TOPK, A=0) == 0 and ws(S.OP_MISA_HISA_TOPK, m=0) == 0
     assert ws(99) == 0
-    for op in range(5):
+    for op in range(6):
         assert ws(op) % 256 == 0
 
 
@@ -129,7 +138,7 @@ def test_workspace_sizes_for_edge_shapes(T, L, B, H):
     # the largest supported L and router shapes on both sides of every path switch
     Lb = S.lib()
     p = _problem(T=T, L=L, B=B, H=H)
-    for op in range(5):
+    for op in range(6):
         n = Lb.misa_workspace_bytes(ctypes.byref(p), op, min(8, H), min(8192, L), min(2048, L), 64)
         assert n > 0 and n % 256 == 0, (op, n)
 

@@ -13,7 +13,7 @@ import torch
 import oracle as O
 import synth
 from parity import RTOL, check_heads, check_row, oracle_problem, to_gpu, tolerance
-from test_gpu_parity import _check_misa, check_hier, check_hisa
+from test_gpu_parity import _check_misa, check_hier, check_hisa, check_misa_hisa
 
 pytestmark = pytest.mark.gpu
 
@@ -107,3 +107,6 @@ def test_c5_glm5_misa_and_hisa():
     _check_misa(inp, wl.B, wl.A, wl.k, _np(idx), _np(sc), label="c5 misa")
     idx, sc = S.hisa_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks)
     check_hisa(inp, wl.B, wl.m, wl.k, _np(idx), _np(sc), label="c5 hisa")
+    heads_o, _ = O.route(P, wl.A)
+    idx, sc = S.misa_hisa_topk(q, w, K, pos, wl.B, wl.A, wl.m, wl.k, ks)
+    check_misa_hisa(inp, wl.B, wl.A, wl.m, wl.k, _np(idx), _np(sc), heads_o, label="c5 misa-hisa")

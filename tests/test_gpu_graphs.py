@@ -99,3 +99,15 @@ def test_graph_cached_means_with_update():
 
     q2, w2, K2, ks2, pos2 = _inputs(58, T, L, H, O.KDT_FP8, positions="random")
     _replays_match(step, lambda: S.hier_topk(q2, w2, K2, pos2, B, A, kp, k, ks2))
+
+
+def test_graph_misa_hisa():
+    T, L, H, B, A, m, k = 16, 6000, 32, 128, 8, 8, 300
+    q, w, K, ks, pos = _inputs(59, T, L, H, O.KDT_FP8, positions="decode")
+    q2, w2, K2, ks2, pos2 = _inputs(60, T, L, H, O.KDT_FP8, positions="random")
+    p = S.make_problem(q, w, K, pos, B, ks)
+    ws = _ws(S.workspace_bytes(p, S.OP_MISA_HISA_TOPK, A=A, m=m, k=k))
+    out = (torch.empty((T, k), dtype=torch.int32, device="cuda"),
+           torch.empty((T, k), dtype=torch.float32, device="cuda"))
+    _replays_match(lambda: S.misa_hisa_topk(q, w, K, pos, B, A, m, k, ks, ws=ws, out=out),
+                   lambda: S.misa_hisa_topk(q2, w2, K2, pos2, B, A, m, k, ks2))

@@ -277,6 +277,77 @@ def test_hisa_topk(case):
     check_hisa(inp, B, m, k, _np(idx), _np(sc))
 
 
+# ----------------------------------------------------------------- MISA inside HISA
+
+MISA_HISA_CASES = [
+    # seed, T, L, H, A, B, m, k, kdt
+    (61, 7, 1000, 64, 8, 128, 3, 100, O.KDT_BF16),
+    (62, 12, 5000, 32, 8, 128, 16, 512, O.KDT_FP8),
+    (63, 5, 600, 64, 4, 64, 20, 40, O.KDT_BF16),       # m*B >= n: MISA
+    (64, 6, 300, 16, 3, 1, 50, 30, O.KDT_BF16),        # token blocks
+    (65, 4, 40000, 32, 8, 128, 64, 2048, O.KDT_FP8),   # long rows
+    (66, 9, 2000, 48, 48, 100, 5, 64, O.KDT_BF16),     # A = H: HISA
+    (67, 1100, 1100, 64, 8, 16, 8, 64, O.KDT_FP8),     # many queries: the two-pass router
+]
+
+
+def check_misa_hisa(inp, B, A, m, k, idx, sc, heads_used, label="misa-hisa"):
+    P = oracle_problem(inp, B)
+    rtol = RTOL[kdtype(inp)]
+    res, blocks, _ = O.misa_hisa_topk(P, A, m, k, heads=heads_used)
+    for t in range(P.T):
+        n = P.n(t)
+        hs = list(heads_used[t])
+        beta = O.routed_block_scores(P, t, hs)
+        rho = O.block_logits(P, t)[hs]
+        # the GPU forms beta_R in float64 and compares it in float32
+        btol = 1e-6 * (np.abs(P.w[t, hs])[:, None] * np.maximum(rho, 0)).sum(axis=0) + 1e-30
+        sure_b, maybe_b = pool_bands(beta, blocks[t], btol)
+        rng = O.block_ranges(n, B)
+        tok = lambda bs: set(s for b in bs for s in range(*rng[b]))
+        check_row(idx[t], sc[t], k, n, "ascending", res[t][0],
+                  lambda s, t=t, hs=hs: O.routed_scores(P, t, hs, s),
+                  lambda s, t=t, hs=hs: tolerance(P, t, hs, s, rtol),
+                  sure_pool=tok(sure_b), maybe_pool=tok(maybe_b), label=f"{label} row {t}")
+
+
+@pytest.mark.parametrize("case", MISA_HISA_CASES,
+                         ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}A{c[4]}B{c[5]}m{c[6]}k{c[7]}kd{c[8]}")
+def test_misa_hisa_topk(case):
+    seed, T, L, H, A, B, m, k, kdt = case
+    inp = _case(seed, T, L, H, kdt, positions="random" if L < 10000 else "decode")
+    q, w, K, ks, pos = to_gpu(inp)
+    heads = S.route(q, w, K, pos, B, A, ks)
+    idx, sc = S.misa_hisa_topk(q, w, K, pos, B, A, m, k, ks)
+    torch.cuda.synchronize()
+    P = oracle_problem(inp, B)
+    heads_o, ill = check_heads(P, A, _np(heads))
+    assert ill == 0
+    check_misa_hisa(inp, B, A, m, k, _np(idx), _np(sc), heads_o)
+
+
+def test_misa_hisa_explicit_heads_and_cached_means():
+    T, L, H, A, B, m, k = 10, 3000, 64, 6, 64, 7, 200
+    inp = _case(68, T, L, H, O.KDT_FP8)
+    rng = np.random.default_rng(1)
+    hs = np.stack([rng.choice(H, A, replace=False) for _ in range(T)]).astype(np.int32)  # any order
+    q, w, K, ks, pos = to_gpu(inp)
+    kbar = S.block_means(K, B, ks)
+    for kb in (None, kbar):
+        idx, sc = S.misa_hisa_topk(q, w, K, pos, B, A, m, k, ks, heads=torch.from_numpy(hs).cuda(), kbar=kb)
+        inp_k = inp if kb is None else dict(inp, kbar=_np(kb))
+        check_misa_hisa(inp_k, B, A, m, k, _np(idx), _np(sc), hs, label="explicit heads")
+
+
+def test_misa_hisa_all_heads_is_hisa_bitwise():
+    T, L, H, B, m, k = 8, 2500, 32, 128, 6, 300
+    inp = _case(69, T, L, H, O.KDT_BF16)
+    q, w, K, ks, pos = to_gpu(inp)
+    a = S.misa_hisa_topk(q, w, K, pos, B, H, m, k, ks)
+    b = S.hisa_topk(q, w, K, pos, B, m, k, ks)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 # ----------------------------------------------------------------- properties
 
 def test_dense_equals_misa_with_all_heads():
@@ -375,3 +446,5 @@ def test_cached_block_means(case, source):
     check_hier(inp, B, A, 256, 64, _np(idx), _np(sc), label="cached hier")
     idx, sc = S.hisa_topk(q, w, K, pos, B, 4, 64, ks, kbar=kbar)
     check_hisa(inp, B, 4, 64, _np(idx), _np(sc), label="cached hisa")
+    idx, sc = S.misa_hisa_topk(q, w, K, pos, B, A, 4, 64, ks, kbar=kbar)
+    check_misa_hisa(inp, B, A, 4, 64, _np(idx), _np(sc), heads_o, label="cached misa-hisa")
