@@ -93,7 +93,8 @@ class Step:
         self.A = wl.A if A is None else A
         q, w, K, ks, pos = tensors
         p = S.make_problem(q, w, K, pos, wl.B, ks)
-        op = {"hier": S.OP_HIER_TOPK, "misa": S.OP_SCORE_TOPK, "hisa": S.OP_HISA_TOPK}[path]
+        op = {"hier": S.OP_HIER_TOPK, "misa": S.OP_SCORE_TOPK, "hisa": S.OP_HISA_TOPK,
+              "misa_hisa": S.OP_MISA_HISA_TOPK}[path]
         nbytes = S.workspace_bytes(p, op, A=self.A, kprime=wl.kprime, k=wl.k, m=wl.m)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.out = (torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda"),
@@ -111,6 +112,9 @@ class Step:
                                kbar=kbar)
         if self.path == "misa":
             return S.score_topk(q, w, K, pos, wl.B, self.A, wl.k, ks, ws=self.ws, out=self.out, kbar=kbar)
+        if self.path == "misa_hisa":
+            return S.misa_hisa_topk(q, w, K, pos, wl.B, self.A, wl.m, wl.k, ks, ws=self.ws, out=self.out,
+                                    kbar=kbar)
         return S.hisa_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out, kbar=kbar)
 
 
@@ -352,6 +356,7 @@ def main():
                                            ("misa_c5", "misa", "c5_glm5_hisa_128k", None, False),
                                            ("hisa_c5", "hisa", "c5_glm5_hisa_128k", None, False),
                                            ("hisa_c5_cached_block_means", "hisa", "c5_glm5_hisa_128k", None, True),
+                                           ("misa_hisa_c5", "misa_hisa", "c5_glm5_hisa_128k", None, False),
                                            ("misa_c2", "misa", "c2_decode_batch", None, False),
                                            ("misa_c3_prefill", "misa", "c3_causal_prefill", None, False)]:
             if nm == name:
