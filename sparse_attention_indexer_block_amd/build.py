@@ -25,9 +25,14 @@ CFLAGS = [
 ]
 
 
+# per-source flags: the scoring kernels keep MFMA accumulators in VGPRs, so the
+# fused epilogue reads them without a copy out of the accumulation registers
+EXTRA = {"score_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

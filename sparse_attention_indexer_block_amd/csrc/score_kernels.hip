@@ -20,6 +20,11 @@ namespace misa {
 
 constexpr int kLdsStride = kHeadDim + 8;  // bf16 per key row in LDS (16 B pad)
 
+// ReLU of an MFMA result as one integer max on its bits: negative values (and
+// -0.0) have the sign bit set and become +0.0. fmaxf would add a quieting step
+// for signalling NaNs, which MFMA results on finite inputs never are.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Row layout of the A operand. With AP <= 16 head slots and RPW a multiple of
 // G = AP / 4, G row tiles form a "quad" of four queries: row r of tile k in the
 // quad is query r / 4, head slot 4 k + r % 4, so the four MFMA result rows a
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
 #pragma unroll
           for (int k = 0; k < RM::G; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part += wv[s * RM::G + k][i] * fmaxf(acc[s * RM::G + k][i], 0.f);
+            for (int i = 0; i < 4; ++i) part += wv[s * RM::G + k][i] * relu(acc[s * RM::G + k][i]);
           const float v = RM::finish(part) * kscale;
           q_row[s][col] = v;
           if constexpr (RMM) {
@@ -567,7 +572,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
 #pragma unroll
         for (int k = 0; k < RM::G; ++k)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part += wv[s * RM::G + k][i] * fmaxf(acc[s * RM::G + k][i], 0.f);
+          for (int i = 0; i < 4; ++i) part += wv[s * RM::G + k][i] * relu(acc[s * RM::G + k][i]);
         const float v = RM::finish(part) * kscale;
         q_row[s][col] = v;
         const bool vis = col < q_n[s];  // (a gathered column past the candidates has key -1)
