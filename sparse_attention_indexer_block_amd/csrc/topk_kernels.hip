@@ -842,8 +842,8 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
 // the sub-range that holds the rem-th largest item.
 
 
-template <int NT, int G>
-__device__ __forceinline__ void reg_threshold(const uint32_t (&u)[G][4], const bool (&in)[G][4], int k,
+template <int NT, int G, typename In>
+__device__ __forceinline__ void reg_threshold(const uint32_t (&u)[G][4], In in, int k,
                                               uint32_t umin, uint32_t umax, RegShared<NT>& sm,
                                               uint32_t& tau, int& need_eq) {
   constexpr int NW = NT / kWave;
@@ -866,7 +866,7 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&u)[G][4], const b
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t v = u[g][e] - umin - base;
-          const bool inr = in[g][e] && (bits >= 32 || (v >> bits) == 0u);
+          const bool inr = in(g, e) && (bits >= 32 || (v >> bits) == 0u);
           x += inr ? (1ull << (4 * (v >> sh))) : 0ull;
         }
 #pragma unroll
@@ -915,8 +915,8 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&u)[G][4], const b
 // Emit the selection in item order: items with key > tau, plus the first
 // need_eq items equal to tau (all items when take_all). Writes positions below
 // k only.
-template <int NT, int G, bool WITH_SCORE, typename IdxOf>
-__device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], const bool (&in)[G][4], int seg0,
+template <int NT, int G, bool WITH_SCORE, typename In, typename IdxOf>
+__device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], In in, int seg0,
                                          bool take_all, uint32_t tau, int need_eq, int k,
                                          RegShared<NT>& sm, IdxOf idx_of, int32_t* out_idx,
                                          float* out_score) {
@@ -929,8 +929,8 @@ __device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], const bool (
     int c = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool gt = in[g][e] && (take_all || u[g][e] > tau);
-      const bool eq = in[g][e] && !take_all && u[g][e] == tau;
+      const bool gt = in(g, e) && (take_all || u[g][e] > tau);
+      const bool eq = in(g, e) && !take_all && u[g][e] == tau;
       c += (gt ? 1 : 0) + (eq ? (1 << 16) : 0);
     }
     cnt[g] = c;
@@ -954,7 +954,7 @@ __device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], const bool (
     int gt_b = gt_run + (exc & 0xffff), eq_b = eq_run + (exc >> 16);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (!in[g][e]) continue;
+      if (!in(g, e)) continue;
       const int s = seg0 + 4 * (lane + kWave * g) + e;
       int p = -1;
       if (take_all || u[g][e] > tau) {
@@ -975,8 +975,16 @@ __device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], const bool (
   }
 }
 
-template <int NT, int G>
-__global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
+// IDX: the row has explicit key indices (row_idx); without them the emitted
+// index is the position, computed where it is written rather than held in
+// registers. The in-range test is likewise recomputed and the threshold bin's
+// ballots are taken again instead of kept. Rows of 16,384 items are built for
+// eight waves per SIMD (64 registers per lane, a few spilled), so two rows
+// share a compute unit: the selection's barrier-separated phases are latency,
+// and a second row fills them (16384 rows of 16384: 0.56 ms against 0.65 ms
+// with one row per unit).
+template <int NT, int G, bool IDX>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 && G == 4 ? 8 : 1))) void k_topk_rows(TopkArgs a) {
   __shared__ TopkShared<NT> sm;
   __shared__ uint32_t cand[kListCap];  // keys of the threshold bin
   constexpr int NW = NT / kWave;
@@ -984,22 +992,23 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
   const int n = min(row_length(a, row), NT * 4 * G);
   const int seg0 = w * 256 * G;
   const float* src = a.S + (size_t)row * a.S_ld;
-  const int32_t* ri = a.row_idx ? a.row_idx + (size_t)row * a.idx_ld : nullptr;
   uint32_t u[G][4];
-  bool in[G][4];
-  i32x4 ix[G];
-  load_groups4<G>(src, seg0, n, lane, kWave, u, in);
-  if (ri && n > seg0) {
-    // index rows share the score rows' padded stride: same clamped 16-byte loads
-    const int last = (n - 1) & ~3;
+  {
+    bool unused[G][4];
+    load_groups4<G>(src, seg0, n, lane, kWave, u, unused);
+  }
+  const int nrel = n - seg0;  // items of this wave's segment that exist (may be <= 0)
+  auto in = [=](int g, int e) { return 4 * (lane + kWave * g) + e < nrel; };
+  i32x4 ix[IDX ? G : 1];
+  if constexpr (IDX) {
+    const int32_t* ri = a.row_idx + (size_t)row * a.idx_ld;
+    if (n > seg0) {
+      // index rows share the score rows' padded stride: same clamped 16-byte loads
+      const int last = (n - 1) & ~3;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      ix[g] = *reinterpret_cast<const i32x4*>(ri + min(seg0 + 4 * (lane + kWave * g), last));
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ix[g][e] = seg0 + 4 * (lane + kWave * g) + e;
+      for (int g = 0; g < G; ++g)
+        ix[g] = *reinterpret_cast<const i32x4*>(ri + min(seg0 + 4 * (lane + kWave * g), last));
+    }
   }
   int32_t* oi = a.out_idx + (size_t)row * a.out_ld;
   float* os = a.out_score ? a.out_score + (size_t)row * a.out_ld : nullptr;
@@ -1013,7 +1022,7 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (in[g][e]) {
+        if (in(g, e)) {
           lo = min(lo, u[g][e]);
           hi = max(hi, u[g][e]);
         }
@@ -1025,7 +1034,7 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (in[g][e]) atomicAdd(&sm.hist[lin_bin(u[g][e], xlo, scale, kFineBins)], 1u);
+        if (in(g, e)) atomicAdd(&sm.hist[lin_bin(u[g][e], xlo, scale, kFineBins)], 1u);
     __syncthreads();
     find_bin<NT>(sm.hist, kFineBins, k, sm);
     const uint32_t bstar = (uint32_t)sm.digit;
@@ -1035,17 +1044,16 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
       // the threshold bin's keys (in item order): straight into sm.list when
       // few enough to rank pairwise, else into cand for radix digits
       uint32_t* dst = c <= kRankCap ? sm.list : cand;
-      uint64_t km[G][4];
+      auto keep = [&](int g, int e) { return in(g, e) && lin_bin(u[g][e], xlo, scale, kFineBins) == bstar; };
       int nw = 0;
       uint32_t clo = 0xffffffffu, chi = 0u;
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool keep = in[g][e] && lin_bin(u[g][e], xlo, scale, kFineBins) == bstar;
-          km[g][e] = wave_ballot(keep);
-          nw += __popcll(km[g][e]);
-          if (keep) {
+          const bool kp = keep(g, e);
+          nw += __popcll(wave_ballot(kp));
+          if (kp) {
             clo = min(clo, u[g][e]);
             chi = max(chi, u[g][e]);
           }
@@ -1058,8 +1066,10 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if ((km[g][e] >> lane) & 1ull) dst[at + lanes_below(km[g][e])] = u[g][e];
-          at += __popcll(km[g][e]);
+          const bool kp = keep(g, e);
+          const uint64_t m = wave_ballot(kp);
+          if (kp) dst[at + lanes_below(m)] = u[g][e];
+          at += __popcll(m);
         }
       if (rem >= c || c > kRankCap) {
         block_minmax<NT>(clo, chi, sm);  // synchronises (the list is complete)
@@ -1080,7 +1090,10 @@ __global__ __launch_bounds__(NT) void k_topk_rows(TopkArgs a) {
       reg_threshold<NT, G>(u, in, k, sm.umin, sm.umax, sm.reg, tau, need_eq);
     }
   }
-  auto idx_of = [&](int g, int e, int) { return ix[g][e]; };
+  auto idx_of = [&](int g, int e, int s) {
+    if constexpr (IDX) return ix[g][e];
+    else return s;
+  };
   if (os) reg_emit<NT, G, true>(u, in, seg0, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
   else reg_emit<NT, G, false>(u, in, seg0, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
   const int nsel = take_all ? n : k;
@@ -1139,10 +1152,14 @@ hipError_t launch_topk_rows(const LaunchCtx& cx, const TopkArgs& a, int max_n) {
   if (a.rows == 0) return hipSuccess;
   if (max_n > kLdsCap) return hipErrorInvalidValue;
   const dim3 grid(a.rows);
-  if (max_n <= 1024) return cx.launch("topk_rows", k_topk_rows<256, 1>, grid, dim3(256), 0, a);
-  if (max_n <= 4096) return cx.launch("topk_rows", k_topk_rows<1024, 1>, grid, dim3(1024), 0, a);
-  if (max_n <= 8192) return cx.launch("topk_rows", k_topk_rows<1024, 2>, grid, dim3(1024), 0, a);
-  return cx.launch("topk_rows", k_topk_rows<1024, 4>, grid, dim3(1024), 0, a);
+#define MISA_ROWS(NT, G)                                                                           \
+  (a.row_idx ? cx.launch("topk_rows", k_topk_rows<NT, G, true>, grid, dim3(NT), 0, a)             \
+             : cx.launch("topk_rows", k_topk_rows<NT, G, false>, grid, dim3(NT), 0, a))
+  if (max_n <= 1024) return MISA_ROWS(256, 1);
+  if (max_n <= 4096) return MISA_ROWS(1024, 1);
+  if (max_n <= 8192) return MISA_ROWS(1024, 2);
+  return MISA_ROWS(1024, 4);
+#undef MISA_ROWS
 }
 
 hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLongWs& ws, int max_n) {
