@@ -48,20 +48,12 @@ __device__ __forceinline__ void merge_part(float& b, float& s, float& e, int& a,
   e = fmaxf(e, e2);
 }
 
-template <int CTRL>
-__device__ __forceinline__ void dpp_merge(float& b, float& s, float& e, int& a) {
-  const float b2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), CTRL, 0xf, 0xf, false));
-  const float s2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), CTRL, 0xf, 0xf, false));
-  const float e2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e), CTRL, 0xf, 0xf, false));
-  const int a2 = __builtin_amdgcn_update_dpp(0, a, CTRL, 0xf, 0xf, false);
-  merge_part(b, s, e, a, b2, s2, e2, a2);
-}
-
 // grid (ntr, ceil(T / QG)), 256 threads: workgroup tr covers block tiles
 // [tr * TPW, tr * TPW + TPW) of QG queries; wave w takes heads [16w, 16w+16).
-// v_mfma_f32_16x16x32_bf16 with rows = heads, columns = blocks; lane l feeds
-// head / block l % 16 with dims [32(l/16), 32(l/16) + 32) over the four K
-// steps, and holds rows 4(l/16) + i of column l % 16 of the result.
+// v_mfma_f32_16x16x32_bf16 with rows = blocks, columns = heads; lane l feeds
+// block / head l % 16 with dims [32(l/16), 32(l/16) + 32) over the four K
+// steps, and holds rows (blocks) 4(l/16) + e of column (head) l % 16 of the
+// result, so that a head's maximum over a tile stays within its column.
 // kb16 [M][2][128] holds the hi / lo split of every block mean; without it
 // (cached means) the split is formed here from kbar.
 // Settling and selection outputs of the single-pass form (see below).
@@ -121,10 +113,11 @@ __device__ __forceinline__ double sum_groups(double v) {
 // and the query's last block), then ranks the heads and writes heads, r and
 // the packed q rows and weights of the chosen heads, as k_route_exact does.
 template <int QG, int TPW, bool FUSED>
-__global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int32_t* pos, int T, int H,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_route_fast(const uint16_t* q, const int32_t* pos, int T, int H,
                                                     int L, int B, int ntr, const uint16_t* kb16,
                                                     const float* kbar, RoutePart* part, RouteSettle st) {
-  const int tr = blockIdx.x, tq0 = blockIdx.y * QG;
+  // the last query groups (most visible blocks under a causal mask) start first
+  const int tr = blockIdx.x, tq0 = (gridDim.y - 1 - blockIdx.y) * QG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
@@ -186,34 +179,22 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
       *reinterpret_cast<u32x4*>(&sml[r * RS + 8 * v]) = ok ? lv[u] : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  // (single-pass form) the queries' last-block sums, for the settling below
-  static_assert(!FUSED || QG <= 2, "two staged last-block rows per workgroup");
-  __shared__ double tsh[FUSED ? QG : 1][kHeadDim];
-  if constexpr (FUSED) {
-    const int i = tid >> 7, d = tid & 127;  // 256 threads: two rows of 128
-    if (i < QG) {
-      const int t = min(tq0 + i, T - 1);
-      tsh[i][d] = st.tsum[(size_t)t * kHeadDim + d];
-    }
-  }
   __syncthreads();
-  float best[QG][4], second[QG][4], err[QG][4];
-  int arg[QG][4];
+  // running record of head 16 wv + col over the blocks of this lane's rows
+  float best[QG], second[QG], err[QG];
+  int arg[QG];
 #pragma unroll
-  for (int i = 0; i < QG; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      best[i][e] = -__builtin_huge_valf();
-      second[i][e] = -__builtin_huge_valf();
-      err[i][e] = 0.f;
-      arg[i][e] = -1;
-    }
+  for (int i = 0; i < QG; ++i) {
+    best[i] = -__builtin_huge_valf();
+    second[i] = -__builtin_huge_valf();
+    err[i] = 0.f;  // largest |q|.|hi| product, scaled to the bound after the loop
+    arg[i] = -1;
+  }
 
   for (int tt = 0; tt < TPW; ++tt) {
     const int b0 = (tr * TPW + tt) * kFastTile;
     if (b0 >= M) break;  // uniform
-    const int blk = b0 + col;
-    // B operands of this lane's block: hi, lo and |hi|, dims 32g .. 32g+31
+    // A operands of this lane's block row b0 + col: hi, lo and |hi|, dims 32g .. 32g+31
     bf16x8 bh[4], bl[4], ba[4];
     const int rl = (tt * kFastTile + col) * RS + 32 * g;
 #pragma unroll
@@ -229,49 +210,50 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
       f32x4 ah = {0.f, 0.f, 0.f, 0.f}, al = ah, aa = ah;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i][s], bh[s], ah, 0, 0, 0);
-        al = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i][s], bl[s], al, 0, 0, 0);
+        ah = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[s], qa[i][s], ah, 0, 0, 0);
+        al = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[s], qa[i][s], al, 0, 0, 0);
         const u32x4 qabs = __builtin_bit_cast(u32x4, qa[i][s]) & u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-        aa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qabs), ba[s], aa, 0, 0, 0);
+        aa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ba[s], __builtin_bit_cast(bf16x8, qabs), aa, 0, 0, 0);
       }
-      if (blk < nfull[i]) {
-        // this lane's own block: running largest, second largest and bound
+      // element e: block b0 + 4g + e of head 16 wv + col
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 4; ++e) {
+        const int blk = b0 + 4 * g + e;
+        if (blk < nfull[i]) {
           const float v = ah[e] + al[e];
-          second[i][e] = fmaxf(second[i][e], fminf(best[i][e], v));
-          if (v > best[i][e]) arg[i][e] = blk;
-          best[i][e] = fmaxf(best[i][e], v);
-          err[i][e] = fmaxf(err[i][e], ldexpf(aa[e], -14) + 1e-30f);
+          second[i] = fmaxf(second[i], fminf(best[i], v));
+          if (v > best[i]) arg[i] = blk;
+          best[i] = fmaxf(best[i], v);
+          err[i] = fmaxf(err[i], aa[e]);
         }
       }
     }
   }
-  // the 16 lanes of a row group hold different blocks of the same heads
+  // the four row groups hold different blocks of the same head: merge across them,
+  // after which every lane of column col holds its head's record
 #pragma unroll
-  for (int i = 0; i < QG; ++i)
+  for (int i = 0; i < QG; ++i) {
+    err[i] = arg[i] >= 0 ? ldexpf(err[i], -14) + 1e-30f : 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dpp_merge<0x121>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:1
-      dpp_merge<0x122>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:2
-      dpp_merge<0x124>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:4
-      dpp_merge<0x128>(best[i][e], second[i][e], err[i][e], arg[i][e]);  // row_ror:8
+    for (int off = 16; off < kWave; off <<= 1) {
+      const float b2 = __shfl_xor(best[i], off, kWave), s2 = __shfl_xor(second[i], off, kWave);
+      const float e2 = __shfl_xor(err[i], off, kWave);
+      const int a2 = __shfl_xor(arg[i], off, kWave);
+      merge_part(best[i], second[i], err[i], arg[i], b2, s2, e2, a2);
     }
+  }
   if constexpr (!FUSED) {
-    if (col == 0) {
+    if (g == 0) {
 #pragma unroll
       for (int i = 0; i < QG; ++i) {
         const int t = tq0 + i;
         if (t >= T) break;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          RoutePart r;
-          r.best = best[i][e];
-          r.second = second[i][e];
-          r.err = err[i][e];
-          r.arg = arg[i][e];
-          part[((size_t)t * ntr + tr) * kWave + kFastTile * wv + 4 * g + e] = r;
-        }
+        RoutePart r;
+        r.best = best[i];
+        r.second = second[i];
+        r.err = err[i];
+        r.arg = arg[i];
+        part[((size_t)t * ntr + tr) * kWave + h_a] = r;
       }
     }
     return;
@@ -287,24 +269,12 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
     double mq[QG];  // max over the candidates of ReLU(rho)
 #pragma unroll
     for (int i = 0; i < QG; ++i) {
-      // the row group of head 16 wv + 4 g + e holds its merged record; code it as
-      // -1 (no block can be positive), the leader block, or the leader + 2^30 when
-      // the second best reaches the leader's bound (every block evaluated)
-      int code[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float thr = best[i][e] - 2.f * err[i][e];
-        const bool use = arg[i][e] >= 0 && best[i][e] + err[i][e] >= 0.f;
-        code[e] = use ? (arg[i][e] | (second[i][e] >= thr ? (1 << 30) : 0)) : -1;
-      }
-      // this lane's A-operand head h_a = 16 wv + col sits in row group col / 4, element col % 4
-      const int srcl = 16 * (col >> 2) + col;
-      int c = -1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = __shfl(code[e], srcl, kWave);
-        c = (col & 3) == e ? v : c;
-      }
+      // this lane's head record, coded as -1 (no block can be positive), the leader
+      // block, or the leader + 2^30 when the second best reaches the leader's bound
+      // (every block evaluated)
+      const float thr = best[i] - 2.f * err[i];
+      const bool use = arg[i] >= 0 && best[i] + err[i] >= 0.f;
+      const int c = use ? (arg[i] | (second[i] >= thr ? (1 << 30) : 0)) : -1;
       cq[i] = c;
       const int b = c >= 0 ? (c & ((1 << 30) - 1)) : 0;  // (block 0 when there is none: unused)
       const double rho = sum_groups(exact_part32(qa[i], st.ksum + (size_t)b * kHeadDim,
@@ -356,19 +326,9 @@ __global__ __launch_bounds__(256) void k_route_fast(const uint16_t* q, const int
       const int n = visible_len(pos[tc], L);
       const int Mt = (int)(((long long)n + B - 1) / B);
       if (Mt > 0) {
-        // the query's own last block, always exactly (its sum staged in LDS)
-        double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const u32x4 qw = __builtin_bit_cast(u32x4, qa[i][s2]);
-#pragma unroll
-          for (int p2 = 0; p2 < 4; ++p2) {
-            const int d = 32 * g + 8 * s2 + 2 * p2;
-            a0 = fma((double)bf16_bits_to_f32(qw[p2] & 0xffffu), tsh[i][d], a0);
-            a1 = fma((double)bf16_bits_to_f32(qw[p2] >> 16), tsh[i][d + 1], a1);
-          }
-        }
-        const double rho = sum_groups(a0 + a1) / (double)(n - (Mt - 1) * B);
+        // the query's own last block, always exactly, from its float64 sum
+        const double tq = exact_part32(qa[i], st.tsum + (size_t)tc * kHeadDim, nullptr, g);
+        const double rho = sum_groups(tq) / (double)(n - (Mt - 1) * B);
         m = rho > m ? rho : m;
       }
       const bool active = t < T && h_a < H;
@@ -653,9 +613,9 @@ hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const floa
   const uint16_t* kb = kbar ? nullptr : kb16;
   const RouteSettle st{w, ksum, tsum, A, heads, r_out, qr, wr};
   const dim3 grid(ntr, (T + 1) / 2);  // two queries and eight block tiles per workgroup
-  if (ntr == 1)  // every block in one range: settle and select in the same launch
-    return cx.launch("route_fast", k_route_fast<2, 8, true>, grid, dim3(256), 0, q, pos, T, H, L, B, ntr, kb,
-                     kbar, pp, st);
+  if (ntr == 1)  // every block in one range: four queries, settled and selected in the same launch
+    return cx.launch("route_fast", k_route_fast<4, 8, true>, dim3(1, (T + 3) / 4), dim3(256), 0, q, pos, T,
+                     H, L, B, ntr, kb, kbar, pp, st);
   hipError_t e = cx.launch("route_fast", k_route_fast<2, 8, false>, grid, dim3(256), 0, q, pos, T, H, L, B,
                            ntr, kb, kbar, pp, st);
   if (e != hipSuccess) return e;
