@@ -107,11 +107,16 @@ __device__ __forceinline__ double sum_groups(double v) {
 }
 
 // FUSED (every complete block of each query inside this workgroup's range,
-// ntr == 1): instead of writing partial records, the workgroup settles each
-// head's maximum in float64 (the candidate block of every head, all blocks
-// for the rare head whose second-best bf16 score reaches the leader's bound,
-// and the query's last block), then ranks the heads and writes heads, r and
-// the packed q rows and weights of the chosen heads, as k_route_exact does.
+// ntr == 1): instead of writing partial records, the workgroup places each
+// head by a certified interval of r (the bf16 leader and its bound, and a
+// float evaluation of the query's last block with its own bound): a head is in
+// when fewer than A heads may beat it, out when at least A heads must, and
+// only the heads left between are settled in float64 (the candidate block,
+// all blocks for the rare head whose second-best bf16 score reaches the
+// leader's bound, and the last block) and ranked among themselves, so the
+// chosen set is the one the float64 router picks. It writes heads, r (every
+// head exactly when asked for) and the packed q rows and weights of the
+// chosen heads, as k_route_exact does.
 template <int QG, int TPW, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_route_fast(const uint16_t* q, const int32_t* pos, int T, int H,
                                                     int L, int B, int ntr, const uint16_t* kb16,
@@ -124,6 +129,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int M = (int)(((long long)L + B - 1) / B);
   const int h_a = kFastTile * wv + col;
   int nfull[QG];  // complete blocks before each query's last block
+  int nvis[QG];   // visible keys of each query
+  float wq[QG];   // (single-pass form) head weight of this lane's head
   bf16x8 qa[QG][4];
 #pragma unroll
   for (int i = 0; i < QG; ++i) {
@@ -131,7 +138,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int n = t < T ? visible_len(pos[t], L) : 0;
     const int Mt = (int)(((long long)n + B - 1) / B);
     nfull[i] = Mt > 0 ? Mt - 1 : 0;
+    nvis[i] = n;
     const bool ok = t < T && h_a < H;
+    wq[i] = FUSED && ok ? st.w[(size_t)t * H + h_a] : 0.f;
     const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)(ok ? t : 0) * H + (ok ? h_a : 0)) * kHeadDim + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) qa[i][s] = __builtin_bit_cast(bf16x8, ok ? src[s] : u32x4{0u, 0u, 0u, 0u});
@@ -140,8 +149,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // the four waves (rows padded by 16 bytes: conflict-free 16-byte reads)
   constexpr int NB = TPW * kFastTile;
   constexpr int RS = kHeadDim + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t smh[NB * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t sml[NB * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t smb[2 * NB * RS];
+  uint16_t* const smh = smb;
+  uint16_t* const sml = smb + NB * RS;
   {
     const int bstart = tr * NB;
     constexpr int NC = NB * 16 / 256;  // 16-byte chunks (8 dims) per thread
@@ -177,6 +187,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const bool ok = bstart + r < M;
       *reinterpret_cast<u32x4*>(&smh[r * RS + 8 * v]) = ok ? hv[u] : u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&sml[r * RS + 8 * v]) = ok ? lv[u] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // (single-pass form) each query's last-block sum, rounded to float, for the
+  // certified interval of its tail term
+  __shared__ float tsh[FUSED ? QG : 1][kHeadDim];
+  if constexpr (FUSED) {
+    for (int x = tid; x < QG * kHeadDim; x += 256) {
+      const int i = x / kHeadDim, d = x % kHeadDim;
+      tsh[i][d] = (float)st.tsum[(size_t)min(tq0 + i, T - 1) * kHeadDim + d];
     }
   }
   __syncthreads();
@@ -258,36 +277,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     return;
   } else {
-    __shared__ double rsh[QG][kWave];
-    __shared__ __attribute__((aligned(16))) uint16_t qrow[4][kHeadDim];  // per wave: one q row
-    __shared__ int rank_part[QG][4][kWave];
-    __shared__ int slot_of[QG][kWave];
-    const double divb = kbar ? 1.0 : (double)B;
-    // candidate of each head and its exact value, for every query of the group at
-    // once (no branch between the queries' requests)
-    int cq[QG];
-    double mq[QG];  // max over the candidates of ReLU(rho)
-#pragma unroll
-    for (int i = 0; i < QG; ++i) {
-      // this lane's head record, coded as -1 (no block can be positive), the leader
-      // block, or the leader + 2^30 when the second best reaches the leader's bound
-      // (every block evaluated)
-      const float thr = best[i] - 2.f * err[i];
-      const bool use = arg[i] >= 0 && best[i] + err[i] >= 0.f;
-      const int c = use ? (arg[i] | (second[i] >= thr ? (1 << 30) : 0)) : -1;
-      cq[i] = c;
-      const int b = c >= 0 ? (c & ((1 << 30) - 1)) : 0;  // (block 0 when there is none: unused)
-      const double rho = sum_groups(exact_part32(qa[i], st.ksum + (size_t)b * kHeadDim,
-                                                 kbar ? kbar + (size_t)b * kHeadDim : nullptr, g)) / divb;
-      mq[i] = c >= 0 && rho > 0.0 ? rho : 0.0;
-    }
+    // The staged means are dead after the tile loop: the settling reuses their LDS.
+    struct Lds {
+      double rlo[QG][kWave], rhi[QG][kWave];  // certified bounds of r(t, h)
+      double rex[QG][kWave];                  // exact r of the heads evaluated
+      int count[QG][4][kWave];                // partial counts of heads that may / must beat h
+      int state[QG][kWave];                   // 0 out, 1 in, 2 evaluated exactly
+      int slot_of[QG][kWave];
+      uint16_t qrow[4][kHeadDim];             // per wave: one q row
+    };
+    static_assert(sizeof(Lds) <= sizeof(smb), "settling scratch fits the staging buffer");
+    Lds& sh = *reinterpret_cast<Lds*>(smb);
+    __syncthreads();  // every wave is past its last read of the staged means
+
+    // Certified interval of r(t, h) = w * max(0, max_b rho) for this lane's head:
+    // max_b rho over the complete blocks lies within err of the largest rho~
+    // (the maximum is 1-Lipschitz in each term), and the last block's rho within
+    // 2^-14 sum |q| |t| / n_tail of its float evaluation (float rounding of the
+    // sum and of 34 accumulation steps stay below 2^-18.8 of that sum).
 #pragma unroll
     for (int i = 0; i < QG; ++i) {
       const int t = tq0 + i;
-      const int tc = t < T ? t : T - 1;  // (rows past T compute on a valid query, never written)
-      const int c = cq[i];
-      double m = mq[i];
-      uint64_t ambm = wave_ballot(g == 0 && c >= 0 && (c >> 30) != 0);
+      const bool active = t < T && h_a < H;
+      const int n = nvis[i];
+      const int Mt = (int)(((long long)n + B - 1) / B);
+      double lo = -__builtin_huge_val(), hi = -__builtin_huge_val();
+      if (arg[i] >= 0) {
+        lo = (double)best[i] - (double)err[i];
+        hi = (double)best[i] + (double)err[i];
+      }
+      if (Mt > 0) {
+        float a = 0.f, ab = 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const u32x4 qw = __builtin_bit_cast(u32x4, qa[i][s2]);
+          const f32x4* tp = reinterpret_cast<const f32x4*>(&tsh[i][32 * g + 8 * s2]);
+          const f32x4 t0 = tp[0], t1 = tp[1];
+#pragma unroll
+          for (int p2 = 0; p2 < 4; ++p2) {
+            const float x0 = bf16_bits_to_f32(qw[p2] & 0xffffu), x1 = bf16_bits_to_f32(qw[p2] >> 16);
+            const float y0 = p2 < 2 ? t0[2 * p2] : t1[2 * p2 - 4], y1 = p2 < 2 ? t0[2 * p2 + 1] : t1[2 * p2 - 3];
+            a = fmaf(x0, y0, a);
+            a = fmaf(x1, y1, a);
+            ab = fmaf(fabsf(x0), fabsf(y0), ab);
+            ab = fmaf(fabsf(x1), fabsf(y1), ab);
+          }
+        }
+        a += __shfl_xor(a, 16, kWave);
+        a += __shfl_xor(a, 32, kWave);
+        ab += __shfl_xor(ab, 16, kWave);
+        ab += __shfl_xor(ab, 32, kWave);
+        const double cnt = (double)(n - (Mt - 1) * B);
+        const double tv = (double)a / cnt, te = ldexp((double)ab / cnt, -14);
+        lo = fmax(lo, tv - te);
+        hi = fmax(hi, tv + te);
+      }
+      const double mlo = fmax(lo, 0.0), mhi = fmax(hi, 0.0);
+      const double wd = (double)wq[i];
+      double rl = wd >= 0.0 ? wd * mlo : wd * mhi, rh = wd >= 0.0 ? wd * mhi : wd * mlo;
+      if (!active) rl = rh = -__builtin_huge_val();
+      if (g == 0) {
+        sh.rlo[i][h_a] = rl;
+        sh.rhi[i][h_a] = rh;
+      }
+    }
+    __syncthreads();
+    {
+      // for head h, against heads [16j, 16j + 16): how many may beat it (upper
+      // bound reaches its lower bound, ties going to the lower head) and how many
+      // must (lower bound reaches its upper bound)
+      const int h = tid & 63, j = tid >> 6;
+#pragma unroll
+      for (int i = 0; i < QG; ++i) {
+        const double lh = sh.rlo[i][h], hh = sh.rhi[i][h];
+        int may = 0, must = 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int o = 16 * j + u;
+          const double l2 = sh.rlo[i][o], h2 = sh.rhi[i][o];
+          may += o != h && (h2 > lh || (h2 == lh && o < h));
+          must += l2 > hh || (l2 == hh && o < h);
+        }
+        sh.count[i][j][h] = may | (must << 8);
+      }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      // in: fewer than A heads may beat it; out: at least A heads must; else
+      // evaluated exactly (every head when the caller asks for r)
+      const int h = tid;
+#pragma unroll
+      for (int i = 0; i < QG; ++i) {
+        const int c = sh.count[i][0][h] + sh.count[i][1][h] + sh.count[i][2][h] + sh.count[i][3][h];
+        const bool active = tq0 + i < T && h < H;
+        sh.state[i][h] = !active ? 0 : st.r_out ? 2 : (c & 255) < st.A ? 1 : (c >> 8) >= st.A ? 0 : 2;
+      }
+    }
+    __syncthreads();
+    const double divb = kbar ? 1.0 : (double)B;
+#pragma unroll
+    for (int i = 0; i < QG; ++i) {
+      const bool need = sh.state[i][h_a] == 2;
+      if (wave_ballot(need) == 0) continue;  // uniform over the wave
+      const int t = tq0 + i;
+      const int tc = t < T ? t : T - 1;
+      // the head's candidate block, coded as -1 (no block can be positive), the
+      // leader block, or the leader + 2^30 when the second best reaches the
+      // leader's bound (every block evaluated)
+      const float thr = best[i] - 2.f * err[i];
+      const bool use = arg[i] >= 0 && best[i] + err[i] >= 0.f;
+      const int c = use ? (arg[i] | (second[i] >= thr ? (1 << 30) : 0)) : -1;
+      const int b = c >= 0 ? (c & ((1 << 30) - 1)) : 0;  // (block 0 when there is none: unused)
+      const double rho = sum_groups(exact_part32(qa[i], st.ksum + (size_t)b * kHeadDim,
+                                                 kbar ? kbar + (size_t)b * kHeadDim : nullptr, g)) / divb;
+      double m = c >= 0 && rho > 0.0 ? rho : 0.0;
+      uint64_t ambm = wave_ballot(g == 0 && need && c >= 0 && (c >> 30) != 0);
       while (ambm) {
         // a head whose bf16 scores cannot separate its blocks: every complete block
         // in float64, the wave's 16 columns taking 16 blocks at a time
@@ -296,13 +400,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (col == hc) {
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2)
-            *reinterpret_cast<u32x4*>(&qrow[wv][32 * g + 8 * s2]) = __builtin_bit_cast(u32x4, qa[i][s2]);
+            *reinterpret_cast<u32x4*>(&sh.qrow[wv][32 * g + 8 * s2]) = __builtin_bit_cast(u32x4, qa[i][s2]);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the row is in LDS for the whole wave
         __builtin_amdgcn_wave_barrier();
         bf16x8 qh[4];
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) qh[s2] = *reinterpret_cast<const bf16x8*>(&qrow[wv][32 * g + 8 * s2]);
+        for (int s2 = 0; s2 < 4; ++s2) qh[s2] = *reinterpret_cast<const bf16x8*>(&sh.qrow[wv][32 * g + 8 * s2]);
         double mb = 0.0;
         for (int b0 = 0; b0 < nfull[i]; b0 += 2 * kFastTile) {  // uniform over the query
           const int b1 = b0 + col, b2 = b0 + kFastTile + col;
@@ -323,48 +427,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (col == hc) m = mb > m ? mb : m;
         __builtin_amdgcn_wave_barrier();
       }
-      const int n = visible_len(pos[tc], L);
+      const int n = nvis[i];
       const int Mt = (int)(((long long)n + B - 1) / B);
       if (Mt > 0) {
-        // the query's own last block, always exactly, from its float64 sum
+        // the query's own last block, exactly, from its float64 sum
         const double tq = exact_part32(qa[i], st.tsum + (size_t)tc * kHeadDim, nullptr, g);
-        const double rho = sum_groups(tq) / (double)(n - (Mt - 1) * B);
-        m = rho > m ? rho : m;
+        const double rho_t = sum_groups(tq) / (double)(n - (Mt - 1) * B);
+        m = rho_t > m ? rho_t : m;
       }
-      const bool active = t < T && h_a < H;
-      const double r = active ? (double)st.w[(size_t)t * H + h_a] * m + 0.0 : -__builtin_huge_val();
-      if (g == 0) {
-        rsh[i][h_a] = r;
-        if (st.r_out && active) st.r_out[(size_t)t * H + h_a] = (float)r;
-      }
-    }
-    __syncthreads();
-    {
-      // rank of head h: wave j compares it with heads [16j, 16j + 16)
-      const int h = tid & 63, j = tid >> 6;
-#pragma unroll
-      for (int i = 0; i < QG; ++i) {
-        const double rh = rsh[i][h];
-        int cnt = 0;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const double r2 = rsh[i][16 * j + u];
-          cnt += (r2 > rh) || (r2 == rh && 16 * j + u < h);
-        }
-        rank_part[i][j][h] = cnt;
+      const double r = (double)wq[i] * m + 0.0;
+      if (g == 0 && need) {
+        sh.rex[i][h_a] = r;
+        if (st.r_out) st.r_out[(size_t)t * H + h_a] = (float)r;
       }
     }
     __syncthreads();
     if (tid < kWave) {
+      // the chosen set: every head that is in, and the best of the exactly
+      // evaluated heads, under (-r, h), up to A
       const int h = tid;
 #pragma unroll
       for (int i = 0; i < QG; ++i) {
         const int t = tq0 + i;
-        const int rank = rank_part[i][0][h] + rank_part[i][1][h] + rank_part[i][2][h] + rank_part[i][3][h];
-        const bool sel = t < T && h < H && rank < st.A;
+        const int sth = sh.state[i][h];
+        const int nin = __builtin_popcountll(wave_ballot(sth == 1));
+        bool sel = sth == 1;
+        if (wave_ballot(sth == 2) != 0) {  // uniform over the wave
+          const double rh = sh.rex[i][h];
+          int rank = 0;
+          for (int o = 0; o < kWave; ++o) {
+            if (sh.state[i][o] != 2) continue;  // uniform
+            const double r2 = sh.rex[i][o];
+            rank += (r2 > rh) || (r2 == rh && o < h);
+          }
+          sel = sel || (sth == 2 && rank < st.A - nin);
+        }
         const uint64_t mask = wave_ballot(sel);
         const int slot = sel ? lanes_below(mask) : -1;
-        slot_of[i][h] = slot;
+        sh.slot_of[i][h] = slot;
         if (sel) {
           if (st.heads) st.heads[(size_t)t * st.A + slot] = h;
           if (st.wr) st.wr[(size_t)t * st.A + slot] = st.w[(size_t)t * H + h];
@@ -376,7 +476,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       // the lanes that hold a chosen head's q row write it to its slot
 #pragma unroll
       for (int i = 0; i < QG; ++i) {
-        const int slot = slot_of[i][h_a];
+        const int slot = sh.slot_of[i][h_a];
         if (slot >= 0) {
           u32x4* dst = reinterpret_cast<u32x4*>(st.qr + ((size_t)(tq0 + i) * st.A + slot) * kHeadDim + 32 * g);
 #pragma unroll

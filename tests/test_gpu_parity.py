@@ -132,6 +132,25 @@ def test_route_equal_blocks(kdt):
     assert ill == 0
 
 
+@pytest.mark.parametrize("kdt", [O.KDT_BF16, O.KDT_FP8])
+def test_route_tied_heads_at_the_cut(kdt):
+    # heads come in identical pairs (same q row, same weight), so r ties exactly within
+    # each pair and, with A odd, the cut splits a pair in every query: no interval can
+    # place those heads, the exact values decide and the lower head must win the tie
+    T, L, H, A, B = 1500, 1500, 64, 7, 16
+    inp = _case(32, T, L, H, kdt, positions="prefill")
+    inp["q"][:, 1::2] = inp["q"][:, 0::2]
+    inp["w"][:, 1::2] = inp["w"][:, 0::2]
+    q, w, K, ks, pos = to_gpu(inp)
+    P = oracle_problem(inp, B)
+    heads_o, r_o = O.route(P, A)
+    for with_r in (False, True):
+        out = S.route(q, w, K, pos, B, A, ks, with_r=with_r)
+        heads = _np(out[0] if with_r else out)
+        for t in range(T):
+            assert sorted(heads[t]) == sorted(int(h) for h in heads_o[t]), f"row {t} (with r: {with_r})"
+
+
 # ----------------------------------------------------------------- MISA
 
 MISA_CASES = [
