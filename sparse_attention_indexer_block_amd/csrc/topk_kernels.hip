@@ -54,6 +54,8 @@ struct alignas(16) TopkShared {
   int digit, rem;
   int flag;
   int nlist;
+  int ncand;            // keys of the threshold bin gathered so far
+  uint32_t cmin, cmax;  // and their extremes
   uint32_t tau;
   int need;
   alignas(16) uint32_t list[kListCap];
@@ -1027,6 +1029,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
           hi = max(hi, u[g][e]);
         }
     for (int b = tid; b < kFineBins; b += NT) sm.hist[b] = 0u;
+    if (tid == 0) {
+      sm.ncand = 0;
+      sm.cmin = 0xffffffffu;
+      sm.cmax = 0u;
+    }
     block_minmax<NT>(lo, hi, sm);  // synchronises
     const float xlo = key_score(sm.umin);
     const float scale = lin_scale(xlo, key_score(sm.umax), kFineBins);
@@ -1041,49 +1048,56 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
     const int rem = sm.rem;
     const int c = (int)sm.hist[bstar];
     if (c <= kListCap) {
-      // the threshold bin's keys (in item order): straight into sm.list when
-      // few enough to rank pairwise, else into cand for radix digits
+      // the threshold bin's keys, in whatever order the atomics give (only their
+      // values decide the threshold): into sm.list when few enough to rank
+      // pairwise, else into cand for radix digits
       uint32_t* dst = c <= kRankCap ? sm.list : cand;
-      auto keep = [&](int g, int e) { return in(g, e) && lin_bin(u[g][e], xlo, scale, kFineBins) == bstar; };
-      int nw = 0;
-      uint32_t clo = 0xffffffffu, chi = 0u;
+      const bool need_ext = rem >= c || c > kRankCap;  // extremes used below (uniform)
+      uint32_t kbits = 0u, clo = 0xffffffffu, chi = 0u;
+      int wcnt = 0;
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool kp = keep(g, e);
-          nw += __popcll(wave_ballot(kp));
+          const bool kp = in(g, e) && lin_bin(u[g][e], xlo, scale, kFineBins) == bstar;
+          kbits |= (uint32_t)kp << (4 * g + e);
+          wcnt += __popcll(wave_ballot(kp));
           if (kp) {
             clo = min(clo, u[g][e]);
             chi = max(chi, u[g][e]);
           }
         }
-      if (lane == 0) sm.wgt[w] = nw;
-      __syncthreads();
-      int at = 0;
-      for (int i = 0; i < w; ++i) at += sm.wgt[i];
+      if (wcnt) {  // uniform: one slot range per wave, taken with one atomic
+        int at = 0;
+        if (lane == 0) at = atomicAdd(&sm.ncand, wcnt);
+        at = __shfl(at, 0, kWave);
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool kp = keep(g, e);
-          const uint64_t m = wave_ballot(kp);
-          if (kp) dst[at + lanes_below(m)] = u[g][e];
-          at += __popcll(m);
+          for (int e = 0; e < 4; ++e) {
+            const bool kp = (kbits >> (4 * g + e)) & 1u;
+            const uint64_t m = wave_ballot(kp);
+            if (kp) dst[at + lanes_below(m)] = u[g][e];
+            at += __popcll(m);
+          }
+        if (need_ext) {
+          clo = wave_min_u32(clo);
+          chi = wave_max_u32(chi);
+          if (lane == 0) {
+            atomicMin(&sm.cmin, clo);
+            atomicMax(&sm.cmax, chi);
+          }
         }
-      if (rem >= c || c > kRankCap) {
-        block_minmax<NT>(clo, chi, sm);  // synchronises (the list is complete)
-      } else {
-        __syncthreads();
       }
+      __syncthreads();  // the list and its extremes are complete
       if (rem >= c) {
-        tau = sm.umin;  // the whole bin is kept
+        tau = sm.cmin;  // the whole bin is kept
         need_eq = c;
       } else if (c <= kRankCap) {
         rank_in_list<NT>(c, rem, sm, tau, need_eq);
       } else {
         auto key_at = [=](int i) { return cand[i]; };
-        radix_threshold<NT>(key_at, c, rem, sm.umin, sm.umax, sm, tau, need_eq);
+        radix_threshold<NT>(key_at, c, rem, sm.cmin, sm.cmax, sm, tau, need_eq);
       }
     } else {
       // a crowded bin (heavy ties): digit-by-digit search over every item
