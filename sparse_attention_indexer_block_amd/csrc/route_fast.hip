@@ -145,6 +145,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int s = 0; s < 4; ++s) qa[i][s] = __builtin_bit_cast(bf16x8, ok ? src[s] : u32x4{0u, 0u, 0u, 0u});
   }
+  // blocks any query of the group can use: only those are staged and scored
+  int mneed = 0;
+#pragma unroll
+  for (int i = 0; i < QG; ++i) mneed = max(mneed, nfull[i]);
+  const int bend = min(M, mneed);
   // hi / lo bf16 parts of the workgroup's block means, staged once in LDS for
   // the four waves (rows padded by 16 bytes: conflict-free 16-byte reads)
   constexpr int NB = TPW * kFastTile;
@@ -160,17 +165,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
         const int c = tid + 256 * u, r = c >> 4, v = c & 15;
-        const int blk = min(bstart + r, M - 1);  // past the end: any valid block, zeroed below
-        hv[u] = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim)[v];
-        lv[u] = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + kHeadDim)[v];
+        const int blk = bstart + r;
+        const bool need = blk < bend;  // rows past it are stored as zeros below
+        hv[u] = need ? reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim)[v] : u32x4{0u, 0u, 0u, 0u};
+        lv[u] = need ? reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + kHeadDim)[v]
+                     : u32x4{0u, 0u, 0u, 0u};
       }
     } else {
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
         const int c = tid + 256 * u, r = c >> 4, v = c & 15;
-        const int blk = min(bstart + r, M - 1);
-        const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)blk * kHeadDim + 8 * v);
-        const f32x4 x0 = src[0], x1 = src[1];
+        const int blk = bstart + r;
+        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
+        if (blk < bend) {
+          const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)blk * kHeadDim + 8 * v);
+          x0 = src[0];
+          x1 = src[1];
+        }
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           uint32_t ha, la, hb, lb;
@@ -184,7 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int u = 0; u < NC; ++u) {
       const int c = tid + 256 * u, r = c >> 4, v = c & 15;
-      const bool ok = bstart + r < M;
+      const bool ok = bstart + r < bend;
       *reinterpret_cast<u32x4*>(&smh[r * RS + 8 * v]) = ok ? hv[u] : u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&sml[r * RS + 8 * v]) = ok ? lv[u] : u32x4{0u, 0u, 0u, 0u};
     }
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   for (int tt = 0; tt < TPW; ++tt) {
     const int b0 = (tr * TPW + tt) * kFastTile;
-    if (b0 >= M) break;  // uniform
+    if (b0 >= bend) break;  // uniform: no query of the group uses these blocks
     // A operands of this lane's block row b0 + col: hi, lo and |hi|, dims 32g .. 32g+31
     bf16x8 bh[4], bl[4], ba[4];
     const int rl = (tt * kFastTile + col) * RS + 32 * g;
@@ -279,9 +290,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   } else {
     // The staged means are dead after the tile loop: the settling reuses their LDS.
     struct Lds {
-      double rlo[QG][kWave], rhi[QG][kWave];  // certified bounds of r(t, h)
+      float2 rb[QG][kWave];                   // certified bounds of r(t, h), rounded outward
       double rex[QG][kWave];                  // exact r of the heads evaluated
-      int count[QG][4][kWave];                // partial counts of heads that may / must beat h
       int state[QG][kWave];                   // 0 out, 1 in, 2 evaluated exactly
       int slot_of[QG][kWave];
       uint16_t qrow[4][kHeadDim];             // per wave: one q row
@@ -337,41 +347,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       double rl = wd >= 0.0 ? wd * mlo : wd * mhi, rh = wd >= 0.0 ? wd * mhi : wd * mlo;
       if (!active) rl = rh = -__builtin_huge_val();
       if (g == 0) {
-        sh.rlo[i][h_a] = rl;
-        sh.rhi[i][h_a] = rh;
+        float fl = (float)rl, fh = (float)rh;  // outward: below rl, above rh
+        if ((double)fl > rl) fl = nextafterf(fl, -__builtin_huge_valf());
+        if ((double)fh < rh) fh = nextafterf(fh, __builtin_huge_valf());
+        sh.rb[i][h_a] = make_float2(fl, fh);
       }
     }
     __syncthreads();
-    {
-      // for head h, against heads [16j, 16j + 16): how many may beat it (upper
-      // bound reaches its lower bound, ties going to the lower head) and how many
-      // must (lower bound reaches its upper bound)
-      const int h = tid & 63, j = tid >> 6;
-#pragma unroll
-      for (int i = 0; i < QG; ++i) {
-        const double lh = sh.rlo[i][h], hh = sh.rhi[i][h];
-        int may = 0, must = 0;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int o = 16 * j + u;
-          const double l2 = sh.rlo[i][o], h2 = sh.rhi[i][o];
-          may += o != h && (h2 > lh || (h2 == lh && o < h));
-          must += l2 > hh || (l2 == hh && o < h);
-        }
-        sh.count[i][j][h] = may | (must << 8);
+    static_assert(QG * kWave <= 256, "one thread per (query, head)");
+    if (tid < QG * kWave) {
+      // head h of query i against every head: how many may beat it (upper bound
+      // at or above its lower bound, ties going to the lower head) and how many
+      // must (lower bound at or above its upper bound). In: fewer than A may;
+      // out: at least A must; else evaluated exactly (every head when the
+      // caller asks for r).
+      const int i = tid >> 6, h = tid & 63;
+      const float2 mine = sh.rb[i][h];
+      int may = 0, must = 0;
+#pragma unroll 8
+      for (int o = 0; o < kWave; ++o) {
+        const float2 b = sh.rb[i][o];
+        may += o != h && (b.y > mine.x || (b.y == mine.x && o < h));
+        must += b.x > mine.y || (b.x == mine.y && o < h);
       }
-    }
-    __syncthreads();
-    if (tid < kWave) {
-      // in: fewer than A heads may beat it; out: at least A heads must; else
-      // evaluated exactly (every head when the caller asks for r)
-      const int h = tid;
-#pragma unroll
-      for (int i = 0; i < QG; ++i) {
-        const int c = sh.count[i][0][h] + sh.count[i][1][h] + sh.count[i][2][h] + sh.count[i][3][h];
-        const bool active = tq0 + i < T && h < H;
-        sh.state[i][h] = !active ? 0 : st.r_out ? 2 : (c & 255) < st.A ? 1 : (c >> 8) >= st.A ? 0 : 2;
-      }
+      const bool active = tq0 + i < T && h < H;
+      sh.state[i][h] = !active ? 0 : st.r_out ? 2 : may < st.A ? 1 : must >= st.A ? 0 : 2;
     }
     __syncthreads();
     const double divb = kbar ? 1.0 : (double)B;
