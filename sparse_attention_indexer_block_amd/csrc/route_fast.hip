@@ -712,7 +712,7 @@ hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const floa
   RoutePart* pp = reinterpret_cast<RoutePart*>(part);
   const uint16_t* kb = kbar ? nullptr : kb16;
   const RouteSettle st{w, ksum, tsum, A, heads, r_out, qr, wr};
-  const dim3 grid(ntr, (T + 1) / 2);  // two queries and eight block tiles per workgroup
+  const dim3 grid(ntr, (T + 1) / 2);  // split form: two queries and eight block tiles per workgroup
   if (ntr == 1)  // every block in one range: four queries, settled and selected in the same launch
     return cx.launch("route_fast", k_route_fast<4, 8, true>, dim3(1, (T + 3) / 4), dim3(256), 0, q, pos, T,
                      H, L, B, ntr, kb, kbar, pp, st);
