@@ -467,3 +467,35 @@ def test_cached_block_means(case, source):
     check_hisa(inp, B, 4, 64, _np(idx), _np(sc), label="cached hisa")
     idx, sc = S.misa_hisa_topk(q, w, K, pos, B, A, 4, 64, ks, kbar=kbar)
     check_misa_hisa(inp, B, A, 4, 64, _np(idx), _np(sc), heads_o, label="cached misa-hisa")
+
+
+KBAR_MANY_CASES = [
+    # seed, T, L, H, A, B, kdt: enough queries for the bf16 router, with every block in
+    # one range (settled in the same launch) and over several ranges (split form)
+    (64, 700, 2000, 64, 8, 16, O.KDT_BF16),
+    (65, 400, 5000, 32, 7, 16, O.KDT_FP8),
+]
+
+
+@pytest.mark.parametrize("source", ["pooled", "arbitrary"])
+@pytest.mark.parametrize("case", KBAR_MANY_CASES, ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}B{c[5]}kd{c[6]}")
+def test_cached_block_means_many_queries(case, source):
+    seed, T, L, H, A, B, kdt = case
+    inp = _case(seed, T, L, H, kdt, positions="prefill")
+    q, w, K, ks, pos = to_gpu(inp)
+    M = -(-L // B)
+    if source == "pooled":
+        kbar = S.block_means(K, B, ks)
+    else:
+        rows = np.random.default_rng(seed).standard_normal((M, 128)).astype(np.float32) * 0.2
+        kbar = torch.from_numpy(rows).cuda()
+    inp = dict(inp, kbar=_np(kbar))
+    P = oracle_problem(inp, B)
+    heads, r = S.route(q, w, K, pos, B, A, ks, with_r=True, kbar=kbar)
+    heads_o, ill = check_heads(P, A, _np(heads), _np(r))
+    assert ill == 0
+    heads2 = S.route(q, w, K, pos, B, A, ks, kbar=kbar)  # placed by intervals
+    _, ill = check_heads(P, A, _np(heads2))
+    assert ill == 0
+    idx, sc = S.score_topk(q, w, K, pos, B, A, 64, ks, kbar=kbar)
+    _check_misa(inp, B, A, 64, _np(idx), _np(sc), heads_o, label="cached misa, many queries")
