@@ -7,12 +7,12 @@ import or call this package, and it shares no code with that library.
 """
 from .indexer import (KDT_BF16, KDT_FP8, Problem, block_logits, block_means, block_ranges,
                       decode_bf16, decode_e4m3fn, dense_scores, dense_topk, dequant_keys,
-                      first_k, full_block_means, head_logits, hisa_block_scores, hisa_topk,
+                      block_maxima, first_k, full_block_means, head_logits, hisa_block_scores, hisa_topk,
                       magnitude_terms, misa_hier_topk, misa_hisa_topk, misa_topk, route,
                       routed_block_scores, routed_scores)
 
 __all__ = ["KDT_BF16", "KDT_FP8", "Problem", "block_logits", "block_means", "block_ranges",
            "decode_bf16", "decode_e4m3fn", "dense_scores", "dense_topk", "dequant_keys",
-           "first_k", "full_block_means", "head_logits", "hisa_block_scores", "hisa_topk",
+           "block_maxima", "first_k", "full_block_means", "head_logits", "hisa_block_scores", "hisa_topk",
            "magnitude_terms", "misa_hier_topk", "misa_hisa_topk", "misa_topk", "route",
            "routed_block_scores", "routed_scores"]

@@ -34,6 +34,11 @@ Where the pages leave a formula open, the fixed reading is:
   * router score r(t,h) = w[t,h] * max_b ReLU(q[t,h] . Kbar_{t,b}); the routed
     set is the first A heads under the key (-r, h).
   * HISA block score beta(t,b) = sum_h w[t,h] * ReLU(q[t,h] . Kbar_{t,b}).
+  * HISA with max pooling (the HISA write-up's limitations section names max
+    pooling in place of mean pooling as a possible improvement): the
+    representative of a block is, per dimension, the largest of its visible
+    keys' values (the tail block over its visible keys only); beta and the
+    refine are otherwise unchanged.  Cached means do not apply to it.
   * MISA inside HISA (the head axis and the token axis combined, as the MISA
     summary's "Contribuciones Clave" and "Significado y Afirmaciones" call them
     complementary): the routed heads R_t replace all H heads in both HISA
@@ -186,6 +191,17 @@ def full_block_means(K_values: np.ndarray, B: int) -> np.ndarray:
         if L > 0 else np.zeros((0, K_values.shape[1]))
 
 
+def block_maxima(P: Problem, t: int) -> np.ndarray:
+    """Max-pooled representatives: per dimension, the largest visible key value
+    of each block [HISA write-up, limitations: max pooling in place of mean
+    pooling]."""
+    rng = block_ranges(P.n(t), P.B)
+    out = np.zeros((len(rng), P.d))
+    for b, (s0, s1) in enumerate(rng):
+        out[b] = P.K[s0:s1].max(axis=0)
+    return out
+
+
 def block_logits(P: Problem, t: int) -> np.ndarray:
     """rho(t,h,b) = q[t,h] . Kbar_{t,b}, shape [H, M_t]."""
     return P.q[t] @ block_means(P, t).T
@@ -256,20 +272,24 @@ def misa_hier_topk(P: Problem, A: int, kprime: int, k: int, heads=None):
     return out, heads, cands
 
 
-def hisa_block_scores(P: Problem, t: int) -> np.ndarray:
+def hisa_block_scores(P: Problem, t: int, pool: str = "mean") -> np.ndarray:
     """beta(t,b): the indexer formula with all H heads applied to the block
-    representatives [HISA Stage 1: the query scores only the representatives]."""
-    rho = block_logits(P, t)
+    representatives [HISA Stage 1: the query scores only the representatives];
+    pool="max" takes the max-pooled representatives instead of the means."""
+    rho = block_logits(P, t) if pool == "mean" else P.q[t] @ block_maxima(P, t).T
     return _canon((P.w[t][:, None] * np.maximum(rho, 0.0)).sum(axis=0))
 
 
-def hisa_topk(P: Problem, m: int, k: int):
+def hisa_topk(P: Problem, m: int, k: int, pool: str = "mean"):
     """HISA [HISA Stage 1 + Stage 2]: keep the top-m blocks by beta (lower block
     index first on ties), run the token-level indexer on the visible tokens of
-    those blocks only, keep top-k.  Returns (per-query results, chosen blocks)."""
+    those blocks only, keep top-k.  pool selects mean (the pages' method) or
+    max-pooled block representatives.  Returns (per-query results, chosen
+    blocks)."""
+    assert pool in ("mean", "max")
     out, chosen = [], []
     for t in range(P.T):
-        beta = hisa_block_scores(P, t)
+        beta = hisa_block_scores(P, t, pool)
         blocks, _ = first_k(beta, np.arange(len(beta)), m)
         chosen.append(np.sort(blocks))
         rng = block_ranges(P.n(t), P.B)

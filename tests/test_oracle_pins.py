@@ -155,6 +155,17 @@ class Exact:
                         for i in range(self.d)])
         return out
 
+    def kmax(self, t):
+        n, out = self.n(t), []
+        for b0 in range(0, n, self.B):
+            b1 = min(b0 + self.B, n)
+            out.append([max(self.K[s, i] for s in range(b0, b1)) for i in range(self.d)])
+        return out
+
+    def beta_max(self, t):
+        return [sum((self.w[t, h] * max(Fraction(0), self.dot(self.q[t, h], c)) for h in range(self.H)),
+                    Fraction(0)) for c in self.kmax(t)]
+
     def r(self, t):
         kb = self.kbar(t)
         return [self.w[t, h] * max([Fraction(0)] + [self.dot(self.q[t, h], c) for c in kb])
@@ -210,6 +221,14 @@ def test_exact_brute_force_int_grid(seed, B):
         (si, _), bl = O.hisa_topk(P, m, k)[0][t], O.hisa_topk(P, m, k)[1][t]
         assert list(bl) == blocks
         assert sorted(si) == sorted(final)
+        # HISA with max-pooled representatives
+        blocks = _rank_select(X.beta_max(t), m)
+        cand = [s for b in blocks for s in range(b * B, min((b + 1) * B, n))]
+        final = [cand[j] for j in _rank_select([ia[s] for s in cand], k)]
+        res, xbl = O.hisa_topk(P, m, k, pool="max")
+        assert [float(v) for v in X.beta_max(t)] == list(O.hisa_block_scores(P, t, "max"))
+        assert list(xbl[t]) == blocks
+        assert sorted(res[t][0]) == sorted(final)
         # MISA inside HISA: the routed heads in both stages
         blocks = _rank_select(X.beta(t, heads[t]), m)
         cand = [s for b in blocks for s in range(b * B, min((b + 1) * B, n))]
@@ -518,3 +537,43 @@ def test_cached_means_closed_form():
             P2 = O.Problem(inp["q"][t:t + 1], inp["w"][t:t + 1], inp["K"], inp["pos"][t:t + 1], B,
                            O.KDT_BF16, None, kbar=k2)
             assert np.array_equal(O.route(P2, 2)[1][0], r[t])
+
+
+def test_hisa_max_pool_reductions():
+    """Max pooling reduces to mean pooling where the two representatives agree:
+    blocks of one key (B = 1), and blocks whose keys are all equal; elsewhere
+    the max-pooled representative dominates the mean in every dimension."""
+    inp = _tiny(7, False, T=4, L=40, H=4, d=16)
+    P1 = O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], 1)
+    a, b = O.hisa_topk(P1, 5, 6), O.hisa_topk(P1, 5, 6, pool="max")
+    for t in range(P1.T):
+        assert list(a[1][t]) == list(b[1][t])
+        assert list(a[0][t][0]) == list(b[0][t][0])
+    B = 4
+    K = inp["K"].copy()
+    for b0 in range(0, K.shape[0], B):
+        K[b0:b0 + B] = K[b0]  # every block holds one key B times
+    PB = O.Problem(inp["q"], inp["w"], K, inp["pos"], B)
+    for t in range(PB.T):
+        assert np.array_equal(O.hisa_block_scores(PB, t), O.hisa_block_scores(PB, t, "max"))
+    P4 = O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], B)
+    for t in range(P4.T):
+        assert np.all(O.block_maxima(P4, t) >= O.block_means(P4, t))
+
+
+def test_hisa_max_pool_keeps_a_needle_block():
+    """Hand-built case (d = 2, one head, w = 1, q = (1, 0)): block 0 holds keys
+    (4, 0) and (-4, 0), whose mean (0, 0) scores 0 while its maximum (4, 0)
+    scores 4; block 1 holds (1, 0) twice and scores 1 either way.  With m = 1
+    mean pooling keeps block 1 and misses the key that scores 4; max pooling
+    keeps block 0 and finds it."""
+    bf = lambda v: np.array(v, dtype=np.float32).view(np.uint32) >> 16
+    q = bf([[[1.0, 0.0]]]).astype(np.uint16)
+    K = bf([[4.0, 0.0], [-4.0, 0.0], [1.0, 0.0], [1.0, 0.0]]).astype(np.uint16)
+    P = O.Problem(q, np.ones((1, 1), np.float32), K, np.array([3], np.int32), 2)
+    assert list(O.hisa_block_scores(P, 0)) == [0.0, 1.0]
+    assert list(O.hisa_block_scores(P, 0, "max")) == [4.0, 1.0]
+    (mi, ms), = O.hisa_topk(P, 1, 1)[0]
+    (xi, xs), = O.hisa_topk(P, 1, 1, pool="max")[0]
+    assert (list(mi), list(ms)) == ([2], [1.0])
+    assert (list(xi), list(xs)) == ([0], [4.0])
