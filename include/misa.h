@@ -14,6 +14,8 @@
  *   hisa_topk       top-m key blocks by their mean-pooled representative, then
  *                   the full indexer on the tokens of those blocks, then top-k
  *                   (HISA write-up, section 3, Stage 1 and Stage 2).
+ *   hisa_maxpool_topk  HISA with max-pooled block representatives (HISA
+ *                   write-up, limitations).
  *   misa_hisa_topk  HISA with the routed heads in both stages: the head axis
  *                   of MISA and the token axis of HISA combined.
  *   misa_block_means  the query-independent block means the router pools.
@@ -162,6 +164,17 @@ misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* head
  * those blocks with all H heads (I_all) and return the top-k. */
 misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* HISA with max-pooled block representatives (HISA write-up, limitations:
+ * max pooling in place of mean pooling, listed as a possible improvement).
+ * As hisa_topk, except that the representative of block b of query t is, per
+ * dimension, the largest of its visible keys' values (dequantised keys; the
+ * tail block over [b*B, n_t) only), so that one key standing out in a block is
+ * not averaged away. Workspace: misa_workspace_bytes(p, MISA_OP_HISA_TOPK, ., .,
+ * k, m). p->kbar must be NULL (cached means do not apply); otherwise errors,
+ * arguments and outputs as hisa_topk. */
+misa_status hisa_maxpool_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* MISA inside HISA. The MISA technical summary presents head routing as an
  * efficiency axis complementary to token-axis hierarchies such as HISA and

@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "misa_score_topk": (i32, [P, i32, vp, i32, vp, vp, vp, sz, vp]),
             "misa_hier_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
             "hisa_topk": (i32, [P, i32, i32, vp, vp, vp, sz, vp]),
+            "hisa_maxpool_topk": (i32, [P, i32, i32, vp, vp, vp, sz, vp]),
             "misa_hisa_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
             "misa_status_str": (ctypes.c_char_p, [i32]),
             "misa_last_error": (ctypes.c_char_p, []),
@@ -224,6 +225,14 @@ def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, kbar=None)
     idx, sc = out if out is not None else _outputs(p, k, q.device)
     ws, n = _workspace(p, OP_HISA_TOPK, q.device, ws, m=m, k=k)
     _check(lib().hisa_topk(ctypes.byref(p), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n, _stream()))
+    return idx, sc
+
+
+def hisa_maxpool_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None):
+    p = make_problem(q, w, K, pos, B, k_scale)
+    idx, sc = out if out is not None else _outputs(p, k, q.device)
+    ws, n = _workspace(p, OP_HISA_TOPK, q.device, ws, m=m, k=k)
+    _check(lib().hisa_maxpool_topk(ctypes.byref(p), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n, _stream()))
     return idx, sc
 
 

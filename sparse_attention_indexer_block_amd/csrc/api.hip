@@ -246,7 +246,8 @@ static misa_status check_out(const void* ptr, const char* name) {
 // and tsum are already in the workspace from an earlier router pass of this call.
 static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws,
                              int A, int32_t* heads, float* r, float* beta, int beta_ld,
-                             uint16_t* qr = nullptr, float* wr = nullptr, bool sums_ready = false) {
+                             uint16_t* qr = nullptr, float* wr = nullptr, bool sums_ready = false,
+                             bool max_pool = false) {
   const bool fp8 = p->k_dtype == MISA_K_FP8_E4M3FN;
   double* ksum = at<double>(ws, pl.ksum);
   double* tsum = at<double>(ws, pl.tsum);
@@ -258,11 +259,11 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   // with cached block means only each query's last block is pooled here
   if (!sums_ready)
     HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
-                              p->kbar != nullptr, kb16),
+                              p->kbar != nullptr, kb16, 0, max_pool),
             "block sums");
   if (!fast) {
     HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, pmax,
-                         heads, r, beta, beta_ld, qr, wr),
+                         heads, r, beta, beta_ld, qr, wr, max_pool),
             "router");
   } else {
     HIP_TRY(launch_route_heads(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, kb16, p->kbar,
@@ -365,10 +366,10 @@ static misa_status run_routed_scores(const LaunchCtx& cx, const misa_problem* p,
 // block scores of every visible block, the top-m blocks, the indexer on their
 // tokens, top-k. sums_ready: the block sums are already in the workspace.
 static misa_status run_hisa(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws, int k,
-                            int32_t* idx, float* scores, bool sums_ready) {
+                            int32_t* idx, float* scores, bool sums_ready, bool max_pool = false) {
   float* beta = at<float>(ws, pl.beta);
   MISA_TRY(run_route(cx, p, pl, ws, 1, nullptr, nullptr, beta, (int)pl.beta_ld, nullptr, nullptr,
-                     sums_ready));
+                     sums_ready, max_pool));
   int32_t* blocks = at<int32_t>(ws, pl.blocks);
   int32_t* nblocks = at<int32_t>(ws, pl.nblocks);
   TopkArgs tb = topk_args(p);
@@ -571,6 +572,21 @@ misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx,
   MISA_TRY(check_ws(pl, ws, ws_bytes));
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
   return run_hisa(cx, p, pl, ws, k, idx, scores, false);
+}
+
+misa_status hisa_maxpool_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,
+                              void* ws, size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, true));
+  if (p->kbar) return fail(MISA_ERR_INVALID_ARG, "kbar must be NULL: cached means do not apply to max pooling");
+  if (m < 1) return fail(MISA_ERR_INVALID_ARG, "m = %d must be >= 1", m);
+  if (k < 1) return fail(MISA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(idx, "idx"));
+  MISA_TRY(check_out(scores, "scores"));
+  const Plan pl = make_plan(p, MISA_OP_HISA_TOPK, 1, 1, k, m);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  return run_hisa(cx, p, pl, ws, k, idx, scores, false, true);
 }
 
 misa_status misa_hisa_topk(const misa_problem* p, int32_t A, const int32_t* heads, int32_t m, int32_t k,

@@ -53,11 +53,12 @@ inline long long padded_ld(long long n) { return ((n + 127) / 128) * 128; }
 // ---- router side (route_kernels.hip)
 // Full-block key sums ksum[ceil(L/B), 128] (and optional means kbar) of blocks
 // first_block .. ceil(L/B) - 1 and, when tsum is given, the sum of each query's
-// last (possibly partial) block.
+// last (possibly partial) block. max_pool: per-dimension maxima instead of the
+// sums (ksum and tsum then hold max-pooled representatives; kbar, kb16 unused).
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
                              double* tsum, bool tails_only = false, uint16_t* kb16 = nullptr,
-                             int first_block = 0);
+                             int first_block = 0, bool max_pool = false);
 // MISA head routing with an exact result (route_fast.hip): bf16 block scores
 // with proven error bounds, then float64 settling of every head's maximum.
 // part: T * route_fast_parts(L, B, T) * 64 records of route_part_bytes();
@@ -74,11 +75,12 @@ hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const floa
 int route_chunks(int L, int B);
 // Router: heads[T,A] (ascending), optional r[T,H], optional HISA block scores
 // beta, and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed
-// in slot order (so scoring needs no head indirection).
+// in slot order (so scoring needs no head indirection). max_pool: ksum and tsum
+// hold max-pooled representatives (launch_block_sums with max_pool), used as given.
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
                         int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
                         const double* tsum, double* pmax, int32_t* heads, float* r_out,
-                        float* beta, int beta_ld, uint16_t* qr, float* wr);
+                        float* beta, int beta_ld, uint16_t* qr, float* wr, bool max_pool = false);
 // Pack q rows and weights of given heads [T,A] in slot order (ids outside [0,H)
 // give zero rows and weights).
 hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,

@@ -50,7 +50,9 @@ struct KeySlice {
 // (rl, dg) takes rows rl, rl + RL, ... and one 16-byte slice of dims. Four rows
 // per thread are loaded before any is added, so the loads overlap. Column sums
 // are left in red[r][d] (r < RL) for the caller to add up.
-template <bool FP8>
+// MAX: per-dimension maximum instead of the sum (max-pooled representatives;
+// exact, the widened values being exact in float64).
+template <bool FP8, bool MAX = false>
 struct RowSum {
   static constexpr int DPT = KeySlice<FP8>::DPT;
   static constexpr int NG = kHeadDim / DPT;  // slices per key
@@ -60,7 +62,7 @@ struct RowSum {
     const int tid = threadIdx.x, dg = tid % NG, rl = tid / NG;
     double acc[DPT];
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) acc[e] = 0.0;
+    for (int e = 0; e < DPT; ++e) acc[e] = MAX ? -__builtin_huge_val() : 0.0;
     constexpr int U = 4;
     for (int sb = s0 + rl; sb < s1; sb += RL * U) {
       u32x4 v[U];
@@ -79,8 +81,15 @@ struct RowSum {
       for (int u = 0; u < U; ++u) {
         double x[DPT];
         KeySlice<FP8>::widen(v[u], sc[u], x);
+        if constexpr (MAX) {
+          if (sb + RL * u < s1) {
 #pragma unroll
-        for (int e = 0; e < DPT; ++e) acc[e] += x[e];
+            for (int e = 0; e < DPT; ++e) acc[e] = x[e] > acc[e] ? x[e] : acc[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < DPT; ++e) acc[e] += x[e];
+        }
       }
     }
 #pragma unroll
@@ -93,13 +102,15 @@ struct RowSum {
 // block b = [b*B, min((b+1)*B, L)) in float64, and (optional) kbar = ksum /
 // count rounded once to float32. Workgroups [M, M+T): tsum[t,:] = sum of the
 // keys of query t's last block [(M_t-1)*B, n_t), possibly partial; zero when
-// the query sees no key. b_base = M computes the query tails only.
-template <bool FP8>
+// the query sees no key. b_base = M computes the query tails only. MAX: the
+// per-dimension maxima of the same keys instead of their sums (max-pooled
+// block representatives; no kbar or kb16), zero for a query with no key.
+template <bool FP8, bool MAX>
 __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* kscale, int L,
                                                     int B, int M, double* ksum, float* kbar,
                                                     uint16_t* kb16, const int32_t* pos, double* tsum,
                                                     int b_base) {
-  constexpr int RL = RowSum<FP8>::RL;
+  constexpr int RL = RowSum<FP8, MAX>::RL;
   __shared__ double red[RL][kHeadDim];
   const int b = (int)blockIdx.x + b_base;
   int s0, s1;
@@ -112,14 +123,19 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
     s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
     s1 = n;
   }
-  RowSum<FP8>::run(K, kscale, s0, s1, red);
+  RowSum<FP8, MAX>::run(K, kscale, s0, s1, red);
   const int tid = threadIdx.x;
   if (tid < kHeadDim) {
-    double s = 0.0;
+    double s = MAX ? -__builtin_huge_val() : 0.0;
 #pragma unroll
-    for (int r = 0; r < RL; ++r) s += red[r][tid];
+    for (int r = 0; r < RL; ++r) {
+      if constexpr (MAX) s = red[r][tid] > s ? red[r][tid] : s;
+      else s += red[r][tid];
+    }
+    if (MAX && s1 <= s0) s = 0.0;  // no key
     if (b < M) {
       ksum[(size_t)b * kHeadDim + tid] = s;
+      if constexpr (MAX) return;
       const double mean = s / (double)(s1 - s0);
       if (kbar) kbar[(size_t)b * kHeadDim + tid] = (float)mean;
       if (kb16) {
@@ -172,7 +188,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
                                                     int ntiles, const double* ksum,
                                                     const float* kbar, const double* tsum,
                                                     double* pmax, double* ptail, float* beta,
-                                                    int beta_ld) {
+                                                    int beta_ld, int max_pool) {
   __shared__ f64x2 kt[kRouteTile][kHeadDim / 2 + 1];  // padded rows
   __shared__ double bsum[4][kRouteTile];
   const int tile = blockIdx.x, tq0 = blockIdx.y * kRouteQG;
@@ -230,8 +246,8 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
       kt[i >> 6][i & 63] = x[u];
     }
   }
-  // full blocks hold sums (divide by B) or cached means (divide by 1)
-  const double div_full = kbar ? 1.0 : (double)B;
+  // full blocks hold sums (divide by B), cached means or maxima (divide by 1)
+  const double div_full = kbar || max_pool ? 1.0 : (double)B;
   __syncthreads();
   f64x2 kv[16];
 #pragma unroll
@@ -272,7 +288,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     }
     const f64x4 acc = acc0 + acc1;
     // this lane holds heads 16 wv + 4 e + g (e = 0..3) against block blk
-    const double cnt = tail ? (double)(n - (Mt - 1) * B) : div_full;
+    const double cnt = tail ? (max_pool ? 1.0 : (double)(n - (Mt - 1) * B)) : div_full;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0);
@@ -406,17 +422,18 @@ __global__ __launch_bounds__(64) void k_gather_heads(const uint16_t* q, const fl
 
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum, bool tails_only, uint16_t* kb16, int first_block) {
+                             double* tsum, bool tails_only, uint16_t* kb16, int first_block, bool max_pool) {
   const int M = (int)(((long long)L + B - 1) / B);
   const int base = tails_only ? M : (first_block < M ? first_block : M);
   const int grid = M - base + (tsum ? T : 0);
   if (grid == 0) return hipSuccess;
   const char* nm = tails_only ? "tail_sums" : "block_sums";
-  if (fp8)
-    return cx.launch(nm, k_block_sums<true>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,
-                     kbar, kb16, pos, tsum, base);
-  return cx.launch(nm, k_block_sums<false>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,
-                   kbar, kb16, pos, tsum, base);
+#define MISA_SUMS_LAUNCH(F8, MX)                                                                    \
+  cx.launch(nm, k_block_sums<F8, MX>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,            \
+            MX ? nullptr : kbar, MX ? nullptr : kb16, pos, tsum, base)
+  if (max_pool) return fp8 ? MISA_SUMS_LAUNCH(true, true) : MISA_SUMS_LAUNCH(false, true);
+  return fp8 ? MISA_SUMS_LAUNCH(true, false) : MISA_SUMS_LAUNCH(false, false);
+#undef MISA_SUMS_LAUNCH
 }
 
 int route_chunks(int L, int B) {
@@ -428,7 +445,7 @@ int route_chunks(int L, int B) {
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
                         int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
                         const double* tsum, double* pmax, int32_t* heads, float* r_out,
-                        float* beta, int beta_ld, uint16_t* qr, float* wr) {
+                        float* beta, int beta_ld, uint16_t* qr, float* wr, bool max_pool) {
   if (T == 0) return hipSuccess;
   const int nt = route_chunks(L, B);
   double* ptail = pmax + (size_t)T * nt * kWave;
@@ -440,7 +457,7 @@ hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, 
   const dim3 grid(nt, (T + qg - 1) / qg);
 #define MISA_ROUTE_LAUNCH(BETA, QG)                                                                \
   cx.launch("route_mfma", k_route_mfma<BETA, QG>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt, ksum, \
-            kbar, tsum, pmax, ptail, beta, beta_ld)
+            kbar, tsum, pmax, ptail, beta, beta_ld, max_pool ? 1 : 0)
   if (beta)
     e = qg == 8 ? MISA_ROUTE_LAUNCH(true, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(true, 2) : MISA_ROUTE_LAUNCH(true, 1));
   else

@@ -20,7 +20,8 @@ def _declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = _declared_functions()
-    assert {"misa_route", "misa_score_topk", "misa_hier_topk", "hisa_topk", "misa_hisa_topk"} <= set(names)
+    assert {"misa_route", "misa_score_topk", "misa_hier_topk", "hisa_topk", "hisa_maxpool_topk",
+            "misa_hisa_topk"} <= set(names)
     lib = ctypes.CDLL(S.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in misa.h but not exported"
@@ -80,6 +81,10 @@ def test_parameter_validation():
     assert L.misa_hier_topk(ctypes.byref(p), 8, None, 15, 16, FAKE, FAKE, FAKE, 1 << 40, None) == -1
     assert L.hisa_topk(ctypes.byref(p), 0, 16, FAKE, FAKE, FAKE, 1 << 40, None) == -1
     assert L.hisa_topk(ctypes.byref(p), 4, 0, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+    assert L.hisa_maxpool_topk(ctypes.byref(p), 0, 16, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+    assert L.hisa_maxpool_topk(ctypes.byref(p), 4, 0, FAKE, FAKE, FAKE, 1 << 40, None) == -1
+    pk = _problem(kbar=FAKE)  # cached means do not apply to max pooling
+    assert L.hisa_maxpool_topk(ctypes.byref(pk), 4, 16, FAKE, FAKE, FAKE, 1 << 40, None) == -1
     mh = lambda A, m, k, heads=None: L.misa_hisa_topk(ctypes.byref(p), A, heads, m, k, FAKE, FAKE, FAKE,
                                                        1 << 40, None)
     assert mh(0, 4, 16) == -1

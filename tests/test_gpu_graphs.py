@@ -111,3 +111,15 @@ def test_graph_misa_hisa():
            torch.empty((T, k), dtype=torch.float32, device="cuda"))
     _replays_match(lambda: S.misa_hisa_topk(q, w, K, pos, B, A, m, k, ks, ws=ws, out=out),
                    lambda: S.misa_hisa_topk(q2, w2, K2, pos2, B, A, m, k, ks2))
+
+
+def test_graph_hisa_maxpool():
+    T, L, H, B, m, k = 16, 6000, 32, 128, 8, 300
+    q, w, K, ks, pos = _inputs(61, T, L, H, O.KDT_FP8, positions="decode")
+    q2, w2, K2, ks2, pos2 = _inputs(62, T, L, H, O.KDT_FP8, positions="random")
+    p = S.make_problem(q, w, K, pos, B, ks)
+    ws = _ws(S.workspace_bytes(p, S.OP_HISA_TOPK, m=m, k=k))
+    out = (torch.empty((T, k), dtype=torch.int32, device="cuda"),
+           torch.empty((T, k), dtype=torch.float32, device="cuda"))
+    _replays_match(lambda: S.hisa_maxpool_topk(q, w, K, pos, B, m, k, ks, ws=ws, out=out),
+                   lambda: S.hisa_maxpool_topk(q2, w2, K2, pos2, B, m, k, ks2))

@@ -267,15 +267,15 @@ HISA_CASES = [
 ]
 
 
-def check_hisa(inp, B, m, k, idx, sc, label="hisa"):
+def check_hisa(inp, B, m, k, idx, sc, label="hisa", pool="mean"):
     P = oracle_problem(inp, B)
     rtol = RTOL[kdtype(inp)]
-    res, blocks = O.hisa_topk(P, m, k)
+    res, blocks = O.hisa_topk(P, m, k, pool)
     allh = list(range(P.H))
     for t in range(P.T):
         n = P.n(t)
-        beta = O.hisa_block_scores(P, t)
-        rho = O.block_logits(P, t)
+        beta = O.hisa_block_scores(P, t, pool)
+        rho = O.block_logits(P, t) if pool == "mean" else P.q[t] @ O.block_maxima(P, t).T
         # the GPU forms beta in float64 and compares it in float32
         btol = 1e-6 * (np.abs(P.w[t])[:, None] * np.maximum(rho, 0)).sum(axis=0) + 1e-30
         sure_b, maybe_b = pool_bands(beta, blocks[t], btol)
@@ -294,6 +294,27 @@ def test_hisa_topk(case):
     q, w, K, ks, pos = to_gpu(inp)
     idx, sc = S.hisa_topk(q, w, K, pos, B, m, k, ks)
     check_hisa(inp, B, m, k, _np(idx), _np(sc))
+
+
+@pytest.mark.parametrize("case", HISA_CASES, ids=lambda c: f"T{c[1]}L{c[2]}H{c[3]}B{c[4]}m{c[5]}k{c[6]}kd{c[7]}")
+def test_hisa_maxpool_topk(case):
+    seed, T, L, H, B, m, k, kdt = case
+    inp = _case(seed + 100, T, L, H, kdt, positions="random" if L < 10000 else "decode", neg_scales=True)
+    q, w, K, ks, pos = to_gpu(inp)
+    idx, sc = S.hisa_maxpool_topk(q, w, K, pos, B, m, k, ks)
+    check_hisa(inp, B, m, k, _np(idx), _np(sc), label="hisa max-pool", pool="max")
+
+
+@pytest.mark.parametrize("kdt", [O.KDT_BF16, O.KDT_FP8])
+def test_hisa_maxpool_token_blocks_is_hisa_bitwise(kdt):
+    # B = 1: each block's maximum and mean are its one key, so both entry points
+    # must return the same bits
+    inp = _case(47, 9, 700, 32, kdt, positions="random")
+    q, w, K, ks, pos = to_gpu(inp)
+    a = S.hisa_topk(q, w, K, pos, 1, 40, 25, ks)
+    b = S.hisa_maxpool_topk(q, w, K, pos, 1, 40, 25, ks)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 # ----------------------------------------------------------------- MISA inside HISA
