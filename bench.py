@@ -94,7 +94,7 @@ class Step:
         q, w, K, ks, pos = tensors
         p = S.make_problem(q, w, K, pos, wl.B, ks)
         op = {"hier": S.OP_HIER_TOPK, "misa": S.OP_SCORE_TOPK, "hisa": S.OP_HISA_TOPK,
-              "misa_hisa": S.OP_MISA_HISA_TOPK}[path]
+              "hisa_maxpool": S.OP_HISA_TOPK, "misa_hisa": S.OP_MISA_HISA_TOPK}[path]
         nbytes = S.workspace_bytes(p, op, A=self.A, kprime=wl.kprime, k=wl.k, m=wl.m)
         self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.out = (torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda"),
@@ -115,6 +115,8 @@ class Step:
         if self.path == "misa_hisa":
             return S.misa_hisa_topk(q, w, K, pos, wl.B, self.A, wl.m, wl.k, ks, ws=self.ws, out=self.out,
                                     kbar=kbar)
+        if self.path == "hisa_maxpool":
+            return S.hisa_maxpool_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out)
         return S.hisa_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out, kbar=kbar)
 
 
@@ -356,6 +358,7 @@ def main():
                                            ("misa_c5", "misa", "c5_glm5_hisa_128k", None, False),
                                            ("hisa_c5", "hisa", "c5_glm5_hisa_128k", None, False),
                                            ("hisa_c5_cached_block_means", "hisa", "c5_glm5_hisa_128k", None, True),
+                                           ("hisa_maxpool_c5", "hisa_maxpool", "c5_glm5_hisa_128k", None, False),
                                            ("misa_hisa_c5", "misa_hisa", "c5_glm5_hisa_128k", None, False),
                                            ("misa_c2", "misa", "c2_decode_batch", None, False),
                                            ("misa_c3_prefill", "misa", "c3_causal_prefill", None, False)]:
