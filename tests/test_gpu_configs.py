@@ -107,6 +107,8 @@ def test_c5_glm5_misa_and_hisa():
     _check_misa(inp, wl.B, wl.A, wl.k, _np(idx), _np(sc), label="c5 misa")
     idx, sc = S.hisa_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks)
     check_hisa(inp, wl.B, wl.m, wl.k, _np(idx), _np(sc), label="c5 hisa")
+    idx, sc = S.hisa_maxpool_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks)
+    check_hisa(inp, wl.B, wl.m, wl.k, _np(idx), _np(sc), label="c5 hisa max-pool", pool="max")
     heads_o, _ = O.route(P, wl.A)
     idx, sc = S.misa_hisa_topk(q, w, K, pos, wl.B, wl.A, wl.m, wl.k, ks)
     check_misa_hisa(inp, wl.B, wl.A, wl.m, wl.k, _np(idx), _np(sc), heads_o, label="c5 misa-hisa")
