@@ -263,7 +263,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // after which every lane of column col holds its head's record
 #pragma unroll
   for (int i = 0; i < QG; ++i) {
-    err[i] = arg[i] >= 0 ? ldexpf(err[i], -14) + 1e-30f : 0.f;
+    // (a block was scored when a leader exists or a bound product is positive: an
+    // overflowed screen can leave only NaN values, but |q|.|hi| is never NaN)
+    err[i] = arg[i] >= 0 || err[i] > 0.f ? ldexpf(err[i], -14) + 1e-30f : 0.f;
 #pragma unroll
     for (int off = 16; off < kWave; off <<= 1) {
       const float b2 = __shfl_xor(best[i], off, kWave), s2 = __shfl_xor(second[i], off, kWave);
@@ -312,6 +314,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const int n = nvis[i];
       const int Mt = (int)(((long long)n + B - 1) / B);
       double lo = -__builtin_huge_val(), hi = -__builtin_huge_val();
+      // a float term that overflowed certifies nothing (fmax would drop a NaN)
+      bool wide = !__builtin_isfinite(err[i]);
       if (arg[i] >= 0) {
         lo = (double)best[i] - (double)err[i];
         hi = (double)best[i] + (double)err[i];
@@ -339,12 +343,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         ab += __shfl_xor(ab, 32, kWave);
         const double cnt = (double)(n - (Mt - 1) * B);
         const double tv = (double)a / cnt, te = ldexp((double)ab / cnt, -14);
+        wide = wide || !(__builtin_isfinite(tv) && __builtin_isfinite(te));
         lo = fmax(lo, tv - te);
         hi = fmax(hi, tv + te);
       }
       const double mlo = fmax(lo, 0.0), mhi = fmax(hi, 0.0);
       const double wd = (double)wq[i];
       double rl = wd >= 0.0 ? wd * mlo : wd * mhi, rh = wd >= 0.0 ? wd * mhi : wd * mlo;
+      // such a head is settled exactly
+      if (wide) {
+        rl = -__builtin_huge_val();
+        rh = __builtin_huge_val();
+      }
       if (!active) rl = rh = -__builtin_huge_val();
       if (g == 0) {
         float fl = (float)rl, fh = (float)rh;  // outward: below rl, above rh
@@ -384,9 +394,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       // the head's candidate block, coded as -1 (no block can be positive), the
       // leader block, or the leader + 2^30 when the second best reaches the
       // leader's bound (every block evaluated)
+      // (a bound that overflowed leaves the screen unusable: every complete block)
+      const bool sure = __builtin_isfinite(err[i]);
       const float thr = best[i] - 2.f * err[i];
-      const bool use = arg[i] >= 0 && best[i] + err[i] >= 0.f;
-      const int c = use ? (arg[i] | (second[i] >= thr ? (1 << 30) : 0)) : -1;
+      const bool use = sure ? arg[i] >= 0 && best[i] + err[i] >= 0.f : nfull[i] > 0;
+      const int c = use ? (max(arg[i], 0) | (!sure || second[i] >= thr ? (1 << 30) : 0)) : -1;
       const int b = c >= 0 ? (c & ((1 << 30) - 1)) : 0;  // (block 0 when there is none: unused)
       const double rho = sum_groups(exact_part32(qa[i], st.ksum + (size_t)b * kHeadDim,
                                                  kbar ? kbar + (size_t)b * kHeadDim : nullptr, g)) / divb;
@@ -602,16 +614,21 @@ __global__ __launch_bounds__(256) void k_route_exact(const uint16_t* q, const fl
       b = fmaxf(b, pb[jj][h]);
       e = fmaxf(e, pe[jj][h]);
     }
-    // b + e < 0: every complete block has rho < 0 (nothing to evaluate)
-    gthr[h] = (active && nfull > 0 && b + e >= 0.f) ? b - 2.f * e : __builtin_huge_valf();
+    // b + e < 0: every complete block has rho < 0 (nothing to evaluate); a bound
+    // that overflowed (|q|.|hi| bounds every bf16 product) leaves the screen
+    // unusable: -inf asks for every complete block
+    const bool unsure = !__builtin_isfinite(e);
+    gthr[h] = (active && nfull > 0 && (unsure || b + e >= 0.f)) ? (unsure ? -__builtin_huge_valf() : b - 2.f * e)
+                                                               : __builtin_huge_valf();
   }
   __syncthreads();
   // candidate blocks of each head (thread j of head h scans ranges j, j+4, ...)
   const float thr = gthr[h];
+  const bool every = thr == -__builtin_huge_valf();
   for (int c = j; c < ntr; c += 4) {
     const RoutePart p = part[((size_t)t * ntr + c) * kWave + h];
-    if (p.arg >= 0 && p.best >= thr) {
-      const bool whole = p.second >= thr;
+    if (every ? c * range_blocks < nfull : (p.arg >= 0 && p.best >= thr)) {
+      const bool whole = every || p.second >= thr;
       const int first = whole ? c * range_blocks : p.arg;
       const int cnt = whole ? min(range_blocks, nfull - c * range_blocks) : 1;
       const int at = atomicAdd(&n_work, cnt);

@@ -151,6 +151,26 @@ def test_route_tied_heads_at_the_cut(kdt):
             assert sorted(heads[t]) == sorted(int(h) for h in heads_o[t]), f"row {t} (with r: {with_r})"
 
 
+@pytest.mark.parametrize("with_r", [False, True])
+@pytest.mark.parametrize("T,L", [(1500, 1500), (400, 3000)], ids=["one_range", "split"])
+def test_route_many_queries_float_overflow(T, L, with_r):
+    # keys near 2^120 with q near 2^12: the bf16 screen's float products overflow, so
+    # no interval or leader certifies anything and every head's complete blocks are
+    # settled in float64 (one range per workgroup, and the split form)
+    H, A, B = 64, 8, 16
+    inp = _case(33, T, L, H, O.KDT_BF16, positions="prefill")
+    to_bits = lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    from_bits = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    inp["K"] = to_bits(from_bits(inp["K"]) * np.float32(2.0 ** 118))
+    inp["q"] = to_bits(from_bits(inp["q"]) * np.float32(2.0 ** 12))
+    q, w, K, ks, pos = to_gpu(inp)
+    P = oracle_problem(inp, B)
+    out = S.route(q, w, K, pos, B, A, ks, with_r=with_r)
+    heads = _np(out[0] if with_r else out)
+    _, ill = check_heads(P, A, heads)
+    assert ill == 0
+
+
 # ----------------------------------------------------------------- MISA
 
 MISA_CASES = [
