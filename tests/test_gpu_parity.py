@@ -171,6 +171,19 @@ def test_route_many_queries_float_overflow(T, L, with_r):
     assert ill == 0
 
 
+@pytest.mark.parametrize("A", [1, 31, 32])
+def test_route_many_queries_extreme_A(A):
+    # the bf16 router's interval placement at the ends: one head kept, one left out, all kept
+    T, L, H, B = 1500, 1500, 32, 16
+    inp = _case(34, T, L, H, O.KDT_FP8, positions="prefill", neg_scales=True)
+    q, w, K, ks, pos = to_gpu(inp)
+    P = oracle_problem(inp, B)
+    for with_r in (False, True):
+        out = S.route(q, w, K, pos, B, A, ks, with_r=with_r)
+        _, ill = check_heads(P, A, _np(out[0] if with_r else out))
+        assert ill == 0
+
+
 # ----------------------------------------------------------------- MISA
 
 MISA_CASES = [
