@@ -212,6 +212,14 @@ def pairs_of(inp):
     return int(np.sum(np.minimum(np.maximum(inp["pos"].astype(np.int64) + 1, 0), inp["wl"].L)))
 
 
+def block_sums_bytes(wl):
+    """Compulsory HBM bytes of one block-pooling launch: every key once, the
+    float64 block sums written and each query's last-block sum written."""
+    per_key = 132 if wl.k_dtype == 1 else 256
+    M = -(-wl.L // wl.B)
+    return wl.L * per_key + M * 128 * 8 + wl.T * 128 * 8
+
+
 def score_kernel_bytes(wl, A):
     """Compulsory HBM bytes of one routed-scoring launch: every key once
     (128 code bytes + 4 scale bytes for fp8, 256 bytes for bf16), the routed
@@ -345,6 +353,12 @@ def main():
                      "algorithmic_bytes_per_launch": algo_bytes},
         "kernels_avg_ms": {k: v[0] for k, v in kms.items()},
     }
+    if kms["block_sums"][0]:
+        # the other full pass over the keys (the longest kernel of the step), same pricing
+        bs = block_sums_bytes(wl) / (kms["block_sums"][0] * 1e-3) / 1e9
+        rec["roofline_block_sums"] = {"bound": "hbm", "achieved": bs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": bs / HBM_PEAK_GBS, "kernel_avg_ms": kms["block_sums"][0],
+                                      "algorithmic_bytes_per_launch": block_sums_bytes(wl)}
     if not args.no_extra:
         extra, loaded = {}, {}
         steps = max(20, args.steps // 4)
