@@ -82,7 +82,8 @@ typedef enum misa_op {
   MISA_OP_HIER_TOPK = 2,
   MISA_OP_HISA_TOPK = 3,
   MISA_OP_BLOCK_MEANS = 4,
-  MISA_OP_MISA_HISA_TOPK = 5
+  MISA_OP_MISA_HISA_TOPK = 5,
+  MISA_OP_BLOCK_SCORES = 6
 } misa_op;
 
 /* One indexer problem. All pointers are device pointers. */
@@ -164,6 +165,18 @@ misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* head
  * those blocks with all H heads (I_all) and return the top-k. */
 misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* HISA Stage 1 block scores on their own (HISA write-up, section 3, Stage 1:
+ * the query is scored against the block representatives only):
+ *   beta[t * beta_ld + b] = sum_h w[t,h] * max(0, q[t,h] . Kbar_{t,b})
+ * for every visible block b < M_t of query t, formed in float64 and rounded
+ * once to float32; entries b >= M_t are not written. These are the values
+ * hisa_topk ranks for its top-m blocks (same kernel, same bits). beta is
+ * device memory [T, beta_ld] float32 with beta_ld >= ceil(L/B).
+ * Workspace: misa_workspace_bytes(p, MISA_OP_BLOCK_SCORES, ...). Cached means
+ * (p->kbar) are used as in hisa_topk. */
+misa_status hisa_block_scores(const misa_problem* p, float* beta, int64_t beta_ld, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* HISA with max-pooled block representatives (HISA write-up, limitations:
  * max pooling in place of mean pooling, listed as a possible improvement).

@@ -12,6 +12,7 @@ Entry points (same names as the C ABI in include/misa.h):
     score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None) -> (idx [T, k] i32, scores [T, k] f32)
     hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None) -> (idx, scores)
     hisa_topk(q, w, K, pos, B, m, k, k_scale=None)      -> (idx, scores)
+    hisa_block_scores(q, w, K, pos, B, k_scale=None)    -> beta [T, ceil(L/B)] f32
     misa_hisa_topk(q, w, K, pos, B, A, m, k, k_scale=None, heads=None) -> (idx, scores)
 
 Inputs are CUDA (HIP) tensors: q [T,H,128] bfloat16 (or int16 bf16 bits),
@@ -29,7 +30,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmisa.so")
 
-OP_ROUTE, OP_SCORE_TOPK, OP_HIER_TOPK, OP_HISA_TOPK, OP_BLOCK_MEANS, OP_MISA_HISA_TOPK = 0, 1, 2, 3, 4, 5
+OP_ROUTE, OP_SCORE_TOPK, OP_HIER_TOPK, OP_HISA_TOPK, OP_BLOCK_MEANS, OP_MISA_HISA_TOPK, OP_BLOCK_SCORES = \
+    0, 1, 2, 3, 4, 5, 6
 KDT_BF16, KDT_FP8 = 0, 1
 STATUS = {0: "MISA_OK", -1: "MISA_ERR_INVALID_ARG", -2: "MISA_ERR_UNSUPPORTED",
           -3: "MISA_ERR_WORKSPACE", -4: "MISA_ERR_HIP"}
@@ -70,6 +72,7 @@ def lib() -> ctypes.CDLL:
             "misa_hier_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
             "hisa_topk": (i32, [P, i32, i32, vp, vp, vp, sz, vp]),
             "hisa_maxpool_topk": (i32, [P, i32, i32, vp, vp, vp, sz, vp]),
+            "hisa_block_scores": (i32, [P, vp, ctypes.c_int64, vp, sz, vp]),
             "misa_hisa_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
             "misa_status_str": (ctypes.c_char_p, [i32]),
             "misa_last_error": (ctypes.c_char_p, []),
@@ -226,6 +229,18 @@ def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, kbar=None)
     ws, n = _workspace(p, OP_HISA_TOPK, q.device, ws, m=m, k=k)
     _check(lib().hisa_topk(ctypes.byref(p), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n, _stream()))
     return idx, sc
+
+
+def hisa_block_scores(q, w, K, pos, B, k_scale=None, ws=None, kbar=None):
+    """HISA Stage 1 block scores beta [T, ceil(L/B)] float32; entries past a
+    query's visible blocks are -inf (filled here before the call; the library
+    writes only the visible blocks)."""
+    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+    M = -(-p.L // int(B))
+    beta = torch.full((p.T, M), float("-inf"), dtype=torch.float32, device=q.device)
+    ws, n = _workspace(p, OP_BLOCK_SCORES, q.device, ws)
+    _check(lib().hisa_block_scores(ctypes.byref(p), _ptr(beta), M, _ptr(ws), n, _stream()))
+    return beta
 
 
 def hisa_maxpool_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None):

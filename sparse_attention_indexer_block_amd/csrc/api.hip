@@ -121,6 +121,7 @@ static Plan make_plan(const misa_problem* p, int op, int A, int kprime, int k, i
       pl.ksum = bp.take((size_t)ceil_div(L, p->B) * 128 * 8);
       break;
     case MISA_OP_ROUTE:
+    case MISA_OP_BLOCK_SCORES:
       plan_route(bp, pl, p);
       break;
     case MISA_OP_SCORE_TOPK:
@@ -437,6 +438,7 @@ size_t misa_workspace_bytes(const misa_problem* p, int32_t op, int32_t A, int32_
       if (A < 1 || A > p->H || m < 1 || k < 1) return 0;
       break;
     case MISA_OP_BLOCK_MEANS:
+    case MISA_OP_BLOCK_SCORES:
       break;
     default:
       return 0;
@@ -572,6 +574,20 @@ misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx,
   MISA_TRY(check_ws(pl, ws, ws_bytes));
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
   return run_hisa(cx, p, pl, ws, k, idx, scores, false);
+}
+
+misa_status hisa_block_scores(const misa_problem* p, float* beta, int64_t beta_ld, void* ws,
+                              size_t ws_bytes, void* stream) {
+  MISA_TRY(check_problem(p, true));
+  const long long M = ((long long)p->L + p->B - 1) / p->B;
+  if (beta_ld < M || beta_ld > (1ll << 30))
+    return fail(MISA_ERR_INVALID_ARG, "beta_ld = %lld must lie in [ceil(L/B) = %lld, 2^30]", (long long)beta_ld, M);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(beta, "beta"));
+  const Plan pl = make_plan(p, MISA_OP_BLOCK_SCORES, 1, 1, 1, 1);
+  MISA_TRY(check_ws(pl, ws, ws_bytes));
+  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
+  return run_route(cx, p, pl, ws, 1, nullptr, nullptr, beta, (int)beta_ld);
 }
 
 misa_status hisa_maxpool_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,

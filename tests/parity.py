@@ -15,7 +15,6 @@ score tolerance, everything integer is compared exactly):
 from __future__ import annotations
 
 import numpy as np
-import torch
 
 import oracle as O
 
@@ -24,6 +23,7 @@ ABS = 2.0 ** -16
 
 
 def to_gpu(inp, device="cuda"):
+    import torch
     q = torch.from_numpy(inp["q"].view(np.int16)).to(device)
     w = torch.from_numpy(inp["w"]).to(device)
     if inp["k_scale"] is not None:

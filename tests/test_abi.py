@@ -152,3 +152,14 @@ def test_profile_api_without_gpu():
     assert S.lib().misa_profile_reset() == 0
     ms, n = S.profile_read("")
     assert (ms, n) == (0.0, 0)
+
+
+def test_block_scores_validation():
+    L = S.lib()
+    p = _problem()
+    M = (1024 + 127) // 128
+    assert L.hisa_block_scores(ctypes.byref(p), FAKE, M - 1, FAKE, 1 << 40, None) == -1   # beta_ld < ceil(L/B)
+    assert L.hisa_block_scores(ctypes.byref(p), None, M, FAKE, 1 << 40, None) == -1       # beta NULL
+    assert L.hisa_block_scores(ctypes.byref(p), FAKE, M, FAKE, 16, None) == -3            # workspace too small
+    assert L.misa_workspace_bytes(ctypes.byref(p), S.OP_BLOCK_SCORES, 1, 1, 1, 1) == \
+        L.misa_workspace_bytes(ctypes.byref(p), S.OP_ROUTE, 1, 1, 1, 1)
