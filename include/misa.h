@@ -160,6 +160,29 @@ misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* head
                            int32_t k, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* Size in bytes of the library's static device scratch (see
+ * misa_hier_topk_noalloc). */
+#define MISA_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* misa_hier_topk for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same arguments, results, validation and errors as
+ * misa_hier_topk, except that there is no workspace argument: the scratch is
+ * a static device array of MISA_STATIC_SCRATCH_BYTES bytes inside the library
+ * (one copy per GPU, held from the library's first use on that GPU until the
+ * process ends). The call allocates and frees nothing.
+ *   - A problem whose scratch need (misa_workspace_bytes(p, MISA_OP_HIER_TOPK,
+ *     A, kprime, k, 1)) exceeds MISA_STATIC_SCRATCH_BYTES is rejected with
+ *     MISA_ERR_WORKSPACE before anything is enqueued (decode batches up to
+ *     T = 16 queries over 131,072 keys fit).
+ *   - Every call on one GPU shares that GPU's scratch and leaves its own
+ *     contents there. Calls ordered on one stream are safe; calls that may
+ *     overlap on one GPU (different streams, or threads enqueuing
+ *     concurrently) race on the scratch and give undefined results.
+ *   - The device is the calling thread's current device. */
+misa_status misa_hier_topk_noalloc(const misa_problem* p, int32_t A, const int32_t* heads, int32_t kprime,
+                                   int32_t k, int32_t* idx, float* scores, void* stream);
+
 /* HISA (HISA write-up, section 3, Stage 1 and Stage 2): keep the top-m blocks
  * of each query by beta (ties to the lower block), score the visible tokens of
  * those blocks with all H heads (I_all) and return the top-k. */

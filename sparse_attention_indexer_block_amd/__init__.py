@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/misa.h):
     route(q, w, K, pos, B, A, k_scale=None, with_r=False) -> heads [T, A] i32 (, r [T, H] f32)
     score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None) -> (idx [T, k] i32, scores [T, k] f32)
     hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None) -> (idx, scores)
+    hier_topk_noalloc(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None) -> (idx, scores)
     hisa_topk(q, w, K, pos, B, m, k, k_scale=None)      -> (idx, scores)
     hisa_block_scores(q, w, K, pos, B, k_scale=None)    -> beta [T, ceil(L/B)] f32
     misa_hisa_topk(q, w, K, pos, B, A, m, k, k_scale=None, heads=None) -> (idx, scores)
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
             "misa_route": (i32, [P, i32, vp, vp, vp, sz, vp]),
             "misa_score_topk": (i32, [P, i32, vp, i32, vp, vp, vp, sz, vp]),
             "misa_hier_topk": (i32, [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]),
+            "misa_hier_topk_noalloc": (i32, [P, i32, vp, i32, i32, vp, vp, vp]),
             "hisa_topk": (i32, [P, i32, i32, vp, vp, vp, sz, vp]),
             "hisa_maxpool_topk": (i32, [P, i32, i32, vp, vp, vp, sz, vp]),
             "hisa_block_scores": (i32, [P, vp, ctypes.c_int64, vp, sz, vp]),
@@ -221,6 +223,24 @@ def hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, ws=None, 
     _check(lib().misa_hier_topk(ctypes.byref(p), A, _ptr(heads), kprime, k, _ptr(idx), _ptr(sc),
                                 _ptr(ws), n, _stream()))
     return idx, sc
+
+
+def hier_topk_noalloc(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, out=None, kbar=None):
+    """misa_hier_topk_noalloc: hier_topk with the library's static device
+    scratch instead of a workspace (nothing is allocated by the call; pass
+    `out` to allocate nothing here either)."""
+    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+    if heads is not None:
+        _dev(heads, "heads")
+        if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):
+            raise ValueError("heads must be int32 [T, A]")
+    idx, sc = out if out is not None else _outputs(p, k, q.device)
+    _check(lib().misa_hier_topk_noalloc(ctypes.byref(p), A, _ptr(heads), kprime, k, _ptr(idx), _ptr(sc),
+                                        _stream()))
+    return idx, sc
+
+
+STATIC_SCRATCH_BYTES = 32 << 20  # MISA_STATIC_SCRATCH_BYTES
 
 
 def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, kbar=None):

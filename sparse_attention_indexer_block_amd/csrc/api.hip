@@ -411,6 +411,91 @@ static misa_status run_hisa(const LaunchCtx& cx, const misa_problem* p, const Pl
   return run_topk(cx, tf, pl, ws, ncmax);
 }
 
+static misa_status check_hier_args(const misa_problem* p, int A, const int32_t* heads, int kprime, int k,
+                                   int32_t* idx, float* scores) {
+  MISA_TRY(check_problem(p, true));
+  if (A < 1 || A > p->H) return fail(MISA_ERR_INVALID_ARG, "A = %d must lie in [1, H = %d]", A, p->H);
+  if (k < 1) return fail(MISA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
+  if (kprime < k) return fail(MISA_ERR_INVALID_ARG, "kprime = %d must be >= k = %d", kprime, k);
+  if (p->T == 0) return MISA_OK;
+  MISA_TRY(check_out(idx, "idx"));
+  MISA_TRY(check_out(scores, "scores"));
+  if (heads && !aligned(heads, 4)) return fail(MISA_ERR_INVALID_ARG, "heads must be 4-byte aligned");
+  return MISA_OK;
+}
+
+// MISA-dagger (MISA technical summary, "Variante Jerarquica"): routed scores,
+// top-k' candidates, all-head rescoring of the candidates, top-k.
+static misa_status run_hier(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws, int A,
+                            const int32_t* heads, int kprime, int k, int32_t* idx, float* scores) {
+  int nmm = 0;
+  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads, &nmm));
+  int32_t* cand = at<int32_t>(ws, pl.cand);
+  int32_t* ncand = at<int32_t>(ws, pl.ncand);
+  const int kc = kprime < p->L ? kprime : p->L;  // candidates kept per query
+  // coarse stage: top-k' of the routed scores (indices only)
+  TopkArgs ta = topk_args(p);
+  ta.S = at<float>(ws, pl.S);
+  ta.S_ld = pl.S_ld;
+  ta.k = kc;
+  ta.out_idx = cand;
+  ta.out_ld = pl.cand_ld;
+  ta.out_count = ncand;
+  MISA_TRY(run_topk(cx, ta, pl, ws, p->L, nmm));
+  // fine stage: all H heads rescore the candidates, then top-k
+  ScoreArgs sa = score_args(p);
+  sa.cand = cand;
+  sa.cand_ld = pl.cand_ld;
+  sa.cand_max = kc;
+  sa.ncand = ncand;
+  sa.S = at<float>(ws, pl.S2);
+  sa.S_ld = pl.S2_ld;
+  HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "rerank scoring");
+  TopkArgs tb = topk_args(p);
+  tb.S = at<float>(ws, pl.S2);
+  tb.S_ld = pl.S2_ld;
+  tb.row_n = ncand;
+  tb.row_idx = cand;
+  tb.idx_ld = pl.cand_ld;
+  tb.k = k;
+  tb.out_idx = idx;
+  tb.out_score = scores;
+  tb.out_ld = k;
+  return run_topk(cx, tb, pl, ws, kc);
+}
+
+// ---------------------------------------------------------------- static scratch
+
+// Device memory for misa_hier_topk_noalloc, which takes no workspace: one copy
+// of this array lives on every GPU the library runs on, from the code
+// object's load until the process ends. Host code never uses the array's name
+// as an address (on the host it is only a stand-in); the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kStaticScratchBytes = MISA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+static misa_status static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MISA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || !aligned(ptr, 256)) return fail(MISA_ERR_HIP, "static scratch has no usable device address");
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MISA_OK;
+}
+
 }  // namespace misa
 
 using namespace misa;
@@ -515,51 +600,25 @@ misa_status misa_score_topk(const misa_problem* p, int32_t A, const int32_t* hea
 misa_status misa_hier_topk(const misa_problem* p, int32_t A, const int32_t* heads, int32_t kprime,
                            int32_t k, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
                            void* stream) {
-  MISA_TRY(check_problem(p, true));
-  if (A < 1 || A > p->H) return fail(MISA_ERR_INVALID_ARG, "A = %d must lie in [1, H = %d]", A, p->H);
-  if (k < 1) return fail(MISA_ERR_INVALID_ARG, "k = %d must be >= 1", k);
-  if (kprime < k) return fail(MISA_ERR_INVALID_ARG, "kprime = %d must be >= k = %d", kprime, k);
+  MISA_TRY(check_hier_args(p, A, heads, kprime, k, idx, scores));
   if (p->T == 0) return MISA_OK;
-  MISA_TRY(check_out(idx, "idx"));
-  MISA_TRY(check_out(scores, "scores"));
-  if (heads && !aligned(heads, 4)) return fail(MISA_ERR_INVALID_ARG, "heads must be 4-byte aligned");
   const Plan pl = make_plan(p, MISA_OP_HIER_TOPK, A, kprime, k, 1);
   MISA_TRY(check_ws(pl, ws, ws_bytes));
-  const LaunchCtx cx{static_cast<hipStream_t>(stream)};
-  int nmm = 0;
-  MISA_TRY(run_routed_scores(cx, p, pl, ws, A, heads, &nmm));
-  int32_t* cand = at<int32_t>(ws, pl.cand);
-  int32_t* ncand = at<int32_t>(ws, pl.ncand);
-  const int kc = kprime < p->L ? kprime : p->L;  // candidates kept per query
-  // coarse stage: top-k' of the routed scores (indices only)
-  TopkArgs ta = topk_args(p);
-  ta.S = at<float>(ws, pl.S);
-  ta.S_ld = pl.S_ld;
-  ta.k = kc;
-  ta.out_idx = cand;
-  ta.out_ld = pl.cand_ld;
-  ta.out_count = ncand;
-  MISA_TRY(run_topk(cx, ta, pl, ws, p->L, nmm));
-  // fine stage: all H heads rescore the candidates, then top-k
-  ScoreArgs sa = score_args(p);
-  sa.cand = cand;
-  sa.cand_ld = pl.cand_ld;
-  sa.cand_max = kc;
-  sa.ncand = ncand;
-  sa.S = at<float>(ws, pl.S2);
-  sa.S_ld = pl.S2_ld;
-  HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "rerank scoring");
-  TopkArgs tb = topk_args(p);
-  tb.S = at<float>(ws, pl.S2);
-  tb.S_ld = pl.S2_ld;
-  tb.row_n = ncand;
-  tb.row_idx = cand;
-  tb.idx_ld = pl.cand_ld;
-  tb.k = k;
-  tb.out_idx = idx;
-  tb.out_score = scores;
-  tb.out_ld = k;
-  return run_topk(cx, tb, pl, ws, kc);
+  return run_hier(LaunchCtx{static_cast<hipStream_t>(stream)}, p, pl, ws, A, heads, kprime, k, idx, scores);
+}
+
+misa_status misa_hier_topk_noalloc(const misa_problem* p, int32_t A, const int32_t* heads, int32_t kprime,
+                                   int32_t k, int32_t* idx, float* scores, void* stream) {
+  MISA_TRY(check_hier_args(p, A, heads, kprime, k, idx, scores));
+  if (p->T == 0) return MISA_OK;
+  const Plan pl = make_plan(p, MISA_OP_HIER_TOPK, A, kprime, k, 1);
+  if (pl.total > kStaticScratchBytes)
+    return fail(MISA_ERR_WORKSPACE,
+                "this problem needs %zu bytes of scratch; the library's static scratch holds %zu "
+                "(use misa_hier_topk with a caller workspace)", pl.total, (size_t)kStaticScratchBytes);
+  void* ws = nullptr;
+  MISA_TRY(static_scratch(&ws));
+  return run_hier(LaunchCtx{static_cast<hipStream_t>(stream)}, p, pl, ws, A, heads, kprime, k, idx, scores);
 }
 
 misa_status hisa_topk(const misa_problem* p, int32_t m, int32_t k, int32_t* idx, float* scores,

@@ -163,3 +163,12 @@ def test_block_scores_validation():
     assert L.hisa_block_scores(ctypes.byref(p), FAKE, M, FAKE, 16, None) == -3            # workspace too small
     assert L.misa_workspace_bytes(ctypes.byref(p), S.OP_BLOCK_SCORES, 1, 1, 1, 1) == \
         L.misa_workspace_bytes(ctypes.byref(p), S.OP_ROUTE, 1, 1, 1, 1)
+
+
+def test_noalloc_rejects_oversized_problems_before_any_gpu_call():
+    L = S.lib()
+    p = _problem(T=64, L=1 << 21, k_dtype=1, k_scale=FAKE)
+    assert L.misa_workspace_bytes(ctypes.byref(p), S.OP_HIER_TOPK, 8, 8192, 2048, 1) > S.STATIC_SCRATCH_BYTES
+    st = L.misa_hier_topk_noalloc(ctypes.byref(p), 8, None, 8192, 2048, FAKE, FAKE, None)
+    assert st == -3 and b"static scratch" in L.misa_last_error()
+    assert L.misa_hier_topk_noalloc(ctypes.byref(_problem()), 8, None, 100, 200, FAKE, FAKE, None) == -1  # k' < k
