@@ -22,9 +22,10 @@ that the library records around each launch, in a second timed pass.
 Secondary lines repeat the protocol for the other workloads, for the dense
 indexer (A = H) as the comparator, and for the steady state of a decode loop
 in which the block means of the keys are cached (computed once per input copy,
-outside the timed region): each timed step brings the cache's last block up to
-date (the block a new key lands in) and each call pools only the queries' own
-last blocks.
+outside the timed region): each call pools only the queries' own last blocks,
+which the cache never stands in for, so the cache changes only when a block
+completes (once every B keys); that refresh (block_means_update of one block)
+is timed on its own and reported beside the cached lines.
 """
 from __future__ import annotations
 
@@ -104,9 +105,10 @@ class Step:
         q, w, K, ks, pos = tensors[:5]
         kbar = tensors[5] if len(tensors) > 5 else None  # cached block means
         wl, S = self.wl, self.S
-        if kbar is not None:
-            # a decode step appends the newest key: bring the cache's last block up to date
-            S.block_means_update(K, wl.B, kbar, kbar.shape[0] - 1, ks, ws=self.ws)
+        # cached block means (kbar) need no refresh inside a step: each query's own
+        # last block is always pooled from K, so only complete blocks before it are
+        # read from the cache, and a cache row changes only when its block
+        # completes (once every B appended keys; block_means_update, timed apart)
         if self.path == "hier":
             return S.hier_topk(q, w, K, pos, wl.B, self.A, wl.kprime, wl.k, ks, ws=self.ws, out=self.out,
                                kbar=kbar)
@@ -237,6 +239,26 @@ def score_kernel_bytes(wl, A):
     return wl.L * per_key + wl.T * A * 128 * 2 + wl.T * wl.H * 4 + wl.T * 4
 
 
+def selection_bytes(wl, pairs):
+    """Compulsory bytes of the MISA-dagger selections of one step: the routed
+    score rows read once and the k' candidate indices written (first stage),
+    then the candidates' indices and scores read and the k outputs written."""
+    return 4 * pairs + 4 * wl.T * wl.kprime + 8 * wl.T * wl.kprime + 8 * wl.T * wl.k
+
+
+def gather_bytes(wl):
+    """Compulsory bytes of the rerank: every candidate's key row (and scale)
+    once, all heads' q rows and weights, the reranked scores written."""
+    per_key = 132 if wl.k_dtype == 1 else 256
+    return wl.T * wl.kprime * per_key + wl.T * wl.H * (256 + 4) + wl.T * wl.kprime * 4
+
+
+def step_bytes_compulsory(wl):
+    """Compulsory bytes of a whole step: the keys once, q, w, pos, outputs."""
+    per_key = 132 if wl.k_dtype == 1 else 256
+    return wl.L * per_key + wl.T * wl.H * (256 + 4) + wl.T * 4 + wl.T * wl.k * 8
+
+
 _CPU = {}
 
 
@@ -302,6 +324,64 @@ def cpu_baseline(inp, wl, budget_s=15.0):
                       f"(one BLAS thread each) in {dt:.1f} s, including worker start-up and input decoding"}
 
 
+def stream_floor(byte_counts, grid=1024, min_rotation=600 << 20):
+    """Floor of one pass over N bytes on this device, timed like the indexer's
+    kernels: a plain 16-byte-load read kernel (libmisa_probe.so) over input
+    copies rotated so that they exceed the caches, with kernel-stamped HIP
+    events per launch, and as a chain of launches replayed in a HIP graph;
+    plus an empty kernel both ways (the fixed cost of any launch)."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_indexer_block_amd", "libmisa_probe.so"))
+    lib.probe_read_stamped.restype = ctypes.c_int
+    lib.probe_read_stamped.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]
+    lib.probe_read_launch.restype = ctypes.c_int
+    lib.probe_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def stamped(ptrs, n16, n):
+        arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs) if ptrs else (ctypes.c_void_p * 1)()
+        ms = (ctypes.c_float * n)()
+        torch.cuda.synchronize()
+        rc = lib.probe_read_stamped(arr, max(1, len(ptrs)), n16, grid, n, ctypes.c_void_p(out.data_ptr()), ms, stream)
+        if rc != 0:
+            raise RuntimeError(f"stream probe failed ({rc})")
+        return [x * 1e3 for x in ms]
+
+    def graphed(ptrs, n16, reps=3):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for p_ in ptrs:
+                lib.probe_read_launch(ctypes.c_void_p(p_), n16, grid, ctypes.c_void_p(out.data_ptr()), st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(ptrs))
+
+    res = {"grid": grid, "empty_stamped_us": float(np.median(stamped([], 0, 40))),
+           "empty_graph_us": graphed([0] * 64, 0), "reads": []}
+    for nbytes in byte_counts:
+        n16 = -(-int(nbytes) // 16)
+        nb = max(4, -(-min_rotation // (n16 * 16)))
+        bufs = [torch.full((n16 * 16,), i & 0xFF, dtype=torch.uint8, device="cuda") for i in range(nb)]
+        ptrs = [b.data_ptr() for b in bufs]
+        st = stamped(ptrs, n16, 2 * nb)[nb:]          # second pass over the rotation
+        gr = graphed(ptrs, n16)
+        res["reads"].append({"bytes": int(nbytes), "stamped_us": float(np.median(st)), "graph_us": gr,
+                             "stamped_gbs": nbytes / (np.median(st) * 1e-6) / 1e9, "graph_gbs": nbytes / (gr * 1e-6) / 1e9})
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
 def traffic_from_profiles(kernel_tag):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 PMC
     summaries, or None when they are missing or the kernel source changed."""
@@ -326,6 +406,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (scale for HBM byte counters)")
+    ap.add_argument("--stream-floor", action="store_true",
+                    help="only time the streaming-read floor for the decode workloads' byte counts")
     ap.add_argument("--only", default=None, metavar="PATH:WORKLOAD",
                     help="time one secondary line only (e.g. misa:c3_causal_prefill) and print it; "
                          "for profiling")
@@ -348,6 +430,14 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return
     S.lib()
+    if args.stream_floor:
+        import synth
+        counts = {nm: score_kernel_bytes(synth.CONFIGS[nm], synth.CONFIGS[nm].A)
+                  for nm in ("c2_decode_batch", "c4_hier_decode_128k", "c5_glm5_hisa_128k")}
+        fl = stream_floor(sorted(set(counts.values())))
+        fl["workload_bytes"] = counts
+        print(json.dumps({"stream_floor": fl}), flush=True)
+        return
     if args.only:
         path, nm = args.only.split(":")
         w1, i1, t1 = load_inputs(nm)
@@ -361,15 +451,32 @@ def main():
     name = "c4_hier_decode_128k"
     wl, inp, tensors = load_inputs(name)
     pairs = pairs_of(inp)
+    fams = ["score_keys", "score_gather", "route_mfma", "route_select", "block_sums", "topk_rows", "topk_hist",
+            "topk_count", "topk_emit"]
     ms, kms, pct = time_path(S, "hier", wl, tensors, args.steps, args.warmup, use_graphs=not args.eager,
-                             kernel=["score_keys", "score_gather", "route_mfma", "route_select",
-                                     "block_sums", "topk"])
+                             kernel=fams)
     value = pairs / (ms * 1e-3)
 
     score_ms, score_n = kms["score_keys"]
     algo_bytes = score_kernel_bytes(wl, wl.A)
     achieved = algo_bytes / (score_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles("score_keys")
+    floor = stream_floor([algo_bytes])
+    fr = floor["reads"][0]
+    # per-step milliseconds of each kernel family (launch averages times launches per step)
+    per_step = {k: (v[0] * v[1] / args.steps if v[0] else 0.0) for k, v in kms.items()}
+    sel_ms = sum(per_step[k] for k in ("topk_rows", "topk_hist", "topk_count", "topk_emit"))
+    sel_bytes = selection_bytes(wl, pairs)
+    gat_bytes = gather_bytes(wl)
+    step_bytes = step_bytes_compulsory(wl)
+
+    def line(bytes_, ms_, **kw):
+        a = bytes_ / (ms_ * 1e-3) / 1e9 if ms_ else None
+        d = {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": a / HBM_PEAK_GBS if a else None, "ms": ms_, "algorithmic_bytes": bytes_}
+        d.update(kw)
+        return d
+
     rec = {
         "metric": "indexer query-key pairs/sec incl. top-k at L=128K; % of HBM/MFMA roofline",
         "value": value,
@@ -396,15 +503,22 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel_avg_ms": score_ms, "kernel_launches": score_n,
-                     "algorithmic_bytes_per_launch": algo_bytes},
+                     "algorithmic_bytes_per_launch": algo_bytes,
+                     # a plain read of the same bytes, timed the same way: the floor one pass can reach
+                     "stream_floor_ms": fr["stamped_us"] * 1e-3, "vs_stream_floor": score_ms / (fr["stamped_us"] * 1e-3)},
         "kernels_avg_ms": {k: v[0] for k, v in kms.items()},
+        "kernels_ms_per_step": per_step,
+        "stream_floor": floor,
+        "rooflines": {
+            "block_sums": line(block_sums_bytes(wl), per_step["block_sums"], kernel="block pooling, K once"),
+            "score_keys": line(algo_bytes, per_step["score_keys"], kernel="routed scoring, K once"),
+            "selection": line(sel_bytes, sel_ms, kernel="top-k' of the score rows + top-k of the candidates",
+                              bytes_rule="4*sum(n_t) + 4*T*k' read-write of the k' stage; 8*T*k' + 8*T*k of the final"),
+            "rerank_gather": line(gat_bytes, per_step["score_gather"], kernel="all-head rescoring of the candidates"),
+            "step": line(step_bytes, ms, kernel="whole step (graph replay)",
+                         bytes_rule="K once + q + w + pos + outputs"),
+        },
     }
-    if kms["block_sums"][0]:
-        # the other full pass over the keys (the longest kernel of the step), same pricing
-        bs = block_sums_bytes(wl) / (kms["block_sums"][0] * 1e-3) / 1e9
-        rec["roofline_block_sums"] = {"bound": "hbm", "achieved": bs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": bs / HBM_PEAK_GBS, "kernel_avg_ms": kms["block_sums"][0],
-                                      "algorithmic_bytes_per_launch": block_sums_bytes(wl)}
     if not args.no_extra:
         extra, loaded = {}, {}
         steps = max(20, args.steps // 4)
@@ -446,6 +560,21 @@ def main():
             del t2
         loaded.clear()
         torch.cuda.empty_cache()
+        # the cache refresh a decode loop pays once every B keys: one block recomputed
+        q4, w4, K4, ks4, pos4 = tensors
+        kb4 = S.block_means(K4, wl.B, ks4)
+        wsu = torch.empty(S.workspace_bytes(S.make_problem(None, None, K4, None, wl.B, ks4), S.OP_BLOCK_MEANS),
+                          dtype=torch.uint8, device="cuda")
+        S.profile_reset()
+        S.profile_enable(True)
+        for _ in range(20):
+            S.block_means_update(K4, wl.B, kb4, kb4.shape[0] - 1, ks4, ws=wsu)
+        torch.cuda.synchronize()
+        S.profile_enable(False)
+        tu, nu = S.profile_read("block_sums")
+        S.profile_reset()
+        extra["cache_refresh_one_block_ms"] = {"kernel_avg_ms": tu / max(1, nu),
+                                               "amortized_per_decode_step_ms": tu / max(1, nu) / wl.B}
         dense = extra["dense_dsa_c4"]["pairs_per_s"]
         extra["misa_over_dense_dsa_c4"] = extra["misa_c4"]["pairs_per_s"] / dense
         extra["misa_cached_block_means_over_dense_dsa_c4"] = \

@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmisa.so")
+PROBE_LIB = os.path.join(HERE, "libmisa_probe.so")  # benchmark's streaming-floor probe
 SOURCES = ["route_kernels.hip", "route_fast.hip", "score_kernels.hip", "topk_kernels.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -53,6 +54,13 @@ def build(jobs: int = 4) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    # the benchmark's streaming-floor probe: a library of its own
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *CFLAGS, "-shared", os.path.join(CSRC, "stream_probe.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -104,7 +104,7 @@ static void plan_route(Bump& bp, Plan& pl, const misa_problem* p) {
   const int M = ceil_div(p->L, p->B);
   pl.ksum = bp.take((size_t)M * 128 * 8);
   pl.tsum = bp.take((size_t)p->T * 128 * 8);
-  pl.pmax = bp.take((size_t)p->T * (route_chunks(p->L, p->B) + 1) * 64 * 8);  // tile maxima + last block
+  pl.pmax = bp.take((size_t)p->T * 64 * 8);  // per-head maxima of the router (float64 bits)
   if (route_fast_wins(p->L, p->B, p->T)) {
     pl.kb16 = bp.take((size_t)M * 2 * 128 * 2);
     pl.part = bp.take((size_t)p->T * route_fast_parts(p->L, p->B, p->T) * 64 * route_part_bytes());
@@ -252,18 +252,21 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   const bool fp8 = p->k_dtype == MISA_K_FP8_E4M3FN;
   double* ksum = at<double>(ws, pl.ksum);
   double* tsum = at<double>(ws, pl.tsum);
-  double* pmax = at<double>(ws, pl.pmax);
   // many queries: a bf16 MFMA pass over hi/lo block means, settled in float64 where it is
   // ambiguous; few queries: every block's rho in float64 directly
   const bool fast = !beta && route_fast_wins(p->L, p->B, p->T);
   uint16_t* kb16 = fast ? at<uint16_t>(ws, pl.kb16) : nullptr;
+  // per-head maxima for the head selection (not needed for block scores alone);
+  // the block-sum kernel clears them before the router raises them
+  unsigned long long* rmax = (!fast && !beta) ? at<unsigned long long>(ws, pl.pmax) : nullptr;
+  if (rmax && sums_ready) return fail(MISA_ERR_HIP, "internal: router maxima need the block-sum pass");
   // with cached block means only each query's last block is pooled here
   if (!sums_ready)
     HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
-                              p->kbar != nullptr, kb16, 0, max_pool),
+                              p->kbar != nullptr, kb16, 0, max_pool, rmax, rmax ? p->T * 64 : 0),
             "block sums");
   if (!fast) {
-    HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, pmax,
+    HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, rmax,
                          heads, r, beta, beta_ld, qr, wr, max_pool),
             "router");
   } else {

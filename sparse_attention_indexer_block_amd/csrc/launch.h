@@ -58,7 +58,8 @@ inline long long padded_ld(long long n) { return ((n + 127) / 128) * 128; }
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
                              double* tsum, bool tails_only = false, uint16_t* kb16 = nullptr,
-                             int first_block = 0, bool max_pool = false);
+                             int first_block = 0, bool max_pool = false,
+                             unsigned long long* zero = nullptr, int zero_n = 0);
 // MISA head routing with an exact result (route_fast.hip): bf16 block scores
 // with proven error bounds, then float64 settling of every head's maximum.
 // part: T * route_fast_parts(L, B, T) * 64 records of route_part_bytes();
@@ -71,15 +72,18 @@ hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const floa
                               int T, int H, int L, int B, int A, const double* ksum, const uint16_t* kb16,
                               const float* kbar, const double* tsum, void* part, int32_t* heads,
                               float* r_out, uint16_t* qr, float* wr);
-// Router tiles of 16 blocks; the pmax workspace holds T * (route_chunks + 1) * 64 doubles.
+// Router tiles of 16 blocks.
 int route_chunks(int L, int B);
-// Router: heads[T,A] (ascending), optional r[T,H], optional HISA block scores
-// beta, and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed
-// in slot order (so scoring needs no head indirection). max_pool: ksum and tsum
-// hold max-pooled representatives (launch_block_sums with max_pool), used as given.
+// Router: per-head maxima max_b ReLU(rho) into rmax[T,64] (float64 bit
+// patterns, zero on entry: launch_block_sums clears them) when rmax is set;
+// then, when heads or r_out is set, heads[T,A] (ascending), optional r[T,H]
+// and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed in
+// slot order (so scoring needs no head indirection). Optional HISA block
+// scores beta. max_pool: ksum and tsum hold max-pooled representatives
+// (launch_block_sums with max_pool), used as given.
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
                         int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
-                        const double* tsum, double* pmax, int32_t* heads, float* r_out,
+                        const double* tsum, unsigned long long* rmax, int32_t* heads, float* r_out,
                         float* beta, int beta_ld, uint16_t* qr, float* wr, bool max_pool = false);
 // Pack q rows and weights of given heads [T,A] in slot order (ids outside [0,H)
 // give zero rows and weights).

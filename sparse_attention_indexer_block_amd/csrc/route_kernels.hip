@@ -105,13 +105,17 @@ struct RowSum {
 // the query sees no key. b_base = M computes the query tails only. MAX: the
 // per-dimension maxima of the same keys instead of their sums (max-pooled
 // block representatives; no kbar or kb16), zero for a query with no key.
+// Workgroup 0 also clears zero[0, zero_n) (the router's per-head maxima,
+// which the router kernel raises with atomic maxima).
 template <bool FP8, bool MAX>
 __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* kscale, int L,
                                                     int B, int M, double* ksum, float* kbar,
                                                     uint16_t* kb16, const int32_t* pos, double* tsum,
-                                                    int b_base) {
+                                                    int b_base, unsigned long long* zero, int zero_n) {
   constexpr int RL = RowSum<FP8, MAX>::RL;
   __shared__ double red[RL][kHeadDim];
+  if (zero && blockIdx.x == 0)
+    for (int i = (int)threadIdx.x; i < zero_n; i += 256) zero[i] = 0ull;
   const int b = (int)blockIdx.x + b_base;
   int s0, s1;
   if (b < M) {
@@ -158,11 +162,13 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
 // takes four head dims; lane l feeds head (A) and block (B) l % 16 with dims
 // [32(l/16), 32(l/16) + 32), one per step, so its operands are contiguous.
 // The result D[row][col] sits at lane col + 16 * (row % 4), element row / 4.
-// Writes, per (t, tile, h), max over the tile's full blocks of ReLU(rho)
-// (zero for tiles past the query's blocks); the tile holding query t's last
-// (possibly partial) block also writes that block's rho to ptail[t, h]. With
-// WITH_BETA it writes the HISA block score beta(t,b) = sum_h w[t,h] ReLU(rho)
-// of every visible block.
+// Raises rmax[t, h] (float64 bit patterns, zero on entry) to the maximum of
+// ReLU(rho) over the tile's blocks, the query's last (possibly partial) block
+// included: every value is >= +0.0, where the order of the bit patterns as
+// unsigned integers is the order of the values, so a 64-bit atomic maximum
+// over all tiles leaves max_b ReLU(rho(t,h,b)) (rmax may be null: not
+// needed). With WITH_BETA it writes the HISA block score
+// beta(t,b) = sum_h w[t,h] ReLU(rho) of every visible block.
 constexpr int kRouteTile = 16;  // blocks per workgroup
 
 // max over the 16 lanes of each row of the wave (every lane gets its row's max)
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
                                                     const int32_t* pos, int T, int H, int L, int B,
                                                     int ntiles, const double* ksum,
                                                     const float* kbar, const double* tsum,
-                                                    double* pmax, double* ptail, float* beta,
+                                                    unsigned long long* rmax, float* beta,
                                                     int beta_ld, int max_pool) {
   __shared__ f64x2 kt[kRouteTile][kHeadDim / 2 + 1];  // padded rows
   __shared__ double bsum[4][kRouteTile];
@@ -260,11 +266,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     if (i + 1 < kRouteQG) MISA_LOAD_Q(i + 1, (i + 1) & 1);
     const int n = n_q[i];
     const int Mt = (int)(((long long)n + B - 1) / B);
-    double* pm = pmax + ((size_t)t * ntiles + tile) * kWave;
-    if (b0 >= Mt) {  // uniform: no block of this tile is visible
-      if (tid < kWave) pm[tid] = 0.0;
-      continue;
-    }
+    if (b0 >= Mt) continue;  // uniform: no block of this tile is visible
     const bool valid = blk < Mt;
     const bool tail = blk == Mt - 1;
     // B operand: the block sums, or this query's own sum for its last block
@@ -289,14 +291,15 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     const f64x4 acc = acc0 + acc1;
     // this lane holds heads 16 wv + 4 e + g (e = 0..3) against block blk
     const double cnt = tail ? (max_pool ? 1.0 : (double)(n - (Mt - 1) * B)) : div_full;
+    if (rmax) {
+      unsigned long long* rm = rmax + (size_t)t * kWave + kRouteTile * wv + g;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0);
-      if (col == 0) pm[kRouteTile * wv + 4 * e + g] = m / div_full;
-    }
-    if (tail) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ptail[(size_t)t * kWave + kRouteTile * wv + 4 * e + g] = acc[e] / cnt;
+      for (int e = 0; e < 4; ++e) {
+        const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0) / div_full;
+        if (col == 0 && m > 0.0) atomicMax(rm + 4 * e, (unsigned long long)__double_as_longlong(m));
+        const double v = acc[e] / cnt;  // the last block: its own count of keys
+        if (tail && v > 0.0) atomicMax(rm + 4 * e, (unsigned long long)__double_as_longlong(v));
+      }
     }
     if constexpr (WITH_BETA) {
       double part = 0.0;
@@ -322,24 +325,19 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
 #undef MISA_LOAD_Q
 
 // Final router step, 256 threads per query: r(t,h) = w[t,h] * max_b ReLU(rho)
-// over the tile maxima and the last block, then the first A heads under
-// (-r, h). heads[t,:] is written in ascending head order; with qr the routed q
+// from the reduced maxima rmax, then the first A heads under (-r, h). heads[t,:] is written in ascending head order; with qr the routed q
 // rows and weights are packed in the same order for the scoring kernel. Every
 // global read is issued up front (none depends on another).
-__global__ __launch_bounds__(256) void k_route_select(const uint16_t* q, const float* w,
-                                                     const int32_t* pos, int H, int L, int B, int A,
-                                                     int ntiles, const double* pmax,
-                                                     const double* ptail, int32_t* heads,
+__global__ __launch_bounds__(256) void k_route_select(const uint16_t* q, const float* w, int H, int A,
+                                                     const unsigned long long* rmax, int32_t* heads,
                                                      float* r_out, uint16_t* qr, float* wr) {
-  __shared__ double part[4][kWave];
   __shared__ double rs[kWave];
   __shared__ int rank_part[4][kWave];
   __shared__ u32x4 qs[kWave * kHeadDim / 8];  // q[t] as 16-byte words
   const int t = blockIdx.x, tid = threadIdx.x, h = tid & 63, j = tid >> 6;
-  const int n = visible_len(pos[t], L);
   const bool active = h < H;
   const float wt = active ? w[(size_t)t * H + h] : 0.f;
-  const double rho_tail = ptail[(size_t)t * kWave + h];
+  const double m = __longlong_as_double((long long)rmax[(size_t)t * kWave + h]);
   if (qr) {
     const u32x4* src = reinterpret_cast<const u32x4*>(q + (size_t)t * H * kHeadDim);
     const int nw = H * kHeadDim / 8;
@@ -347,29 +345,8 @@ __global__ __launch_bounds__(256) void k_route_select(const uint16_t* q, const f
     for (int u = 0; u < 4; ++u)
       if (tid + 256 * u < nw) qs[tid + 256 * u] = src[tid + 256 * u];
   }
-  const double* pm = pmax + (size_t)t * ntiles * kWave + h;
-  double m = 0.0;
-  constexpr int U = 16;
-  for (int c0 = j; c0 < ntiles; c0 += 4 * U) {
-    double v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 4 * u;
-      v[u] = c < ntiles ? pm[(size_t)c * kWave] : 0.0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) m = v[u] > m ? v[u] : m;
-  }
-  part[j][h] = m;
-  __syncthreads();
-  const int Mt = (int)(((long long)n + B - 1) / B);
-  double r = 0.0;
   if (j == 0) {
-    m = part[0][h];
-#pragma unroll
-    for (int jj = 1; jj < 4; ++jj) m = part[jj][h] > m ? part[jj][h] : m;
-    if (Mt > 0) m = rho_tail > m ? rho_tail : m;
-    r = active ? (double)wt * m + 0.0 : -__builtin_huge_val();
+    const double r = active ? (double)wt * m + 0.0 : -__builtin_huge_val();
     if (r_out && active) r_out[(size_t)t * H + h] = (float)r;
     rs[h] = r;
   }
@@ -422,7 +399,8 @@ __global__ __launch_bounds__(64) void k_gather_heads(const uint16_t* q, const fl
 
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum, bool tails_only, uint16_t* kb16, int first_block, bool max_pool) {
+                             double* tsum, bool tails_only, uint16_t* kb16, int first_block, bool max_pool,
+                             unsigned long long* zero, int zero_n) {
   const int M = (int)(((long long)L + B - 1) / B);
   const int base = tails_only ? M : (first_block < M ? first_block : M);
   const int grid = M - base + (tsum ? T : 0);
@@ -430,7 +408,7 @@ hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* ks
   const char* nm = tails_only ? "tail_sums" : "block_sums";
 #define MISA_SUMS_LAUNCH(F8, MX)                                                                    \
   cx.launch(nm, k_block_sums<F8, MX>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,            \
-            MX ? nullptr : kbar, MX ? nullptr : kb16, pos, tsum, base)
+            MX ? nullptr : kbar, MX ? nullptr : kb16, pos, tsum, base, zero, zero_n)
   if (max_pool) return fp8 ? MISA_SUMS_LAUNCH(true, true) : MISA_SUMS_LAUNCH(false, true);
   return fp8 ? MISA_SUMS_LAUNCH(true, false) : MISA_SUMS_LAUNCH(false, false);
 #undef MISA_SUMS_LAUNCH
@@ -444,11 +422,10 @@ int route_chunks(int L, int B) {
 
 hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
                         int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
-                        const double* tsum, double* pmax, int32_t* heads, float* r_out,
+                        const double* tsum, unsigned long long* rmax, int32_t* heads, float* r_out,
                         float* beta, int beta_ld, uint16_t* qr, float* wr, bool max_pool) {
   if (T == 0) return hipSuccess;
   const int nt = route_chunks(L, B);
-  double* ptail = pmax + (size_t)T * nt * kWave;
   hipError_t e;
   // one query per workgroup while that leaves few workgroups per CU; past
   // that, groups of queries share each staged tile
@@ -457,16 +434,16 @@ hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, 
   const dim3 grid(nt, (T + qg - 1) / qg);
 #define MISA_ROUTE_LAUNCH(BETA, QG)                                                                \
   cx.launch("route_mfma", k_route_mfma<BETA, QG>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt, ksum, \
-            kbar, tsum, pmax, ptail, beta, beta_ld, max_pool ? 1 : 0)
+            kbar, tsum, rmax, beta, beta_ld, max_pool ? 1 : 0)
   if (beta)
     e = qg == 8 ? MISA_ROUTE_LAUNCH(true, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(true, 2) : MISA_ROUTE_LAUNCH(true, 1));
   else
     e = qg == 8 ? MISA_ROUTE_LAUNCH(false, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(false, 2) : MISA_ROUTE_LAUNCH(false, 1));
 #undef MISA_ROUTE_LAUNCH
   if (e != hipSuccess) return e;
-  if (!heads && !r_out) return hipSuccess;  // block scores only
-  return cx.launch("route_select", k_route_select, dim3(T), dim3(256), 0, q, w, pos, H, L, B, A, nt,
-                   (const double*)pmax, (const double*)ptail, heads, r_out, qr, wr);
+  if (!heads && !r_out) return hipSuccess;  // block scores, or maxima for the scoring kernel
+  return cx.launch("route_select", k_route_select, dim3(T), dim3(256), 0, q, w, H, A,
+                   (const unsigned long long*)rmax, heads, r_out, qr, wr);
 }
 
 hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,

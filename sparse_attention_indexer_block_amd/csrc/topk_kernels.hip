@@ -21,10 +21,10 @@
 namespace misa {
 
 constexpr int kLdsCap = 16384;     // items per row selected inside LDS
-constexpr int kChunk = 4096;       // items per workgroup in the long-row passes
-constexpr int kMaxChunks = 2048;   // chunks per long row (rows up to 2^23 items)
+constexpr int kChunk = 2048;       // items per workgroup in the long-row passes
+constexpr int kMaxChunks = 4096;   // chunks per long row (rows up to 2^23 items)
 constexpr int kBoundaryCap = 4096; // boundary-bin items resolved inside LDS
-constexpr int kCoarseBits = 12;
+constexpr int kCoarseBits = 10;
 constexpr int kCoarseBins = 1 << kCoarseBits;  // long rows: bins of the first pass
 constexpr int kFineBins = 2048;                  // rows in one workgroup
 constexpr int kListCap = 4096;     // survivors of the first radix digit kept in LDS
