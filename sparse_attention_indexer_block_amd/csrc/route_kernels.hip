@@ -49,16 +49,22 @@ struct KeySlice {
 // Sum of key rows [s0, s1) in float64, one workgroup of 256 threads; thread
 // (rl, dg) takes rows rl, rl + RL, ... and one 16-byte slice of dims. Four rows
 // per thread are loaded before any is added, so the loads overlap. Column sums
-// are left in red[r][d] (r < RL) for the caller to add up.
+// are left in red for the caller to add up: value e of slice dg of row group rl
+// sits at red[rl * kRedStride + e * NG + dg] (so one store instruction of a wave
+// covers contiguous doubles, and the padded row stride puts alternate row
+// groups on the other half of the LDS banks); column c of that layout holds
+// dim (c % NG) * DPT + c / NG.
 // MAX: per-dimension maximum instead of the sum (max-pooled representatives;
 // exact, the widened values being exact in float64).
+constexpr int kRedStride = kHeadDim + 8;  // doubles per row group of the reduction buffer
+
 template <bool FP8, bool MAX = false>
 struct RowSum {
   static constexpr int DPT = KeySlice<FP8>::DPT;
   static constexpr int NG = kHeadDim / DPT;  // slices per key
   static constexpr int RL = 256 / NG;        // rows in flight per pass
-  static __device__ __forceinline__ void run(const void* K, const float* kscale, int s0, int s1,
-                                             double (*red)[kHeadDim]) {
+  static __device__ __forceinline__ int dim_of(int c) { return (c % NG) * DPT + c / NG; }
+  static __device__ __forceinline__ void run(const void* K, const float* kscale, int s0, int s1, double* red) {
     const int tid = threadIdx.x, dg = tid % NG, rl = tid / NG;
     double acc[DPT];
 #pragma unroll
@@ -93,7 +99,7 @@ struct RowSum {
       }
     }
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) red[rl][dg * DPT + e] = acc[e];
+    for (int e = 0; e < DPT; ++e) red[rl * kRedStride + e * NG + dg] = acc[e];
     __syncthreads();
   }
 };
@@ -112,8 +118,9 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
                                                     int B, int M, double* ksum, float* kbar,
                                                     uint16_t* kb16, const int32_t* pos, double* tsum,
                                                     int b_base, unsigned long long* zero, int zero_n) {
-  constexpr int RL = RowSum<FP8, MAX>::RL;
-  __shared__ double red[RL][kHeadDim];
+  using RS = RowSum<FP8, MAX>;
+  constexpr int RL = RS::RL;
+  __shared__ double red[RL * kRedStride];
   if (zero && blockIdx.x == 0)
     for (int i = (int)threadIdx.x; i < zero_n; i += 256) zero[i] = 0ull;
   const int b = (int)blockIdx.x + b_base;
@@ -127,30 +134,33 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
     s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
     s1 = n;
   }
-  RowSum<FP8, MAX>::run(K, kscale, s0, s1, red);
+  RS::run(K, kscale, s0, s1, red);
   const int tid = threadIdx.x;
   if (tid < kHeadDim) {
+    // thread c adds column c of the row groups (contiguous LDS reads); it holds dim d
     double s = MAX ? -__builtin_huge_val() : 0.0;
 #pragma unroll
     for (int r = 0; r < RL; ++r) {
-      if constexpr (MAX) s = red[r][tid] > s ? red[r][tid] : s;
-      else s += red[r][tid];
+      const double x = red[r * kRedStride + tid];
+      if constexpr (MAX) s = x > s ? x : s;
+      else s += x;
     }
+    const int d = RS::dim_of(tid);
     if (MAX && s1 <= s0) s = 0.0;  // no key
     if (b < M) {
-      ksum[(size_t)b * kHeadDim + tid] = s;
+      ksum[(size_t)b * kHeadDim + d] = s;
       if constexpr (MAX) return;
       const double mean = s / (double)(s1 - s0);
-      if (kbar) kbar[(size_t)b * kHeadDim + tid] = (float)mean;
+      if (kbar) kbar[(size_t)b * kHeadDim + d] = (float)mean;
       if (kb16) {
         // bf16 hi / lo split of the mean for the router's fast pass
         uint32_t hi, lo;
         split_bf16(mean, hi, lo);
-        kb16[(size_t)b * 2 * kHeadDim + tid] = (uint16_t)hi;
-        kb16[(size_t)b * 2 * kHeadDim + kHeadDim + tid] = (uint16_t)lo;
+        kb16[(size_t)b * 2 * kHeadDim + d] = (uint16_t)hi;
+        kb16[(size_t)b * 2 * kHeadDim + kHeadDim + d] = (uint16_t)lo;
       }
     } else {
-      tsum[(size_t)(b - M) * kHeadDim + tid] = s;
+      tsum[(size_t)(b - M) * kHeadDim + d] = s;
     }
   }
 }

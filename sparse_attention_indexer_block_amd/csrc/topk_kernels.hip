@@ -28,7 +28,7 @@ constexpr int kCoarseBits = 10;
 constexpr int kCoarseBins = 1 << kCoarseBits;  // long rows: bins of the first pass
 constexpr int kFineBins = 2048;                  // rows in one workgroup
 constexpr int kListCap = 4096;     // survivors of the first radix digit kept in LDS
-constexpr int kRankCap = 128;      // lists this short are ranked pairwise instead of by digits
+constexpr int kRankCap = 512;      // lists this short are ranked pairwise instead of by digits
 
 template <int NT>
 struct RegShared {
