@@ -53,6 +53,8 @@ import numpy as np
 
 KDT_BF16 = 0
 KDT_FP8 = 1
+QDT_BF16 = 0
+QDT_FP8 = 1
 
 
 # ---------------------------------------------------------------- decoding
@@ -92,6 +94,15 @@ def dequant_keys(K, k_dtype: int, k_scale=None) -> np.ndarray:
     return codes * np.asarray(k_scale, dtype=np.float32).astype(np.float64)[:, None]
 
 
+def dequant_queries(q, q_dtype: int, q_scale=None) -> np.ndarray:
+    """Query values in float64: bf16 queries as decoded; fp8 queries are E4M3FN
+    codes times one fp32 scale per (query, head) (the product is exact)."""
+    if q_dtype == QDT_BF16:
+        return decode_bf16(q)
+    codes = decode_e4m3fn(q)
+    return codes * np.asarray(q_scale, dtype=np.float32).astype(np.float64)[:, :, None]
+
+
 class Problem:
     """Decoded inputs of one indexer call (float64 copies, exact).
 
@@ -99,10 +110,14 @@ class Problem:
     row b stands for the mean of block b wherever that block is complete and
     lies before the query's own last block (the router's block statistics are
     query independent there [MISA]); a query's last block is always pooled from
-    its visible keys."""
+    its visible keys.
 
-    def __init__(self, q_bits, w, K, pos, B, k_dtype=KDT_BF16, k_scale=None, kbar=None):
-        self.q = decode_bf16(q_bits)                                   # [T,H,d]
+    q is bf16 bits, or (q_dtype QDT_FP8) E4M3FN codes with q_scale [T,H]: the
+    value of q[t,h,i] is code * q_scale[t,h]; the definitions are unchanged."""
+
+    def __init__(self, q_bits, w, K, pos, B, k_dtype=KDT_BF16, k_scale=None, kbar=None,
+                 q_dtype=QDT_BF16, q_scale=None):
+        self.q = dequant_queries(q_bits, q_dtype, q_scale)             # [T,H,d]
         self.w = np.asarray(w, dtype=np.float32).astype(np.float64)   # [T,H]
         self.K = dequant_keys(K, k_dtype, k_scale)                     # [L,d]
         self.pos = np.asarray(pos, dtype=np.int64)

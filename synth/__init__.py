@@ -23,6 +23,8 @@ Encodings:
   and handed over as raw uint16 bit patterns.
 * fp8 keys are OCP E4M3FN bytes with one fp32 scale per token, scale = amax/448;
   values are clipped to +-448 before the cast so nothing saturates to NaN.
+* fp8 queries (q_fp8=True) are E4M3FN bytes with one fp32 scale per
+  (query, head) row, quantised the same way.
 """
 from __future__ import annotations
 
@@ -102,6 +104,20 @@ def quantize_keys_fp8(kf: np.ndarray):
     return codes, scale
 
 
+def quantize_queries_fp8(q32: np.ndarray):
+    """Per-(query, head) fp8 quantisation of q [T,H,d]: codes [T,H,d] uint8 and
+    scales [T,H] float32 (amax/448; 1.0 for an all-zero row)."""
+    T, H, d = q32.shape
+    codes, scale = quantize_keys_fp8(q32.reshape(T * H, d))
+    return codes.reshape(T, H, d), scale.reshape(T, H)
+
+
+def fp8_codes_to_f32(codes: np.ndarray) -> np.ndarray:
+    """E4M3FN bytes -> float32 (exact); used only to build needles."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float32).numpy()
+
+
 def positions_for(wl: Workload) -> np.ndarray:
     if wl.positions == "prefill":
         assert wl.T <= wl.L
@@ -141,11 +157,12 @@ def _needle_slots(rng, wl: Workload, pos: np.ndarray):
     return out
 
 
-def make_inputs(wl: Workload, seed: int = 0, T: Optional[int] = None):
+def make_inputs(wl: Workload, seed: int = 0, T: Optional[int] = None, q_fp8: bool = False):
     """Build one seeded problem.
 
     Returns a dict of numpy arrays:
-      q      [T,H,d] uint16 (bf16 bits)
+      q      [T,H,d] uint16 (bf16 bits), or uint8 E4M3FN codes with q_fp8
+      q_scale[T,H]   float32 per-(query, head) scale (q_fp8 only, else None)
       w      [T,H]   float32
       K      [L,d]   uint16 (bf16 bits) or uint8 (e4m3fn bytes)
       k_scale[L]     float32 (fp8 only, else None)
@@ -161,7 +178,12 @@ def make_inputs(wl: Workload, seed: int = 0, T: Optional[int] = None):
     pos = positions_for(wl)
 
     q32 = rq.standard_normal((wl.T, wl.H, wl.d), dtype=np.float32)
-    q_bits = encode_bf16(q32)
+    if q_fp8:
+        q_bits, q_scale = quantize_queries_fp8(q32)
+        qv = fp8_codes_to_f32(q_bits) * q_scale[:, :, None]
+    else:
+        q_bits, q_scale = encode_bf16(q32), None
+        qv = bf16_bits_to_f32(q_bits)
     w = (rw.standard_normal((wl.T, wl.H), dtype=np.float32) / np.float32(8.0)).astype(np.float32)
     kf = rk.standard_normal((wl.L, wl.d), dtype=np.float32)
     if wl.block_offsets > 0:
@@ -171,7 +193,6 @@ def make_inputs(wl: Workload, seed: int = 0, T: Optional[int] = None):
 
     needles = [[] for _ in range(wl.T)]
     if wl.needles > 0:
-        qv = bf16_bits_to_f32(q_bits)
         needles = _needle_slots(rn, wl, pos)
         for t, slots in enumerate(needles):
             hstar = int(np.argmax(w[t]))
@@ -187,16 +208,18 @@ def make_inputs(wl: Workload, seed: int = 0, T: Optional[int] = None):
         K, k_scale = quantize_keys_fp8(kf)
     else:
         K, k_scale = encode_bf16(kf), None
-    return {"q": q_bits, "w": w, "K": K, "k_scale": k_scale, "pos": pos,
+    return {"q": q_bits, "q_scale": q_scale, "w": w, "K": K, "k_scale": k_scale, "pos": pos,
             "needles": needles, "wl": wl}
 
 
 def random_small(seed: int, T: int, L: int, H: int, d: int = 128, k_dtype: int = KDT_BF16,
-                 positions: str = "random", w_scale: float = 0.125, int_grid: bool = False):
+                 positions: str = "random", w_scale: float = 0.125, int_grid: bool = False,
+                 q_fp8: bool = False):
     """Small randomised problems for sweeps and edge cases.
 
     positions: "random" (uniform in [0, L)), "decode" (last T), "prefill" (pos[t]=t, T<=L)
     int_grid: draw q, K and w from a small dyadic grid so exact ties are common.
+    q_fp8: q as E4M3FN codes with a per-(query, head) scale (inp["q_scale"]).
     """
     rng = np.random.default_rng(np.random.SeedSequence([seed, T, L, H, d, k_dtype]))
     if int_grid:
@@ -217,5 +240,9 @@ def random_small(seed: int, T: int, L: int, H: int, d: int = 128, k_dtype: int =
         K, k_scale = quantize_keys_fp8(kf)
     else:
         K, k_scale = encode_bf16(kf), None
-    return {"q": encode_bf16(q32), "w": w.astype(np.float32), "K": K, "k_scale": k_scale,
+    if q_fp8:
+        q, q_scale = quantize_queries_fp8(q32)
+    else:
+        q, q_scale = encode_bf16(q32), None
+    return {"q": q, "q_scale": q_scale, "w": w.astype(np.float32), "K": K, "k_scale": k_scale,
             "pos": pos, "needles": [[] for _ in range(T)]}

@@ -19,12 +19,23 @@ import numpy as np
 import oracle as O
 
 RTOL = {O.KDT_BF16: 2e-3, O.KDT_FP8: 1.5e-2}
+
+
+def rtol_of(inp):
+    """bf16 tolerance only when neither keys nor queries are fp8."""
+    fp8 = inp["k_scale"] is not None or inp.get("q_scale") is not None
+    return RTOL[O.KDT_FP8 if fp8 else O.KDT_BF16]
 ABS = 2.0 ** -16
 
 
 def to_gpu(inp, device="cuda"):
+    """(q, w, K, k_scale, pos) device tensors; fp8 queries come as uint8 codes
+    (their scales: q_scale_gpu)."""
     import torch
-    q = torch.from_numpy(inp["q"].view(np.int16)).to(device)
+    if inp.get("q_scale") is not None:
+        q = torch.from_numpy(inp["q"]).to(device)
+    else:
+        q = torch.from_numpy(inp["q"].view(np.int16)).to(device)
     w = torch.from_numpy(inp["w"]).to(device)
     if inp["k_scale"] is not None:
         K = torch.from_numpy(inp["K"]).to(device)
@@ -36,16 +47,25 @@ def to_gpu(inp, device="cuda"):
     return q, w, K, ks, pos
 
 
+def q_scale_gpu(inp, device="cuda"):
+    import torch
+    qs = inp.get("q_scale")
+    return None if qs is None else torch.from_numpy(qs).to(device)
+
+
 def oracle_problem(inp, B, rows=None):
     """Oracle problem of an input dict; an optional inp["kbar"] (float32 cached
-    block means) is passed through."""
+    block means) and inp["q_scale"] (fp8 queries) are passed through."""
     kdt = O.KDT_FP8 if inp["k_scale"] is not None else O.KDT_BF16
     kbar = inp.get("kbar")
+    qs = inp.get("q_scale")
+    qdt = O.QDT_FP8 if qs is not None else O.QDT_BF16
     if rows is None:
-        return O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], B, kdt, inp["k_scale"], kbar=kbar)
+        return O.Problem(inp["q"], inp["w"], inp["K"], inp["pos"], B, kdt, inp["k_scale"], kbar=kbar,
+                         q_dtype=qdt, q_scale=qs)
     rows = np.asarray(rows)
     return O.Problem(inp["q"][rows], inp["w"][rows], inp["K"], inp["pos"][rows], B, kdt, inp["k_scale"],
-                     kbar=kbar)
+                     kbar=kbar, q_dtype=qdt, q_scale=None if qs is None else qs[rows])
 
 
 def kdtype(inp):
