@@ -50,20 +50,28 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_FP8_PEAK_TFLOPS = 5000.0
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def load_inputs(name, seed=0):
-    log(f"generating {name}")
+def load_inputs(name, seed=0, q_fp8=False):
+    """(workload, host inputs, device tensors (q, w, K, k_scale, pos, q_scale));
+    q_fp8: queries as E4M3FN codes with per-(query, head) scales."""
+    log(f"generating {name}{' with fp8 queries' if q_fp8 else ''}")
     import torch
     import synth
     wl = synth.CONFIGS[name]
-    inp = synth.make_inputs(wl, seed=seed)
+    inp = synth.make_inputs(wl, seed=seed, q_fp8=q_fp8)
     dev = "cuda"
-    q = torch.from_numpy(inp["q"].view(np.int16)).to(dev)
+    if q_fp8:
+        q = torch.from_numpy(inp["q"]).to(dev)
+        qs = torch.from_numpy(inp["q_scale"]).to(dev)
+    else:
+        q = torch.from_numpy(inp["q"].view(np.int16)).to(dev)
+        qs = None
     w = torch.from_numpy(inp["w"]).to(dev)
     pos = torch.from_numpy(inp["pos"]).to(dev)
     if inp["k_scale"] is not None:
@@ -72,7 +80,7 @@ def load_inputs(name, seed=0):
     else:
         K = torch.from_numpy(inp["K"].view(np.int16)).to(dev)
         ks = None
-    return wl, inp, (q, w, K, ks, pos)
+    return wl, inp, (q, w, K, ks, pos, qs)
 
 
 def rotation_sets(tensors, min_bytes=600 << 20):
@@ -92,8 +100,8 @@ class Step:
         import torch
         self.S, self.path, self.wl = S, path, wl
         self.A = wl.A if A is None else A
-        q, w, K, ks, pos = tensors
-        p = S.make_problem(q, w, K, pos, wl.B, ks)
+        q, w, K, ks, pos, qs = tensors[:6]
+        p = S.make_problem(q, w, K, pos, wl.B, ks, None, qs)
         op = {"hier": S.OP_HIER_TOPK, "misa": S.OP_SCORE_TOPK, "hisa": S.OP_HISA_TOPK,
               "hisa_maxpool": S.OP_HISA_TOPK, "misa_hisa": S.OP_MISA_HISA_TOPK}[path]
         nbytes = S.workspace_bytes(p, op, A=self.A, kprime=wl.kprime, k=wl.k, m=wl.m)
@@ -102,8 +110,8 @@ class Step:
                     torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda"))
 
     def __call__(self, tensors):
-        q, w, K, ks, pos = tensors[:5]
-        kbar = tensors[5] if len(tensors) > 5 else None  # cached block means
+        q, w, K, ks, pos, qs = tensors[:6]
+        kbar = tensors[6] if len(tensors) > 6 else None  # cached block means
         wl, S = self.wl, self.S
         # cached block means (kbar) need no refresh inside a step: each query's own
         # last block is always pooled from K, so only complete blocks before it are
@@ -111,15 +119,16 @@ class Step:
         # completes (once every B appended keys; block_means_update, timed apart)
         if self.path == "hier":
             return S.hier_topk(q, w, K, pos, wl.B, self.A, wl.kprime, wl.k, ks, ws=self.ws, out=self.out,
-                               kbar=kbar)
+                               kbar=kbar, q_scale=qs)
         if self.path == "misa":
-            return S.score_topk(q, w, K, pos, wl.B, self.A, wl.k, ks, ws=self.ws, out=self.out, kbar=kbar)
+            return S.score_topk(q, w, K, pos, wl.B, self.A, wl.k, ks, ws=self.ws, out=self.out, kbar=kbar,
+                                q_scale=qs)
         if self.path == "misa_hisa":
             return S.misa_hisa_topk(q, w, K, pos, wl.B, self.A, wl.m, wl.k, ks, ws=self.ws, out=self.out,
-                                    kbar=kbar)
+                                    kbar=kbar, q_scale=qs)
         if self.path == "hisa_maxpool":
-            return S.hisa_maxpool_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out)
-        return S.hisa_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out, kbar=kbar)
+            return S.hisa_maxpool_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out, q_scale=qs)
+        return S.hisa_topk(q, w, K, pos, wl.B, wl.m, wl.k, ks, ws=self.ws, out=self.out, kbar=kbar, q_scale=qs)
 
 
 def time_path(S, path, wl, tensors, steps, warmup, use_graphs=True, A=None, kernel=None, cached=False):
@@ -211,9 +220,13 @@ def quality(S, path, wl, inp, tensors, A=None):
     """Selection quality beside speed (the pages report both), from the GPU's
     selections: see selection_quality."""
     import torch
-    q, w, K, ks, pos = tensors
+    q, w, K, ks, pos, qs = tensors
     idx = Step(S, path, wl, tensors, A=A)(tensors)[0]
-    dense = S.score_topk(q, w, K, pos, wl.B, wl.H, wl.k, ks)[0]
+    if qs is None:
+        dense = S.score_topk(q, w, K, pos, wl.B, wl.H, wl.k, ks)[0]
+    else:
+        # fp8 queries: the dense top-k as HISA keeping every block (m*B >= n is the dense indexer)
+        dense = S.hisa_topk(q, w, K, pos, wl.B, -(-wl.L // wl.B), wl.k, ks, q_scale=qs)[0]
     torch.cuda.synchronize()
     return selection_quality(idx.cpu().numpy(), dense.cpu().numpy(), inp["needles"])
 
@@ -230,13 +243,14 @@ def block_sums_bytes(wl):
     return wl.L * per_key + M * 128 * 8 + wl.T * 128 * 8
 
 
-def score_kernel_bytes(wl, A):
+def score_kernel_bytes(wl, A, q_fp8=False):
     """Compulsory HBM bytes of one routed-scoring launch: every key once
     (128 code bytes + 4 scale bytes for fp8, 256 bytes for bf16), the routed
-    q rows, the head weights and positions. Score rows written for the
-    selection are intermediate and not counted."""
+    q rows (128 code bytes for fp8 queries, 256 for bf16), the head weights
+    and positions. Score rows written for the selection are intermediate and
+    not counted."""
     per_key = 132 if wl.k_dtype == 1 else 256
-    return wl.L * per_key + wl.T * A * 128 * 2 + wl.T * wl.H * 4 + wl.T * 4
+    return wl.L * per_key + wl.T * A * (128 if q_fp8 else 256) + wl.T * wl.H * 4 + wl.T * 4
 
 
 def selection_bytes(wl, pairs):
@@ -526,6 +540,7 @@ def main():
         # keeps them; each step refreshes the last block), so only each query's own
         # last block is pooled per call
         for label, path, nm, A, cached in [("hier_c4_cached_block_means", "hier", name, None, True),
+                                           ("hier_c4_fp8q", "hier", name + "+fp8q", None, False),
                                            ("misa_c4", "misa", name, None, False),
                                            ("misa_c4_cached_block_means", "misa", name, None, True),
                                            ("dense_dsa_c4", "misa", name, 64, False),
@@ -534,15 +549,18 @@ def main():
                                            ("hisa_c5_cached_block_means", "hisa", "c5_glm5_hisa_128k", None, True),
                                            ("hisa_maxpool_c5", "hisa_maxpool", "c5_glm5_hisa_128k", None, False),
                                            ("misa_hisa_c5", "misa_hisa", "c5_glm5_hisa_128k", None, False),
+                                           ("misa_c5_fp8q", "misa", "c5_glm5_hisa_128k+fp8q", None, False),
+                                           ("hisa_c5_fp8q", "hisa", "c5_glm5_hisa_128k+fp8q", None, False),
                                            ("misa_c2", "misa", "c2_decode_batch", None, False),
                                            ("misa_c3_prefill", "misa", "c3_causal_prefill", None, False)]:
+            base, fp8q = nm.split("+")[0], nm.endswith("+fp8q")
             if nm == name:
                 w2, i2, t2 = wl, inp, tensors
             else:
                 if nm not in loaded:
                     loaded.clear()  # keep one secondary workload resident at a time
                     torch.cuda.empty_cache()
-                    loaded[nm] = load_inputs(nm)
+                    loaded[nm] = load_inputs(base, q_fp8=fp8q)
                 w2, i2, t2 = loaded[nm]
             st = steps if "c3" not in nm else 5
             m2, k2, pc2 = time_path(S, path, w2, t2, st, 2, use_graphs=not args.eager, A=A,
@@ -553,15 +571,22 @@ def main():
             if k2["score_keys"][0]:
                 flops = 2.0 * (A or w2.A) * 128 * p2
                 e["score_keys_tflops"] = flops / (k2["score_keys"][0] * 1e-3) / 1e12
-                e["score_keys_hbm_gbs"] = score_kernel_bytes(w2, A or w2.A) / (k2["score_keys"][0] * 1e-3) / 1e9
+                e["score_keys_hbm_gbs"] = score_kernel_bytes(w2, A or w2.A, fp8q) / (k2["score_keys"][0] * 1e-3) / 1e9
+                e["score_keys_hbm_frac"] = e["score_keys_hbm_gbs"] / HBM_PEAK_GBS
+                if fp8q:  # fp8 x fp8 matrix cores: their own peak
+                    e["score_keys_mfma_frac"] = e["score_keys_tflops"] / MFMA_FP8_PEAK_TFLOPS
+                    e["compute"] = "fp8 e4m3 q and K, v_mfma_scale_f32_16x16x128_f8f6f4 (fp32 accumulate)"
             if not cached and "c3" not in nm and A is None:
                 e["quality"] = quality(S, path, w2, i2, t2)
+            if path in ("hisa", "hier") and k2["score_gather"][0]:
+                gfl = 2.0 * w2.H * 128 * (w2.T * min(w2.kprime if path == "hier" else w2.m * w2.B, w2.L))
+                e["score_gather_tflops"] = gfl / (k2["score_gather"][0] * 1e-3) / 1e12
             extra[label] = e
             del t2
         loaded.clear()
         torch.cuda.empty_cache()
         # the cache refresh a decode loop pays once every B keys: one block recomputed
-        q4, w4, K4, ks4, pos4 = tensors
+        q4, w4, K4, ks4, pos4, _ = tensors
         kb4 = S.block_means(K4, wl.B, ks4)
         wsu = torch.empty(S.workspace_bytes(S.make_problem(None, None, K4, None, wl.B, ks4), S.OP_BLOCK_MEANS),
                           dtype=torch.uint8, device="cuda")

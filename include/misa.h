@@ -48,8 +48,16 @@
  *   - pos values outside [0, L) are clamped: pos < 0 gives a row with no
  *     visible key (all padding), pos >= L behaves as pos = L-1.
  *   - Supported on the GPU: d = 128; 1 <= H <= 64; 1 <= A <= H; B >= 1;
- *     q bf16; K bf16 or OCP E4M3FN with a per-token fp32 scale (any finite
+ *     q bf16, or OCP E4M3FN codes with a per-(query, head) fp32 scale;
+ *     K bf16 or OCP E4M3FN with a per-token fp32 scale (any finite scale
  *     value; the sign of a negative scale is honoured).
+ *   - fp8 queries (q_dtype MISA_Q_FP8_E4M3FN) need fp8 keys (the contraction
+ *     runs on fp8 x fp8 matrix cores) and decode-shaped batches wherever heads
+ *     are routed or keys are scored over the whole prefix (misa_route,
+ *     misa_score_topk, misa_hier_topk, misa_hisa_topk: T * A' <= 256 with A'
+ *     = A rounded up to a power of two >= 4, and the few-query router);
+ *     hisa_topk and hisa_maxpool_topk take any T. Otherwise
+ *     MISA_ERR_UNSUPPORTED.
  *   - Calls that share a workspace must be ordered on one stream; otherwise the
  *     library is stateless and reentrant.
  */
@@ -76,6 +84,11 @@ typedef enum misa_kdtype {
   MISA_K_FP8_E4M3FN = 1   /* K[L,d] as OCP E4M3FN bytes; value = code * k_scale[s] */
 } misa_kdtype;
 
+typedef enum misa_qdtype {
+  MISA_Q_BF16 = 0,        /* q[T,H,d] as bf16 bit patterns (uint16) */
+  MISA_Q_FP8_E4M3FN = 1   /* q[T,H,d] as OCP E4M3FN bytes; value = code * q_scale[t,h] */
+} misa_qdtype;
+
 typedef enum misa_op {
   MISA_OP_ROUTE = 0,
   MISA_OP_SCORE_TOPK = 1,
@@ -94,12 +107,14 @@ typedef struct misa_problem {
   int32_t L;               /* keys (>= 1) */
   int32_t B;               /* block size of the router / HISA blocks (>= 1) */
   int32_t k_dtype;         /* misa_kdtype */
-  const uint16_t* q;       /* [T,H,d] bf16 bits */
+  const void* q;           /* [T,H,d] bf16 bits, or E4M3FN bytes (q_dtype) */
   const float* w;          /* [T,H]   per-query head weights */
   const void* K;           /* [L,d]   shared indexer keys (bf16 bits or e4m3fn bytes) */
   const float* k_scale;    /* [L]     per-token scale, required iff k_dtype is fp8, else NULL */
   const int32_t* pos;      /* [T]     causal position of each query */
   const float* kbar;       /* [ceil(L/B),d] cached block means, or NULL (see below) */
+  int32_t q_dtype;         /* misa_qdtype (MISA_Q_BF16 for bf16 queries) */
+  const float* q_scale;    /* [T,H]   per-(query, head) scale, required iff q_dtype is fp8, else NULL */
 } misa_problem;
 
 /* Cached block means (kbar). When p->kbar is NULL every call pools the keys

@@ -31,6 +31,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmisa.so")
 
+QDT_BF16, QDT_FP8 = 0, 1
 OP_ROUTE, OP_SCORE_TOPK, OP_HIER_TOPK, OP_HISA_TOPK, OP_BLOCK_MEANS, OP_MISA_HISA_TOPK, OP_BLOCK_SCORES = \
     0, 1, 2, 3, 4, 5, 6
 KDT_BF16, KDT_FP8 = 0, 1
@@ -48,7 +49,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("L", ctypes.c_int32), ("B", ctypes.c_int32), ("k_dtype", ctypes.c_int32),
                 ("q", ctypes.c_void_p), ("w", ctypes.c_void_p), ("K", ctypes.c_void_p),
-                ("k_scale", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("kbar", ctypes.c_void_p)]
+                ("k_scale", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("kbar", ctypes.c_void_p),
+                ("q_dtype", ctypes.c_int32), ("q_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -112,9 +114,11 @@ def _dev(t: torch.Tensor, name: str):
 
 def make_problem(q: Optional[torch.Tensor], w: Optional[torch.Tensor], K: torch.Tensor,
                  pos: Optional[torch.Tensor], B: int, k_scale: Optional[torch.Tensor] = None,
-                 kbar: Optional[torch.Tensor] = None):
+                 kbar: Optional[torch.Tensor] = None, q_scale: Optional[torch.Tensor] = None):
     """Fill the C problem struct from tensors (no copies). `kbar` is an optional
-    float32 [ceil(L/B), d] tensor of cached block means (see block_means)."""
+    float32 [ceil(L/B), d] tensor of cached block means (see block_means).
+    q as uint8 / float8_e4m3fn codes means fp8 queries, with q_scale [T,H]
+    float32 (value = code * q_scale[t,h])."""
     _dev(K, "K")
     if K.dtype in (torch.uint8, torch.float8_e4m3fn):
         kdt = KDT_FP8
@@ -131,10 +135,21 @@ def make_problem(q: Optional[torch.Tensor], w: Optional[torch.Tensor], K: torch.
         raise ValueError(f"unsupported key dtype {K.dtype}")
     L, d = K.shape
     T, H = 0, 1
+    qdt = QDT_BF16
     if q is not None:
         _dev(q, "q"), _dev(w, "w"), _dev(pos, "pos")
-        if q.dtype not in (torch.bfloat16, torch.int16):
-            raise ValueError("q must be bfloat16 (or int16 bf16 bits)")
+        if q.dtype in (torch.uint8, torch.float8_e4m3fn):
+            qdt = QDT_FP8
+            if q_scale is None:
+                raise ValueError("fp8 queries need q_scale")
+            _dev(q_scale, "q_scale")
+            if q_scale.dtype != torch.float32 or tuple(q_scale.shape) != tuple(q.shape[:2]):
+                raise ValueError("q_scale must be float32 [T, H]")
+        elif q.dtype in (torch.bfloat16, torch.int16):
+            if q_scale is not None:
+                raise ValueError("q_scale is only for fp8 queries")
+        else:
+            raise ValueError("q must be bfloat16 (or int16 bf16 bits), or uint8 / float8_e4m3fn codes")
         if w.dtype != torch.float32 or pos.dtype != torch.int32:
             raise ValueError("w must be float32 and pos int32")
         T, H, dq = q.shape
@@ -145,7 +160,7 @@ def make_problem(q: Optional[torch.Tensor], w: Optional[torch.Tensor], K: torch.
         if kbar.dtype != torch.float32 or tuple(kbar.shape) != (-(-L // int(B)), d):
             raise ValueError("kbar must be float32 [ceil(L/B), d]")
     p = Problem(T, H, d, L, int(B), kdt, _ptr(q), _ptr(w), _ptr(K), _ptr(k_scale), _ptr(pos),
-                _ptr(kbar))
+                _ptr(kbar), qdt, _ptr(q_scale if qdt == QDT_FP8 else None))
     return p
 
 
@@ -184,8 +199,8 @@ def block_means_update(K, B, kbar, first_block, k_scale=None, ws=None):
     return kbar
 
 
-def route(q, w, K, pos, B, A, k_scale=None, with_r=False, ws=None, kbar=None):
-    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+def route(q, w, K, pos, B, A, k_scale=None, with_r=False, ws=None, kbar=None, q_scale=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar, q_scale)
     heads = torch.empty((p.T, A), dtype=torch.int32, device=q.device)
     r = torch.empty((p.T, p.H), dtype=torch.float32, device=q.device) if with_r else None
     ws, n = _workspace(p, OP_ROUTE, q.device, ws, A=A)
@@ -198,8 +213,8 @@ def _outputs(p, k, device):
             torch.empty((p.T, k), dtype=torch.float32, device=device))
 
 
-def score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None, ws=None, out=None, kbar=None):
-    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+def score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None, ws=None, out=None, kbar=None, q_scale=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar, q_scale)
     if heads is not None:
         _dev(heads, "heads")
         if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):
@@ -212,8 +227,8 @@ def score_topk(q, w, K, pos, B, A, k, k_scale=None, heads=None, ws=None, out=Non
 
 
 def hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, ws=None, out=None,
-              kbar=None):
-    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+              kbar=None, q_scale=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar, q_scale)
     if heads is not None:
         _dev(heads, "heads")
         if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):
@@ -225,11 +240,11 @@ def hier_topk(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, ws=None, 
     return idx, sc
 
 
-def hier_topk_noalloc(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, out=None, kbar=None):
+def hier_topk_noalloc(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, out=None, kbar=None, q_scale=None):
     """misa_hier_topk_noalloc: hier_topk with the library's static device
     scratch instead of a workspace (nothing is allocated by the call; pass
     `out` to allocate nothing here either)."""
-    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+    p = make_problem(q, w, K, pos, B, k_scale, kbar, q_scale)
     if heads is not None:
         _dev(heads, "heads")
         if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):
@@ -243,19 +258,19 @@ def hier_topk_noalloc(q, w, K, pos, B, A, kprime, k, k_scale=None, heads=None, o
 STATIC_SCRATCH_BYTES = 32 << 20  # MISA_STATIC_SCRATCH_BYTES
 
 
-def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, kbar=None):
-    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+def hisa_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, kbar=None, q_scale=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar, q_scale)
     idx, sc = out if out is not None else _outputs(p, k, q.device)
     ws, n = _workspace(p, OP_HISA_TOPK, q.device, ws, m=m, k=k)
     _check(lib().hisa_topk(ctypes.byref(p), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n, _stream()))
     return idx, sc
 
 
-def hisa_block_scores(q, w, K, pos, B, k_scale=None, ws=None, kbar=None):
+def hisa_block_scores(q, w, K, pos, B, k_scale=None, ws=None, kbar=None, q_scale=None):
     """HISA Stage 1 block scores beta [T, ceil(L/B)] float32; entries past a
     query's visible blocks are -inf (filled here before the call; the library
     writes only the visible blocks)."""
-    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+    p = make_problem(q, w, K, pos, B, k_scale, kbar, q_scale)
     M = -(-p.L // int(B))
     beta = torch.full((p.T, M), float("-inf"), dtype=torch.float32, device=q.device)
     ws, n = _workspace(p, OP_BLOCK_SCORES, q.device, ws)
@@ -263,16 +278,16 @@ def hisa_block_scores(q, w, K, pos, B, k_scale=None, ws=None, kbar=None):
     return beta
 
 
-def hisa_maxpool_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None):
-    p = make_problem(q, w, K, pos, B, k_scale)
+def hisa_maxpool_topk(q, w, K, pos, B, m, k, k_scale=None, ws=None, out=None, q_scale=None):
+    p = make_problem(q, w, K, pos, B, k_scale, None, q_scale)
     idx, sc = out if out is not None else _outputs(p, k, q.device)
     ws, n = _workspace(p, OP_HISA_TOPK, q.device, ws, m=m, k=k)
     _check(lib().hisa_maxpool_topk(ctypes.byref(p), m, k, _ptr(idx), _ptr(sc), _ptr(ws), n, _stream()))
     return idx, sc
 
 
-def misa_hisa_topk(q, w, K, pos, B, A, m, k, k_scale=None, heads=None, ws=None, out=None, kbar=None):
-    p = make_problem(q, w, K, pos, B, k_scale, kbar)
+def misa_hisa_topk(q, w, K, pos, B, A, m, k, k_scale=None, heads=None, ws=None, out=None, kbar=None, q_scale=None):
+    p = make_problem(q, w, K, pos, B, k_scale, kbar, q_scale)
     if heads is not None:
         _dev(heads, "heads")
         if heads.dtype != torch.int32 or tuple(heads.shape) != (p.T, A):

@@ -207,7 +207,15 @@ static misa_status check_problem(const misa_problem* p, bool need_queries) {
   if (!fp8 && p->k_scale) return fail(MISA_ERR_INVALID_ARG, "k_scale must be NULL for bf16 keys");
   if (p->k_scale && !aligned(p->k_scale, 4)) return fail(MISA_ERR_INVALID_ARG, "k_scale must be 4-byte aligned");
   if (p->kbar && !aligned(p->kbar, 16)) return fail(MISA_ERR_INVALID_ARG, "kbar must be 16-byte aligned");
+  if (p->q_dtype != MISA_Q_BF16 && p->q_dtype != MISA_Q_FP8_E4M3FN)
+    return fail(MISA_ERR_INVALID_ARG, "q_dtype = %d is not a misa_qdtype", p->q_dtype);
   if (need_queries && p->T > 0) {
+    const bool qf8 = p->q_dtype == MISA_Q_FP8_E4M3FN;
+    if (qf8 && !p->q_scale) return fail(MISA_ERR_INVALID_ARG, "q_scale is required for fp8 queries");
+    if (!qf8 && p->q_scale) return fail(MISA_ERR_INVALID_ARG, "q_scale must be NULL for bf16 queries");
+    if (qf8 && !aligned(p->q_scale, 4)) return fail(MISA_ERR_INVALID_ARG, "q_scale must be 4-byte aligned");
+    if (qf8 && !fp8)
+      return fail(MISA_ERR_UNSUPPORTED, "fp8 queries need fp8 keys (fp8 x fp8 matrix products)");
     if (!p->q || !p->w || !p->pos) return fail(MISA_ERR_INVALID_ARG, "q, w and pos must be non-NULL");
     if (!aligned(p->q, 16)) return fail(MISA_ERR_INVALID_ARG, "q must be 16-byte aligned");
     if (!aligned(p->w, 4) || !aligned(p->pos, 4)) return fail(MISA_ERR_INVALID_ARG, "w and pos must be 4-byte aligned");
@@ -260,17 +268,21 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   // the block-sum kernel clears them before the router raises them
   unsigned long long* rmax = (!fast && !beta) ? at<unsigned long long>(ws, pl.pmax) : nullptr;
   if (rmax && sums_ready) return fail(MISA_ERR_HIP, "internal: router maxima need the block-sum pass");
+  const bool qf8 = p->q_dtype == MISA_Q_FP8_E4M3FN;
+  if (qf8 && fast)
+    return fail(MISA_ERR_UNSUPPORTED, "fp8 queries: T = %d queries over %d blocks need the many-query router",
+                p->T, ceil_div(p->L, p->B));
   // with cached block means only each query's last block is pooled here
   if (!sums_ready)
     HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
                               p->kbar != nullptr, kb16, 0, max_pool, rmax, rmax ? p->T * 64 : 0),
             "block sums");
   if (!fast) {
-    HIP_TRY(launch_route(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar, tsum, rmax,
-                         heads, r, beta, beta_ld, qr, wr, max_pool),
+    HIP_TRY(launch_route(cx, p->q, qf8, p->q_scale, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar,
+                         tsum, rmax, heads, r, beta, beta_ld, qr, wr, max_pool),
             "router");
   } else {
-    HIP_TRY(launch_route_heads(cx, p->q, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, kb16, p->kbar,
+    HIP_TRY(launch_route_heads(cx, static_cast<const uint16_t*>(p->q), p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, kb16, p->kbar,
                                tsum, at<void>(ws, pl.part), heads, r, qr, wr),
             "router");
   }
@@ -312,6 +324,8 @@ static ScoreArgs score_args(const misa_problem* p) {
   ScoreArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = p->q;
+  a.q_fp8 = p->q_dtype == MISA_Q_FP8_E4M3FN;
+  a.qscale = p->q_scale;  // null for rows that already carry their scales
   a.w = p->w;
   a.H = p->H;
   a.T = p->T;
@@ -341,7 +355,8 @@ static misa_status run_routed_scores(const LaunchCtx& cx, const misa_problem* p,
   float* wr = at<float>(ws, pl.wr);
   if (heads) {
     // caller-chosen heads: pack their q rows and weights
-    HIP_TRY(launch_gather_heads(cx, p->q, p->w, heads, p->T, p->H, A, qr, wr), "head gather");
+    HIP_TRY(launch_gather_heads(cx, p->q, sa.q_fp8, p->q_scale, p->w, heads, p->T, p->H, A, qr, wr),
+            "head gather");
   } else if (A < p->H) {
     // routing packs the q rows and weights of the chosen heads as it selects them
     MISA_TRY(run_route(cx, p, pl, ws, A, at<int32_t>(ws, pl.heads), nullptr, nullptr, 0, qr, wr));
@@ -350,6 +365,7 @@ static misa_status run_routed_scores(const LaunchCtx& cx, const misa_problem* p,
     sa.q = qr;
     sa.w = wr;
     sa.H = A;
+    sa.qscale = nullptr;  // packed fp8 rows carry their scales (sign in the codes, |scale| in w)
   }  // else dense: all H heads in their own order
   sa.A = A;
   sa.S = at<float>(ws, pl.S);
@@ -424,6 +440,8 @@ static misa_status check_hier_args(const misa_problem* p, int A, const int32_t* 
   MISA_TRY(check_out(idx, "idx"));
   MISA_TRY(check_out(scores, "scores"));
   if (heads && !aligned(heads, 4)) return fail(MISA_ERR_INVALID_ARG, "heads must be 4-byte aligned");
+  if (p->q_dtype == MISA_Q_FP8_E4M3FN && !score_fp8q_supported(p->T, A))
+    return fail(MISA_ERR_UNSUPPORTED, "fp8 queries: T = %d with A = %d exceeds the decode-shaped batches", p->T, A);
   return MISA_OK;
 }
 
@@ -585,6 +603,8 @@ misa_status misa_score_topk(const misa_problem* p, int32_t A, const int32_t* hea
   MISA_TRY(check_out(idx, "idx"));
   MISA_TRY(check_out(scores, "scores"));
   if (heads && !aligned(heads, 4)) return fail(MISA_ERR_INVALID_ARG, "heads must be 4-byte aligned");
+  if (p->q_dtype == MISA_Q_FP8_E4M3FN && !score_fp8q_supported(p->T, A))
+    return fail(MISA_ERR_UNSUPPORTED, "fp8 queries: T = %d with A = %d exceeds the decode-shaped batches", p->T, A);
   const Plan pl = make_plan(p, MISA_OP_SCORE_TOPK, A, 1, k, 1);
   MISA_TRY(check_ws(pl, ws, ws_bytes));
   const LaunchCtx cx{static_cast<hipStream_t>(stream)};
@@ -685,14 +705,18 @@ misa_status misa_hisa_topk(const misa_problem* p, int32_t A, const int32_t* head
   uint16_t* qr = at<uint16_t>(ws, pl.qr);
   float* wr = at<float>(ws, pl.wr);
   if (heads)
-    HIP_TRY(launch_gather_heads(cx, p->q, p->w, heads, p->T, p->H, A, qr, wr), "head gather");
+    HIP_TRY(launch_gather_heads(cx, p->q, p->q_dtype == MISA_Q_FP8_E4M3FN, p->q_scale, p->w, heads, p->T, p->H, A,
+                                qr, wr),
+            "head gather");
   else
     MISA_TRY(run_route(cx, p, pl, ws, A, at<int32_t>(ws, pl.heads), nullptr, nullptr, 0, qr, wr));
   // both HISA stages with the routed heads: their packed rows stand in for q and w
+  // (packed fp8 rows carry their scales: scale 1 from here on)
   misa_problem pr = *p;
   pr.q = qr;
   pr.w = wr;
   pr.H = A;
+  pr.q_scale = nullptr;
   return run_hisa(cx, &pr, pl, ws, k, idx, scores, heads == nullptr);
 }
 

@@ -81,18 +81,28 @@ int route_chunks(int L, int B);
 // slot order (so scoring needs no head indirection). Optional HISA block
 // scores beta. max_pool: ksum and tsum hold max-pooled representatives
 // (launch_block_sums with max_pool), used as given.
-hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
-                        int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
-                        const double* tsum, unsigned long long* rmax, int32_t* heads, float* r_out,
-                        float* beta, int beta_ld, uint16_t* qr, float* wr, bool max_pool = false);
+// q_fp8: q holds E4M3FN codes with one scale per (query, head) in qscale (null:
+// scale 1, for rows that already carry their scales; the head selection needs
+// the scales). Packed rows of fp8 queries are codes with the scale's sign
+// folded in, and their weights w * |scale|.
+hipError_t launch_route(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,
+                        const int32_t* pos, int T, int H, int L, int B, int A, const double* ksum,
+                        const float* kbar, const double* tsum, unsigned long long* rmax, int32_t* heads,
+                        float* r_out, float* beta, int beta_ld, void* qr, float* wr, bool max_pool = false);
 // Pack q rows and weights of given heads [T,A] in slot order (ids outside [0,H)
 // give zero rows and weights).
-hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,
-                               const int32_t* heads, int T, int H, int A, uint16_t* qr, float* wr);
+hipError_t launch_gather_heads(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,
+                               const int32_t* heads, int T, int H, int A, void* qr, float* wr);
+// true when launch_score_keys can score fp8 queries for this batch (decode
+// shapes: every routed row of a query group in one workgroup)
+bool score_fp8q_supported(int T, int A);
 
 // ---- scoring (score_kernels.hip)
 struct ScoreArgs {
-  const uint16_t* q;     // [T,H,128] bf16; slot j < A of query t scores row j
+  const void* q;         // [T,H,128] bf16, or E4M3FN codes (q_fp8); slot j < A of query t scores row j
+  int q_fp8;             // q holds fp8 codes (keys must be fp8): fp8 x fp8 matrix products
+  const float* qscale;   // q_fp8: [T,H] per-row scales (null: rows already carry the sign and
+                         // the weights |scale|, as packed by the router)
   const float* w;        // [T,H]
   int A, H, T;           // A <= H rows of each query are scored (H is the row stride)
   const void* K;         // [L,128] bf16 or e4m3fn

@@ -198,8 +198,11 @@ __device__ __forceinline__ double row_max16(double v) {
   return dpp_max<0x128>(v);  // row_ror:8
 }
 
-template <bool WITH_BETA, int kRouteQG>
-__global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const float* w,
+// QF8: q holds E4M3FN codes with one scale per (query, head) in qscale (null:
+// scale 1, rows that already carry their scales); the value code * scale is
+// formed exactly in float64.
+template <bool WITH_BETA, int kRouteQG, bool QF8>
+__global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* qscale, const float* w,
                                                     const int32_t* pos, int T, int H, int L, int B,
                                                     int ntiles, const double* ksum,
                                                     const float* kbar, const double* tsum,
@@ -223,14 +226,19 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     const int t = tq0 + i;
     n_q[i] = t < T ? visible_len(pos[t], L) : 0;
   }
+  // 32 dims per lane: 64 bytes of bf16, or 32 fp8 codes and the row's scale
+  constexpr int QW16 = QF8 ? 2 : 4;
   u32x4 qv[2][4];
+  double qsc[2] = {1.0, 1.0};
 #define MISA_LOAD_Q(i, slot)                                                                     \
   do {                                                                                           \
     const int t_ = tq0 + (i);                                                                    \
     const bool ok_ = t_ < T && h_a < H;                                                          \
-    const u32x4* src_ = reinterpret_cast<const u32x4*>(                                          \
-        q + ((size_t)(ok_ ? t_ : 0) * H + (ok_ ? h_a : 0)) * kHeadDim + 32 * g);                 \
-    _Pragma("unroll") for (int v_ = 0; v_ < 4; ++v_) qv[slot][v_] = ok_ ? src_[v_] : u32x4{0u, 0u, 0u, 0u}; \
+    const size_t row_ = (size_t)(ok_ ? t_ : 0) * H + (ok_ ? h_a : 0);                            \
+    const u32x4* src_ = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) +     \
+                                                       row_ * kHeadDim * (QF8 ? 1 : 2) + 32 * g * (QF8 ? 1 : 2)); \
+    _Pragma("unroll") for (int v_ = 0; v_ < QW16; ++v_) qv[slot][v_] = ok_ ? src_[v_] : u32x4{0u, 0u, 0u, 0u}; \
+    if (QF8) qsc[slot] = ok_ ? (qscale ? (double)qscale[row_] : 1.0) : 0.0;                      \
   } while (0)
   MISA_LOAD_Q(0, 0);
   if (kbar) {
@@ -292,9 +300,19 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
     f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int s = 0; s < 32; s += 2) {
-      const uint32_t word = qv[i & 1][s >> 3][(s >> 1) & 3];
-      const double a0 = (double)bf16_bits_to_f32(word & 0xffffu);
-      const double a1 = (double)bf16_bits_to_f32(word >> 16);
+      double a0, a1;
+      if constexpr (QF8) {
+        // codes s and s + 1 of the lane's 32, times the row's scale (exact)
+        const uint32_t word = qv[i & 1][s >> 4][(s >> 2) & 3];
+        float f0, f1;
+        fp8x2_to_f32<false>((s & 2) ? (word >> 16) : word, f0, f1);
+        a0 = (double)f0 * qsc[i & 1];
+        a1 = (double)f1 * qsc[i & 1];
+      } else {
+        const uint32_t word = qv[i & 1][s >> 3][(s >> 1) & 3];
+        a0 = (double)bf16_bits_to_f32(word & 0xffffu);
+        a1 = (double)bf16_bits_to_f32(word >> 16);
+      }
       acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, kb[s >> 1][0], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, kb[s >> 1][1], acc1, 0, 0, 0);
     }
@@ -335,22 +353,30 @@ __global__ __launch_bounds__(256) void k_route_mfma(const uint16_t* q, const flo
 #undef MISA_LOAD_Q
 
 // Final router step, 256 threads per query: r(t,h) = w[t,h] * max_b ReLU(rho)
-// from the reduced maxima rmax, then the first A heads under (-r, h). heads[t,:] is written in ascending head order; with qr the routed q
-// rows and weights are packed in the same order for the scoring kernel. Every
-// global read is issued up front (none depends on another).
-__global__ __launch_bounds__(256) void k_route_select(const uint16_t* q, const float* w, int H, int A,
-                                                     const unsigned long long* rmax, int32_t* heads,
-                                                     float* r_out, uint16_t* qr, float* wr) {
+// from the reduced maxima rmax, then the first A heads under (-r, h).
+// heads[t,:] is written in ascending head order; with qr the routed q rows and
+// weights are packed in the same order for the scoring kernel. Every global
+// read is issued up front (none depends on another). QF8: the rows are fp8
+// codes; a packed row is the head's codes with the sign of its scale folded in
+// (bit 7 flipped when the scale is negative) and its weight is w * |scale|, so
+// that w * ReLU(q . k) of the packed row equals the head's term.
+template <bool QF8>
+__global__ __launch_bounds__(256) void k_route_select(const void* q, const float* qscale, const float* w, int H,
+                                                     int A, const unsigned long long* rmax, int32_t* heads,
+                                                     float* r_out, void* qr, float* wr) {
+  constexpr int RB = QF8 ? kHeadDim : 2 * kHeadDim;  // bytes per q row
+  constexpr int RW = RB / 16;                          // 16-byte words per q row
   __shared__ double rs[kWave];
   __shared__ int rank_part[4][kWave];
-  __shared__ u32x4 qs[kWave * kHeadDim / 8];  // q[t] as 16-byte words
+  __shared__ u32x4 qs[kWave * RW];  // q[t] as 16-byte words
   const int t = blockIdx.x, tid = threadIdx.x, h = tid & 63, j = tid >> 6;
   const bool active = h < H;
   const float wt = active ? w[(size_t)t * H + h] : 0.f;
+  const float sc = (QF8 && active) ? qscale[(size_t)t * H + h] : 1.f;
   const double m = __longlong_as_double((long long)rmax[(size_t)t * kWave + h]);
   if (qr) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + (size_t)t * H * kHeadDim);
-    const int nw = H * kHeadDim / 8;
+    const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) + (size_t)t * H * RB);
+    const int nw = H * RW;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (tid + 256 * u < nw) qs[tid + 256 * u] = src[tid + 256 * u];
@@ -382,26 +408,39 @@ __global__ __launch_bounds__(256) void k_route_select(const uint16_t* q, const f
     const int slot = lanes_below(mask);
     heads[(size_t)t * A + slot] = h;
     if (qr) {
-      wr[(size_t)t * A + slot] = wt;
-      u32x4* dst = reinterpret_cast<u32x4*>(qr + ((size_t)t * A + slot) * kHeadDim);
+      wr[(size_t)t * A + slot] = QF8 ? wt * fabsf(sc) : wt;
+      const uint32_t flip = (QF8 && sc < 0.f) ? 0x80808080u : 0u;
+      u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(qr) + ((size_t)t * A + slot) * RB);
 #pragma unroll
-      for (int v = 0; v < kHeadDim / 8; ++v) dst[v] = qs[h * (kHeadDim / 8) + v];
+      for (int v = 0; v < RW; ++v) {
+        u32x4 x = qs[h * RW + v];
+        x[0] ^= flip;
+        x[1] ^= flip;
+        x[2] ^= flip;
+        x[3] ^= flip;
+        dst[v] = x;
+      }
     }
   }
 }
 
 // Pack the q rows and weights of caller-given heads in slot order; one wave
-// per (query, slot), each lane copying 4 bytes.
-__global__ __launch_bounds__(64) void k_gather_heads(const uint16_t* q, const float* w,
-                                                     const int32_t* heads, int H, int A,
-                                                     uint16_t* qr, float* wr) {
+// per (query, slot), each lane copying 4 bytes (ids outside [0,H) give zero
+// rows and weights). QF8: as in k_route_select, the sign of the scale is
+// folded into the codes and |scale| into the weight.
+template <bool QF8>
+__global__ __launch_bounds__(64) void k_gather_heads(const void* q, const float* qscale, const float* w,
+                                                     const int32_t* heads, int H, int A, void* qr, float* wr) {
+  constexpr int RB = QF8 ? kHeadDim : 2 * kHeadDim;
   const int t = blockIdx.y, j = blockIdx.x, lane = threadIdx.x;
   const int h = heads[(size_t)t * A + j];
   const bool ok = h >= 0 && h < H;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(q + ((size_t)t * H + (ok ? h : 0)) * kHeadDim);
-  uint32_t* dst = reinterpret_cast<uint32_t*>(qr + ((size_t)t * A + j) * kHeadDim);
-  dst[lane] = ok ? src[lane] : 0u;
-  if (lane == 0) wr[(size_t)t * A + j] = ok ? w[(size_t)t * H + h] : 0.f;
+  const float sc = (QF8 && ok) ? qscale[(size_t)t * H + h] : 1.f;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(q) +
+                                                          ((size_t)t * H + (ok ? h : 0)) * RB);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(qr) + ((size_t)t * A + j) * RB);
+  if (lane * 4 < RB) dst[lane] = ok ? (src[lane] ^ ((QF8 && sc < 0.f) ? 0x80808080u : 0u)) : 0u;
+  if (lane == 0) wr[(size_t)t * A + j] = ok ? (QF8 ? w[(size_t)t * H + h] * fabsf(sc) : w[(size_t)t * H + h]) : 0.f;
 }
 
 // -------------------------------------------------------------------------
@@ -430,36 +469,46 @@ int route_chunks(int L, int B) {
   return c < 1 ? 1 : c;
 }
 
-hipError_t launch_route(const LaunchCtx& cx, const uint16_t* q, const float* w, const int32_t* pos,
-                        int T, int H, int L, int B, int A, const double* ksum, const float* kbar,
-                        const double* tsum, unsigned long long* rmax, int32_t* heads, float* r_out,
-                        float* beta, int beta_ld, uint16_t* qr, float* wr, bool max_pool) {
+hipError_t launch_route(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,
+                        const int32_t* pos, int T, int H, int L, int B, int A, const double* ksum,
+                        const float* kbar, const double* tsum, unsigned long long* rmax, int32_t* heads,
+                        float* r_out, float* beta, int beta_ld, void* qr, float* wr, bool max_pool) {
   if (T == 0) return hipSuccess;
   const int nt = route_chunks(L, B);
+  const bool f8 = q_fp8;
+  if (f8 && (heads || r_out) && !qscale) return hipErrorInvalidValue;  // selection needs the scales
   hipError_t e;
   // one query per workgroup while that leaves few workgroups per CU; past
   // that, groups of queries share each staged tile
   const long long work = (long long)nt * T;
   const int qg = work > 16384 ? 8 : (work > 2048 ? 2 : 1);
   const dim3 grid(nt, (T + qg - 1) / qg);
-#define MISA_ROUTE_LAUNCH(BETA, QG)                                                                \
-  cx.launch("route_mfma", k_route_mfma<BETA, QG>, grid, dim3(256), 0, q, w, pos, T, H, L, B, nt, ksum, \
-            kbar, tsum, rmax, beta, beta_ld, max_pool ? 1 : 0)
+#define MISA_ROUTE_LAUNCH(BETA, QG)                                                                     \
+  (f8 ? cx.launch("route_mfma", k_route_mfma<BETA, QG, true>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, B, \
+                  nt, ksum, kbar, tsum, rmax, beta, beta_ld, max_pool ? 1 : 0)                            \
+      : cx.launch("route_mfma", k_route_mfma<BETA, QG, false>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, \
+                  B, nt, ksum, kbar, tsum, rmax, beta, beta_ld, max_pool ? 1 : 0))
   if (beta)
     e = qg == 8 ? MISA_ROUTE_LAUNCH(true, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(true, 2) : MISA_ROUTE_LAUNCH(true, 1));
   else
     e = qg == 8 ? MISA_ROUTE_LAUNCH(false, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(false, 2) : MISA_ROUTE_LAUNCH(false, 1));
 #undef MISA_ROUTE_LAUNCH
   if (e != hipSuccess) return e;
-  if (!heads && !r_out) return hipSuccess;  // block scores, or maxima for the scoring kernel
-  return cx.launch("route_select", k_route_select, dim3(T), dim3(256), 0, q, w, H, A,
+  if (!heads && !r_out) return hipSuccess;  // block scores only
+  if (f8)
+    return cx.launch("route_select", k_route_select<true>, dim3(T), dim3(256), 0, q, qscale, w, H, A,
+                     (const unsigned long long*)rmax, heads, r_out, qr, wr);
+  return cx.launch("route_select", k_route_select<false>, dim3(T), dim3(256), 0, q, qscale, w, H, A,
                    (const unsigned long long*)rmax, heads, r_out, qr, wr);
 }
 
-hipError_t launch_gather_heads(const LaunchCtx& cx, const uint16_t* q, const float* w,
-                               const int32_t* heads, int T, int H, int A, uint16_t* qr, float* wr) {
+hipError_t launch_gather_heads(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,
+                               const int32_t* heads, int T, int H, int A, void* qr, float* wr) {
   if (T == 0) return hipSuccess;
-  return cx.launch("gather_heads", k_gather_heads, dim3(A, T), dim3(64), 0, q, w, heads, H, A, qr, wr);
+  if (q_fp8 && !qscale) return hipErrorInvalidValue;
+  if (q_fp8)
+    return cx.launch("gather_heads", k_gather_heads<true>, dim3(A, T), dim3(64), 0, q, qscale, w, heads, H, A, qr, wr);
+  return cx.launch("gather_heads", k_gather_heads<false>, dim3(A, T), dim3(64), 0, q, qscale, w, heads, H, A, qr, wr);
 }
 
 }  // namespace misa

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
       const int t = g * QW + qi;
       if (t < p.T && j < p.A) {
         const bf16x8* src = reinterpret_cast<const bf16x8*>(
-            p.q + ((size_t)t * p.H + j) * kHeadDim + 32 * (lane >> 4));
+            reinterpret_cast<const uint16_t*>(p.q) + ((size_t)t * p.H + j) * kHeadDim + 32 * (lane >> 4));
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = src[ks];
       } else {
@@ -304,8 +304,16 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
 // each wave loads its own B fragments straight from global memory: no LDS, no
 // barriers, D groups of 16 keys in flight per wave. Lane l covers key
 // (l mod 16) of a group and head dims [32*(l/16), 32*(l/16) + 32).
-template <int AP, int RPW, int WR, bool FP8, bool GATHER>
+//
+// QF8 (fp8 queries and fp8 keys): one v_mfma_scale_f32_16x16x128_f8f6f4 per
+// row tile and key group takes all 128 dims (both block scales 2^0), with the
+// E4M3 codes of q and of the key as its operands, each lane holding the same
+// 32 dims of its row and of its key; a row's per-(query, head) scale is
+// positive-homogeneous through ReLU like the key's, so its sign is folded into
+// the row's codes and |scale| into the row's weight.
+template <int AP, int RPW, int WR, bool FP8, bool GATHER, bool QF8 = false>
 __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
+  static_assert(!QF8 || FP8, "fp8 queries are scored against fp8 keys");
   constexpr int WC = 4 / WR;                        // key groups per tile (waves sharing rows)
   constexpr int ROWS = WR * RPW * 16;               // rows per workgroup
   constexpr int QW = ROWS / AP;                     // queries per workgroup
@@ -332,24 +340,59 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   // weights are loaded once into LDS (one pad word per row keeps the 16-byte
   // row reads conflict-free) instead of once per wave.
   constexpr bool STAGE = WC > 1;
-  constexpr int QSTR = kHeadDim / 8 + 1;
-  constexpr int SQ = STAGE ? ROWS * 16 / 256 : 0;  // 16-byte q words per thread
+  constexpr int RW = QF8 ? kHeadDim / 16 : kHeadDim / 8;  // 16-byte words per q row
+  constexpr int QSTR = RW + 1;
+  constexpr int SQ = STAGE ? (ROWS * RW + 255) / 256 : 0;  // 16-byte q words per thread (rounded up)
   __shared__ u32x4 qsh[STAGE ? ROWS * QSTR : 1];
   __shared__ float wsh[STAGE ? ROWS : 1];
   u32x4 qstage[SQ > 0 ? SQ : 1];
   float wstage = 0.f;
-  if constexpr (STAGE) {
+  const uint8_t* qbytes = reinterpret_cast<const uint8_t*>(p.q);
+  // fp8 rows with their own scales: the sign goes into the codes, |scale| into the weight
+  auto row_flip = [&](int t, int j) -> uint32_t {
+    if constexpr (QF8) return (p.qscale && p.qscale[(size_t)t * p.H + j] < 0.f) ? 0x80808080u : 0u;
+    else return 0u;
+  };
+  auto row_weight = [&](int t, int j) -> float {
+    const float wt = p.w[(size_t)t * p.H + j];
+    if constexpr (QF8) return p.qscale ? wt * fabsf(p.qscale[(size_t)t * p.H + j]) : wt;
+    else return wt;
+  };
+  if constexpr (STAGE && !QF8) {
 #pragma unroll
     for (int u = 0; u < SQ; ++u) {
       const int i = tid + 256 * u, row = i >> 4, v = i & 15;
       const int qi = row / AP, j = row % AP, t = g * QW + qi;
       qstage[u] = (t < p.T && j < p.A)
-                      ? reinterpret_cast<const u32x4*>(p.q + ((size_t)t * p.H + j) * kHeadDim)[v]
+                      ? reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.q) +
+                                                       ((size_t)t * p.H + j) * kHeadDim)[v]
                       : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < ROWS) {
       const int qi = tid / AP, j = tid % AP, t = g * QW + qi;
       wstage = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
+    }
+  }
+  if constexpr (STAGE && QF8) {
+#pragma unroll
+    for (int u = 0; u < SQ; ++u) {
+      const int i = tid + 256 * u, row = i / RW, v = i % RW;
+      const int qi = row / AP, j = row % AP, t = g * QW + qi;
+      if (i < ROWS * RW && t < p.T && j < p.A) {
+        u32x4 x = reinterpret_cast<const u32x4*>(qbytes + ((size_t)t * p.H + j) * RW * 16)[v];
+        const uint32_t f = row_flip(t, j);
+        x[0] ^= f;
+        x[1] ^= f;
+        x[2] ^= f;
+        x[3] ^= f;
+        qstage[u] = x;
+      } else {
+        qstage[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < ROWS) {
+      const int qi = tid / AP, j = tid % AP, t = g * QW + qi;
+      wstage = (t < p.T && j < p.A) ? row_weight(t, j) : 0.f;
     }
   }
 
@@ -430,7 +473,7 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
 #pragma unroll
     for (int u = 0; u < SQ; ++u) {
       const int i = tid + 256 * u;
-      qsh[(i >> 4) * QSTR + (i & 15)] = qstage[u];
+      if (QF8 ? i < ROWS * RW : true) qsh[(i / RW) * QSTR + (i % RW)] = qstage[u];
     }
     if (tid < ROWS) wsh[tid] = wstage;
   }
@@ -452,16 +495,23 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   // ---- A operand (q rows of the scored heads) and epilogue weights, kept in
   // registers; issued before the key stream so the first MFMA waits on one
   // round trip only.
-  bf16x8 afrag[RPW][4];
+  // A operand per row tile: 4 x 8 bf16 (bf16 rows), or 32 fp8 codes (QF8)
+  bf16x8 afrag[QF8 ? 1 : RPW][4];
+  i32x8 afrag8[QF8 ? RPW : 1];
   float wv[RPW][4];
 #pragma unroll
   for (int r = 0; r < RPW && STAGE; ++r) {
     // staged rows are in (query, slot) order: row qi * AP + j
     int qi, j;
     RM::at(wr * RPW + r, lane & 15, qi, j);
+    if constexpr (QF8) {
+      const u32x4 lo = qsh[(qi * AP + j) * QSTR + 2 * slice], hi = qsh[(qi * AP + j) * QSTR + 2 * slice + 1];
+      afrag8[r] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      afrag[r][ks] = __builtin_bit_cast(bf16x8, qsh[(qi * AP + j) * QSTR + 4 * slice + ks]);
+      for (int ks = 0; ks < 4; ++ks)
+        afrag[r][ks] = __builtin_bit_cast(bf16x8, qsh[(qi * AP + j) * QSTR + 4 * slice + ks]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       RM::at(wr * RPW + r, 4 * slice + i, qi, j);
@@ -474,14 +524,26 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
       int qi, j;
       RM::at(wr * RPW + r, lane & 15, qi, j);
       const int t = g * QW + qi;
-      if (t < p.T && j < p.A) {
-        const bf16x8* src = reinterpret_cast<const bf16x8*>(
-            p.q + ((size_t)t * p.H + j) * kHeadDim + 32 * slice);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = src[ks];
+      if constexpr (QF8) {
+        if (t < p.T && j < p.A) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(qbytes + ((size_t)t * p.H + j) * kHeadDim + 32 * slice);
+          const u32x4 lo = src[0], hi = src[1];
+          const int f = (int)row_flip(t, j);
+          afrag8[r] = i32x8{(int)lo[0] ^ f, (int)lo[1] ^ f, (int)lo[2] ^ f, (int)lo[3] ^ f,
+                            (int)hi[0] ^ f, (int)hi[1] ^ f, (int)hi[2] ^ f, (int)hi[3] ^ f};
+        } else {
+          afrag8[r] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
       } else {
+        if (t < p.T && j < p.A) {
+          const bf16x8* src = reinterpret_cast<const bf16x8*>(
+              reinterpret_cast<const uint16_t*>(p.q) + ((size_t)t * p.H + j) * kHeadDim + 32 * slice);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = bf16x8{};
+          for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = src[ks];
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) afrag[r][ks] = bf16x8{};
+        }
       }
     }
 #pragma unroll
@@ -489,7 +551,8 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
       int qi, j;
       RM::at(wr * RPW + r, 4 * slice + i, qi, j);
       const int t = g * QW + qi;
-      wv[r][i] = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
+      if constexpr (QF8) wv[r][i] = (t < p.T && j < p.A) ? row_weight(t, j) : 0.f;
+      else wv[r][i] = (t < p.T && j < p.A) ? p.w[(size_t)t * p.H + j] : 0.f;
     }
   }
 
@@ -523,20 +586,27 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
     for (int d = 0; d < D; ++d) {
       const int gi = gb + d;
       if (gi >= ngroups) break;  // uniform
-      // B fragments for the four K steps (fp8 codes widen exactly to bf16)
-      bf16x8 bfrag[4];
+      // B fragments for the four K steps (fp8 codes widen exactly to bf16), or
+      // the key's 32 fp8 codes as they are (QF8)
+      bf16x8 bfrag[QF8 ? 1 : 4];
+      i32x8 bfrag8;
+      if constexpr (QF8) {
+        bfrag8 = i32x8{(int)kv[d][0][0], (int)kv[d][0][1], (int)kv[d][0][2], (int)kv[d][0][3],
+                       (int)kv[d][1][0], (int)kv[d][1][1], (int)kv[d][1][2], (int)kv[d][1][3]};
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if constexpr (FP8) {
-          const uint32_t w0 = kv[d][ks >> 1][(ks & 1) * 2], w1 = kv[d][ks >> 1][(ks & 1) * 2 + 1];
-          u32x4 b;
-          b[0] = fp8x2_to_bf16x2<false>(w0);
-          b[1] = fp8x2_to_bf16x2<true>(w0);
-          b[2] = fp8x2_to_bf16x2<false>(w1);
-          b[3] = fp8x2_to_bf16x2<true>(w1);
-          bfrag[ks] = __builtin_bit_cast(bf16x8, b);
-        } else {
-          bfrag[ks] = __builtin_bit_cast(bf16x8, kv[d][ks]);
+        for (int ks = 0; ks < 4; ++ks) {
+          if constexpr (FP8) {
+            const uint32_t w0 = kv[d][ks >> 1][(ks & 1) * 2], w1 = kv[d][ks >> 1][(ks & 1) * 2 + 1];
+            u32x4 b;
+            b[0] = fp8x2_to_bf16x2<false>(w0);
+            b[1] = fp8x2_to_bf16x2<true>(w0);
+            b[2] = fp8x2_to_bf16x2<false>(w1);
+            b[3] = fp8x2_to_bf16x2<true>(w1);
+            bfrag[ks] = __builtin_bit_cast(bf16x8, b);
+          } else {
+            bfrag[ks] = __builtin_bit_cast(bf16x8, kv[d][ks]);
+          }
         }
       }
       float kscale = ksv[d];
@@ -550,9 +620,14 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (QF8) {
+          // all 128 dims at once; E8M0 block scales 127 = 2^0 for both operands
+          a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag8[r], bfrag8, a4, 0, 0, 0, 127, 0, 127);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[r][ks], bfrag[ks], a4, 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks)
+            a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[r][ks], bfrag[ks], a4, 0, 0, 0);
+        }
         acc[r] = a4;
       }
       if constexpr (FP8) {
@@ -677,6 +752,10 @@ static hipError_t run_direct(const LaunchCtx& cx, ScoreArgs a, bool fp8, const c
   a.nsplit = splits;
   if (nsplit_out) *nsplit_out = splits;
   const dim3 grid = GATHER ? dim3(splits, groups) : dim3(groups, splits);
+  if (a.q_fp8) {
+    if (!fp8) return hipErrorInvalidValue;  // fp8 queries are scored against fp8 keys
+    return cx.launch(name, k_score_direct<AP, RPW, WR, true, GATHER, true>, grid, dim3(256), 0, a);
+  }
   if (fp8) return cx.launch(name, k_score_direct<AP, RPW, WR, true, GATHER>, grid, dim3(256), 0, a);
   return cx.launch(name, k_score_direct<AP, RPW, WR, false, GATHER>, grid, dim3(256), 0, a);
 }
@@ -704,6 +783,8 @@ static bool direct_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, long long ro
   return true;
 }
 
+bool score_fp8q_supported(int T, int A) { return A >= 1 && A <= kMaxHeads && (long long)T * pad_heads(A) <= 256; }
+
 hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* nsplit_out) {
   if (a.T == 0) return hipSuccess;
   if (a.S_ld % 128 != 0 || a.S_ld < a.L) return hipErrorInvalidValue;  // whole tiles per row
@@ -722,6 +803,7 @@ hipError_t launch_score_keys(const LaunchCtx& cx, ScoreArgs a, bool fp8, int* ns
     default: done = direct_keys<64>(cx, a, fp8, rows, nsplit_out, &err); break;
   }
   if (done) return err;
+  if (a.q_fp8) return hipErrorInvalidValue;  // fp8 queries: decode-shaped batches only
   // larger batches (prefill): LDS-staged key tiles shared by 256 rows
   switch (ap) {
     case 4: return run_score<4, 4, 4, 8>(cx, a, fp8, nm, nsplit_out);
