@@ -310,6 +310,56 @@ __device__ __forceinline__ void radix_threshold(KeyAt key_at, int n, int k, uint
   need_eq = rem;
 }
 
+// Threshold of the c keys key_at(0..c) (1 <= rem < c, extremes umin, umax):
+// tau = the rem-th largest and need_eq = rem - #{keys > tau}. A short list is
+// ranked pairwise. A longer one takes one pass of kSubBins bins linear in the
+// score over [umin, umax]; the bin of a key never decreases as the key grows,
+// so keys of higher bins all exceed, and keys of lower bins all fall below,
+// every key of the bin holding the rem-th largest. That bin's keys (a few,
+// unless many keys tie) are then ranked pairwise; a crowded bin falls back to
+// radix digits over the whole list. Work is linear in c, not quadratic.
+template <int NT, typename KeyAt>
+__device__ __forceinline__ void list_threshold(KeyAt key_at, int c, int rem, uint32_t umin, uint32_t umax,
+                                               TopkShared<NT>& sm, uint32_t& tau, int& need_eq) {
+  constexpr int kPairCap = 64;
+  constexpr int kSubBins = 1024;
+  const int tid = threadIdx.x;
+  if (c <= kPairCap) {
+    for (int i = tid; i < c; i += NT) sm.list[i] = key_at(i);
+    __syncthreads();
+    rank_in_list<NT>(c, rem, sm, tau, need_eq);
+    return;
+  }
+  const float xlo = key_score(umin);
+  const float scale = lin_scale(xlo, key_score(umax), kSubBins);
+  for (int b = tid; b < kSubBins; b += NT) sm.hist[b] = 0u;
+  if (tid == 0) sm.nlist = 0;
+  __syncthreads();
+  for (int i = tid; i < c; i += NT) atomicAdd(&sm.hist[lin_bin(key_at(i), xlo, scale, kSubBins)], 1u);
+  __syncthreads();
+  find_bin<NT>(sm.hist, kSubBins, rem, sm);  // synchronises
+  const uint32_t bstar = (uint32_t)sm.digit;
+  const int nl = (int)sm.hist[bstar];
+  const int r2 = sm.rem;
+  if (nl > kRankCap) {
+    __syncthreads();  // everyone has read the histogram before it is reused
+    radix_threshold<NT>(key_at, c, rem, umin, umax, sm, tau, need_eq);
+    return;
+  }
+  for (int i0 = 0; i0 < c; i0 += NT) {
+    const int i = i0 + tid;
+    const uint32_t x = i < c ? key_at(i) : 0u;
+    const bool keep = i < c && lin_bin(x, xlo, scale, kSubBins) == bstar;
+    const uint64_t m = wave_ballot(keep);
+    int at = 0;
+    if ((tid & 63) == 0 && m) at = atomicAdd(&sm.nlist, __popcll(m));
+    at = __shfl(at, 0, kWave);
+    if (keep) sm.list[at + lanes_below(m)] = x;
+  }
+  __syncthreads();
+  rank_in_list<NT>(nl, r2, sm, tau, need_eq);
+}
+
 // Emit the selection in ascending item order: items with key > tau plus the
 // first need_eq items equal to tau (every item when take_all). Each wave owns a
 // contiguous segment; a count pass and a write pass keep the order.
@@ -746,13 +796,9 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
   if (rem >= cb) {
     tau = sm.umin;  // every item of the boundary bin is kept
     need_eq = cb;
-  } else if (cb <= kRankCap) {
-    for (int i = tid; i < cb; i += NT) sm.list[i] = blist[i];
-    __syncthreads();
-    rank_in_list<NT>(cb, rem, sm, tau, need_eq);
   } else if (in_lds) {
     auto key_at = [=](int i) { return blist[i]; };
-    radix_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
+    list_threshold<NT>(key_at, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
   } else {
     radix_threshold<NT>(item, cb, rem, sm.umin, sm.umax, sm, tau, need_eq);
   }
