@@ -104,7 +104,7 @@ static void plan_route(Bump& bp, Plan& pl, const misa_problem* p) {
   const int M = ceil_div(p->L, p->B);
   pl.ksum = bp.take((size_t)M * 128 * 8);
   pl.tsum = bp.take((size_t)p->T * 128 * 8);
-  pl.pmax = bp.take((size_t)p->T * 64 * 8);  // per-head maxima of the router (float64 bits)
+  pl.pmax = bp.take((size_t)p->T * 64 * 8 * (kRouteSlots + 1));  // router: partial maxima, last-block values
   if (route_fast_wins(p->L, p->B, p->T)) {
     pl.kb16 = bp.take((size_t)M * 2 * 128 * 2);
     pl.part = bp.take((size_t)p->T * route_fast_parts(p->L, p->B, p->T) * 64 * route_part_bytes());
@@ -275,7 +275,7 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   // with cached block means only each query's last block is pooled here
   if (!sums_ready)
     HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
-                              p->kbar != nullptr, kb16, 0, max_pool, rmax, rmax ? p->T * 64 : 0),
+                              p->kbar != nullptr, kb16, 0, max_pool, rmax, rmax ? p->T * 64 * kRouteSlots : 0),
             "block sums");
   if (!fast) {
     HIP_TRY(launch_route(cx, p->q, qf8, p->q_scale, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar,

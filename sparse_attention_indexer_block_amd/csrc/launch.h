@@ -74,8 +74,12 @@ hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const floa
                               float* r_out, uint16_t* qr, float* wr);
 // Router tiles of 16 blocks.
 int route_chunks(int L, int B);
-// Router: per-head maxima max_b ReLU(rho) into rmax[T,64] (float64 bit
-// patterns, zero on entry: launch_block_sums clears them) when rmax is set;
+// Partial per-head maxima of the router per query (tiles spread over them).
+constexpr int kRouteSlots = 8;
+// Router: per-head maxima of the complete blocks into rmax[T,kRouteSlots,64]
+// (float64 bit patterns, zero on entry: launch_block_sums clears them) and the
+// last block's ReLU(rho) into the T*64 doubles after them, when rmax is set
+// (required for the head ranking);
 // then, when heads or r_out is set, heads[T,A] (ascending), optional r[T,H]
 // and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed in
 // slot order (so scoring needs no head indirection). Optional HISA block

@@ -46,9 +46,10 @@ struct KeySlice {
   }
 };
 
-// Sum of key rows [s0, s1) in float64, one workgroup of 256 threads; thread
-// (rl, dg) takes rows rl, rl + RL, ... and one 16-byte slice of dims. Four rows
-// per thread are loaded before any is added, so the loads overlap. Column sums
+// Sum of key rows [s0, s1) in float64, one workgroup of kSumThreads threads;
+// thread (rl, dg) takes rows rl, rl + RL, ... and one 16-byte slice of dims. A
+// whole 128-key block's rows of a thread (8 fp8 or 16 bf16 slices) are loaded
+// before any is added, so the loads overlap. Column sums
 // are left in red for the caller to add up: value e of slice dg of row group rl
 // sits at red[rl * kRedStride + e * NG + dg] (so one store instruction of a wave
 // covers contiguous doubles, and the padded row stride puts alternate row
@@ -57,19 +58,24 @@ struct KeySlice {
 // MAX: per-dimension maximum instead of the sum (max-pooled representatives;
 // exact, the widened values being exact in float64).
 constexpr int kRedStride = kHeadDim + 8;  // doubles per row group of the reduction buffer
+// 128 threads keep the reduction buffer at 17 KiB (fp8) so that every
+// workgroup of a 128K-key problem (1024 blocks plus the query tails) is
+// resident at once; with 256 threads a second round of workgroups waited for
+// the first to finish.
+constexpr int kSumThreads = 128;
 
 template <bool FP8, bool MAX = false>
 struct RowSum {
   static constexpr int DPT = KeySlice<FP8>::DPT;
   static constexpr int NG = kHeadDim / DPT;  // slices per key
-  static constexpr int RL = 256 / NG;        // rows in flight per pass
+  static constexpr int RL = kSumThreads / NG;  // row groups
+  static constexpr int U = kHeadDim / RL;        // rows per thread per pass (one 128-key block)
   static __device__ __forceinline__ int dim_of(int c) { return (c % NG) * DPT + c / NG; }
   static __device__ __forceinline__ void run(const void* K, const float* kscale, int s0, int s1, double* red) {
     const int tid = threadIdx.x, dg = tid % NG, rl = tid / NG;
     double acc[DPT];
 #pragma unroll
     for (int e = 0; e < DPT; ++e) acc[e] = MAX ? -__builtin_huge_val() : 0.0;
-    constexpr int U = 4;
     for (int sb = s0 + rl; sb < s1; sb += RL * U) {
       u32x4 v[U];
       double sc[U];
@@ -104,32 +110,38 @@ struct RowSum {
   }
 };
 
-// Workgroup b (= blockIdx.x + b_base) in [0, M): ksum[b,:] = sum of the keys of
-// block b = [b*B, min((b+1)*B, L)) in float64, and (optional) kbar = ksum /
-// count rounded once to float32. Workgroups [M, M+T): tsum[t,:] = sum of the
-// keys of query t's last block [(M_t-1)*B, n_t), possibly partial; zero when
-// the query sees no key. b_base = M computes the query tails only. MAX: the
+// Workgroups [0, ntail): tsum[t,:] = sum of the keys of query t's last block
+// [(M_t-1)*B, n_t), possibly partial; zero when the query sees no key (they
+// come first so that the tails, which often all read the same last block,
+// start before the long tail of the grid). Workgroup ntail + i: block
+// b = b_base + i in [0, M): ksum[b,:] = sum of the keys of block
+// b = [b*B, min((b+1)*B, L)) in float64, and (optional) kbar = ksum / count
+// rounded once to float32. MAX: the
 // per-dimension maxima of the same keys instead of their sums (max-pooled
 // block representatives; no kbar or kb16), zero for a query with no key.
-// Workgroup 0 also clears zero[0, zero_n) (the router's per-head maxima,
-// which the router kernel raises with atomic maxima).
+// The workgroups also clear zero[0, zero_n) (the router's per-head maxima,
+// which the router kernel raises with atomic maxima), each a share.
 template <bool FP8, bool MAX>
-__global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* kscale, int L,
+__global__ __launch_bounds__(kSumThreads) void k_block_sums(const void* K, const float* kscale, int L,
                                                     int B, int M, double* ksum, float* kbar,
                                                     uint16_t* kb16, const int32_t* pos, double* tsum,
-                                                    int b_base, unsigned long long* zero, int zero_n) {
+                                                    int ntail, int b_base, unsigned long long* zero,
+                                                    int zero_n) {
   using RS = RowSum<FP8, MAX>;
   constexpr int RL = RS::RL;
   __shared__ double red[RL * kRedStride];
-  if (zero && blockIdx.x == 0)
-    for (int i = (int)threadIdx.x; i < zero_n; i += 256) zero[i] = 0ull;
-  const int b = (int)blockIdx.x + b_base;
+  if (zero)
+    for (int i = (int)(blockIdx.x * kSumThreads + threadIdx.x); i < zero_n; i += (int)gridDim.x * kSumThreads)
+      zero[i] = 0ull;
+  const int wg = (int)blockIdx.x;
+  const bool is_tail = wg < ntail;
+  const int b = is_tail ? -1 : wg - ntail + b_base;
   int s0, s1;
-  if (b < M) {
+  if (!is_tail) {
     s0 = (int)((long long)b * B);
     s1 = (int)((long long)s0 + B < L ? (long long)s0 + B : L);
   } else {
-    const int n = visible_len(pos[b - M], L);
+    const int n = visible_len(pos[wg], L);
     const int Mt = (int)(((long long)n + B - 1) / B);
     s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
     s1 = n;
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
     }
     const int d = RS::dim_of(tid);
     if (MAX && s1 <= s0) s = 0.0;  // no key
-    if (b < M) {
+    if (!is_tail) {
       ksum[(size_t)b * kHeadDim + d] = s;
       if constexpr (MAX) return;
       const double mean = s / (double)(s1 - s0);
@@ -160,7 +172,7 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
         kb16[(size_t)b * 2 * kHeadDim + kHeadDim + d] = (uint16_t)lo;
       }
     } else {
-      tsum[(size_t)(b - M) * kHeadDim + d] = s;
+      tsum[(size_t)wg * kHeadDim + d] = s;
     }
   }
 }
@@ -172,13 +184,19 @@ __global__ __launch_bounds__(256) void k_block_sums(const void* K, const float* 
 // takes four head dims; lane l feeds head (A) and block (B) l % 16 with dims
 // [32(l/16), 32(l/16) + 32), one per step, so its operands are contiguous.
 // The result D[row][col] sits at lane col + 16 * (row % 4), element row / 4.
-// Raises rmax[t, h] (float64 bit patterns, zero on entry) to the maximum of
-// ReLU(rho) over the tile's blocks, the query's last (possibly partial) block
-// included: every value is >= +0.0, where the order of the bit patterns as
-// unsigned integers is the order of the values, so a 64-bit atomic maximum
-// over all tiles leaves max_b ReLU(rho(t,h,b)) (rmax may be null: not
-// needed). With WITH_BETA it writes the HISA block score
-// beta(t,b) = sum_h w[t,h] ReLU(rho) of every visible block.
+// Raises rmax[t, tile % kRouteSlots, h] (float64 bit patterns, zero on entry)
+// to the maximum of ReLU(q . Ksum_b) over the tile's complete blocks: the raw
+// product with the block's sum (or its cached mean, or its maxima), which the
+// ranking kernel divides by the block size once; dividing the maximum gives the
+// same value as dividing every block's product, division by a positive
+// constant being monotone. Every value is >= +0.0, where the order of the bit
+// patterns as unsigned integers is the order of the values, so 64-bit atomic
+// maxima leave the maximum; spreading the tiles over kRouteSlots partial
+// maxima keeps the atomics on any one address few (the ranking kernel takes
+// the largest slot). The tile holding the query's last (possibly partial)
+// block stores that block's ReLU(rho) into rtail[t, h] with plain stores (one
+// tile per query). rmax may be null (not needed). With WITH_BETA it writes the
+// HISA block score beta(t,b) = sum_h w[t,h] ReLU(rho) of every visible block.
 constexpr int kRouteTile = 16;  // blocks per workgroup
 
 // max over the 16 lanes of each row of the wave (every lane gets its row's max)
@@ -206,8 +224,8 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
                                                     const int32_t* pos, int T, int H, int L, int B,
                                                     int ntiles, const double* ksum,
                                                     const float* kbar, const double* tsum,
-                                                    unsigned long long* rmax, float* beta,
-                                                    int beta_ld, int max_pool) {
+                                                    unsigned long long* rmax, double* rtail,
+                                                    float* beta, int beta_ld, int max_pool) {
   __shared__ f64x2 kt[kRouteTile][kHeadDim / 2 + 1];  // padded rows
   __shared__ double bsum[4][kRouteTile];
   const int tile = blockIdx.x, tq0 = blockIdx.y * kRouteQG;
@@ -320,13 +338,19 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
     // this lane holds heads 16 wv + 4 e + g (e = 0..3) against block blk
     const double cnt = tail ? (max_pool ? 1.0 : (double)(n - (Mt - 1) * B)) : div_full;
     if (rmax) {
-      unsigned long long* rm = rmax + (size_t)t * kWave + kRouteTile * wv + g;
+      unsigned long long* rm = rmax + ((size_t)t * kRouteSlots + tile % kRouteSlots) * kWave + kRouteTile * wv + g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0) / div_full;
+        const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0);
         if (col == 0 && m > 0.0) atomicMax(rm + 4 * e, (unsigned long long)__double_as_longlong(m));
-        const double v = acc[e] / cnt;  // the last block: its own count of keys
-        if (tail && v > 0.0) atomicMax(rm + 4 * e, (unsigned long long)__double_as_longlong(v));
+      }
+      if (Mt - 1 < b0 + kRouteTile && tail) {  // the query's last block: its own count of keys
+        double* rt = rtail + (size_t)t * kWave + kRouteTile * wv + g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double v = acc[e] / cnt;
+          rt[4 * e] = v > 0.0 ? v : 0.0;
+        }
       }
     }
     if constexpr (WITH_BETA) {
@@ -353,7 +377,9 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
 #undef MISA_LOAD_Q
 
 // Final router step, 256 threads per query: r(t,h) = w[t,h] * max_b ReLU(rho)
-// from the reduced maxima rmax, then the first A heads under (-r, h).
+// from the complete blocks' maximum rmax (divided here by div_full, the block
+// size, or 1 for means and maxima) and the last block's rtail, then the first
+// A heads under (-r, h).
 // heads[t,:] is written in ascending head order; with qr the routed q rows and
 // weights are packed in the same order for the scoring kernel. Every global
 // read is issued up front (none depends on another). QF8: the rows are fp8
@@ -362,8 +388,9 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
 // that w * ReLU(q . k) of the packed row equals the head's term.
 template <bool QF8>
 __global__ __launch_bounds__(256) void k_route_select(const void* q, const float* qscale, const float* w, int H,
-                                                     int A, const unsigned long long* rmax, int32_t* heads,
-                                                     float* r_out, void* qr, float* wr) {
+                                                     int A, const int32_t* pos, int L, double div_full,
+                                                     const unsigned long long* rmax, const double* rtail,
+                                                     int32_t* heads, float* r_out, void* qr, float* wr) {
   constexpr int RB = QF8 ? kHeadDim : 2 * kHeadDim;  // bytes per q row
   constexpr int RW = RB / 16;                          // 16-byte words per q row
   __shared__ double rs[kWave];
@@ -373,7 +400,16 @@ __global__ __launch_bounds__(256) void k_route_select(const void* q, const float
   const bool active = h < H;
   const float wt = active ? w[(size_t)t * H + h] : 0.f;
   const float sc = (QF8 && active) ? qscale[(size_t)t * H + h] : 1.f;
-  const double m = __longlong_as_double((long long)rmax[(size_t)t * kWave + h]);
+  const bool any_key = visible_len(pos[t], L) > 0;
+  unsigned long long mraw = 0ull;  // float64 bits of values >= +0.0: integer order is value order
+#pragma unroll
+  for (int i = 0; i < kRouteSlots; ++i) {
+    const unsigned long long x = rmax[((size_t)t * kRouteSlots + i) * kWave + h];
+    mraw = x > mraw ? x : mraw;
+  }
+  const double mfull = __longlong_as_double((long long)mraw) / div_full;
+  const double mtail = any_key ? rtail[(size_t)t * kWave + h] : 0.0;
+  const double m = mtail > mfull ? mtail : mfull;
   if (qr) {
     const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) + (size_t)t * H * RB);
     const int nw = H * RW;
@@ -452,12 +488,13 @@ hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* ks
                              unsigned long long* zero, int zero_n) {
   const int M = (int)(((long long)L + B - 1) / B);
   const int base = tails_only ? M : (first_block < M ? first_block : M);
-  const int grid = M - base + (tsum ? T : 0);
+  const int ntail = tsum ? T : 0;
+  const int grid = M - base + ntail;
   if (grid == 0) return hipSuccess;
   const char* nm = tails_only ? "tail_sums" : "block_sums";
 #define MISA_SUMS_LAUNCH(F8, MX)                                                                    \
-  cx.launch(nm, k_block_sums<F8, MX>, dim3(grid), dim3(256), 0, K, kscale, L, B, M, ksum,            \
-            MX ? nullptr : kbar, MX ? nullptr : kb16, pos, tsum, base, zero, zero_n)
+  cx.launch(nm, k_block_sums<F8, MX>, dim3(grid), dim3(kSumThreads), 0, K, kscale, L, B, M, ksum,            \
+            MX ? nullptr : kbar, MX ? nullptr : kb16, pos, tsum, ntail, base, zero, zero_n)
   if (max_pool) return fp8 ? MISA_SUMS_LAUNCH(true, true) : MISA_SUMS_LAUNCH(false, true);
   return fp8 ? MISA_SUMS_LAUNCH(true, false) : MISA_SUMS_LAUNCH(false, false);
 #undef MISA_SUMS_LAUNCH
@@ -483,11 +520,12 @@ hipError_t launch_route(const LaunchCtx& cx, const void* q, bool q_fp8, const fl
   const long long work = (long long)nt * T;
   const int qg = work > 16384 ? 8 : (work > 2048 ? 2 : 1);
   const dim3 grid(nt, (T + qg - 1) / qg);
+  double* rtail = rmax ? reinterpret_cast<double*>(rmax + (size_t)T * kRouteSlots * kWave) : nullptr;
 #define MISA_ROUTE_LAUNCH(BETA, QG)                                                                     \
   (f8 ? cx.launch("route_mfma", k_route_mfma<BETA, QG, true>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, B, \
-                  nt, ksum, kbar, tsum, rmax, beta, beta_ld, max_pool ? 1 : 0)                            \
+                  nt, ksum, kbar, tsum, rmax, rtail, beta, beta_ld, max_pool ? 1 : 0)                     \
       : cx.launch("route_mfma", k_route_mfma<BETA, QG, false>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, \
-                  B, nt, ksum, kbar, tsum, rmax, beta, beta_ld, max_pool ? 1 : 0))
+                  B, nt, ksum, kbar, tsum, rmax, rtail, beta, beta_ld, max_pool ? 1 : 0))
   if (beta)
     e = qg == 8 ? MISA_ROUTE_LAUNCH(true, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(true, 2) : MISA_ROUTE_LAUNCH(true, 1));
   else
@@ -495,11 +533,13 @@ hipError_t launch_route(const LaunchCtx& cx, const void* q, bool q_fp8, const fl
 #undef MISA_ROUTE_LAUNCH
   if (e != hipSuccess) return e;
   if (!heads && !r_out) return hipSuccess;  // block scores only
+  if (!rmax) return hipErrorInvalidValue;  // the ranking needs the maxima
+  const double div_full = kbar || max_pool ? 1.0 : (double)B;
   if (f8)
-    return cx.launch("route_select", k_route_select<true>, dim3(T), dim3(256), 0, q, qscale, w, H, A,
-                     (const unsigned long long*)rmax, heads, r_out, qr, wr);
-  return cx.launch("route_select", k_route_select<false>, dim3(T), dim3(256), 0, q, qscale, w, H, A,
-                   (const unsigned long long*)rmax, heads, r_out, qr, wr);
+    return cx.launch("route_select", k_route_select<true>, dim3(T), dim3(256), 0, q, qscale, w, H, A, pos, L,
+                     div_full, (const unsigned long long*)rmax, (const double*)rtail, heads, r_out, qr, wr);
+  return cx.launch("route_select", k_route_select<false>, dim3(T), dim3(256), 0, q, qscale, w, H, A, pos, L,
+                   div_full, (const unsigned long long*)rmax, (const double*)rtail, heads, r_out, qr, wr);
 }
 
 hipError_t launch_gather_heads(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,
