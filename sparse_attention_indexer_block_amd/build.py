@@ -64,6 +64,42 @@ def build(jobs: int = 4) -> str:
     return LIB
 
 
+def build_host_asan(out_dir: str, jobs: int = 4) -> str:
+    """The library with its host code (argument validation, workspace
+    planning, dispatch) instrumented with AddressSanitizer, as
+    libmisa_asan.so in out_dir; the device code is built as usual, without
+    sanitizer. It serves the CPU tests of the C ABI's validation paths, which
+    return before any launch. Load it with the sanitizer runtime preloaded
+    (asan_runtime())."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [*CFLAGS, "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+    def one(src):
+        obj = os.path.join(out_dir, src.replace(".hip", ".asan.o"))
+        r = subprocess.run([HIPCC, *flags, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"host ASan build failed for {src}:\n{r.stdout}{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(one, SOURCES))
+    out = os.path.join(out_dir, "libmisa_asan.so")
+    # the sanitizer runtime is not linked into a shared library; it is preloaded
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host ASan link failed:\n{r.stdout}{r.stderr}")
+    return out
+
+
+def asan_runtime() -> str:
+    """The compiler's AddressSanitizer runtime (to preload), or '' if absent."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    return path if path and os.path.isabs(path) and os.path.exists(path) else ""
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)

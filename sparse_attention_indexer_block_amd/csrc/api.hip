@@ -104,7 +104,8 @@ static void plan_route(Bump& bp, Plan& pl, const misa_problem* p) {
   const int M = ceil_div(p->L, p->B);
   pl.ksum = bp.take((size_t)M * 128 * 8);
   pl.tsum = bp.take((size_t)p->T * 128 * 8);
-  pl.pmax = bp.take((size_t)p->T * 64 * 8 * (kRouteSlots + 1));  // router: partial maxima, last-block values
+  // router: per-tile head maxima, then the last blocks' values
+  pl.pmax = bp.take((size_t)p->T * (route_chunks(p->L, p->B) + 1) * 64 * 8);
   if (route_fast_wins(p->L, p->B, p->T)) {
     pl.kb16 = bp.take((size_t)M * 2 * 128 * 2);
     pl.part = bp.take((size_t)p->T * route_fast_parts(p->L, p->B, p->T) * 64 * route_part_bytes());
@@ -253,10 +254,13 @@ static misa_status check_out(const void* ptr, const char* name) {
 
 // sums_ready: the block sums (ksum, or only the query tails with cached means)
 // and tsum are already in the workspace from an earlier router pass of this call.
+// keep_sums: leave ksum and the query tails tsum in the workspace for a later
+// block-score pass of the same call (the float64 head ranking alone pools each
+// query's last block itself and reads no tails).
 static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const Plan& pl, void* ws,
                              int A, int32_t* heads, float* r, float* beta, int beta_ld,
                              uint16_t* qr = nullptr, float* wr = nullptr, bool sums_ready = false,
-                             bool max_pool = false) {
+                             bool max_pool = false, bool keep_sums = false) {
   const bool fp8 = p->k_dtype == MISA_K_FP8_E4M3FN;
   double* ksum = at<double>(ws, pl.ksum);
   double* tsum = at<double>(ws, pl.tsum);
@@ -264,22 +268,26 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
   // ambiguous; few queries: every block's rho in float64 directly
   const bool fast = !beta && route_fast_wins(p->L, p->B, p->T);
   uint16_t* kb16 = fast ? at<uint16_t>(ws, pl.kb16) : nullptr;
-  // per-head maxima for the head selection (not needed for block scores alone);
-  // the block-sum kernel clears them before the router raises them
-  unsigned long long* rmax = (!fast && !beta) ? at<unsigned long long>(ws, pl.pmax) : nullptr;
-  if (rmax && sums_ready) return fail(MISA_ERR_HIP, "internal: router maxima need the block-sum pass");
+  // float64 head ranking: per-tile maxima of the complete blocks (plain stores)
+  double* part = (!fast && !beta) ? at<double>(ws, pl.pmax) : nullptr;
   const bool qf8 = p->q_dtype == MISA_Q_FP8_E4M3FN;
   if (qf8 && fast)
     return fail(MISA_ERR_UNSUPPORTED, "fp8 queries: T = %d queries over %d blocks need the many-query router",
                 p->T, ceil_div(p->L, p->B));
-  // with cached block means only each query's last block is pooled here
+  if (part && max_pool) return fail(MISA_ERR_HIP, "internal: max pooling ranks no heads");
+  // query tails: pooled by the block-sum pass whenever it runs (the ranking
+  // kernel pools them itself only with cached means, where no such pass runs)
+  const bool tails = !part || keep_sums || p->kbar == nullptr;
+  // with cached block means only the query tails are pooled here (nothing is
+  // launched when no tails are needed either)
   if (!sums_ready)
-    HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos, tsum,
-                              p->kbar != nullptr, kb16, 0, max_pool, rmax, rmax ? p->T * 64 * kRouteSlots : 0),
+    HIP_TRY(launch_block_sums(cx, p->K, p->k_scale, fp8, p->L, p->B, ksum, nullptr, p->T, p->pos,
+                              tails ? tsum : nullptr, p->kbar != nullptr, kb16, 0, max_pool),
             "block sums");
   if (!fast) {
     HIP_TRY(launch_route(cx, p->q, qf8, p->q_scale, p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, p->kbar,
-                         tsum, rmax, heads, r, beta, beta_ld, qr, wr, max_pool),
+                         tails ? tsum : nullptr, p->K, p->k_scale, fp8, part, heads, r, beta, beta_ld, qr, wr,
+                         max_pool),
             "router");
   } else {
     HIP_TRY(launch_route_heads(cx, static_cast<const uint16_t*>(p->q), p->w, p->pos, p->T, p->H, p->L, p->B, A, ksum, kb16, p->kbar,
@@ -708,8 +716,9 @@ misa_status misa_hisa_topk(const misa_problem* p, int32_t A, const int32_t* head
     HIP_TRY(launch_gather_heads(cx, p->q, p->q_dtype == MISA_Q_FP8_E4M3FN, p->q_scale, p->w, heads, p->T, p->H, A,
                                 qr, wr),
             "head gather");
-  else
-    MISA_TRY(run_route(cx, p, pl, ws, A, at<int32_t>(ws, pl.heads), nullptr, nullptr, 0, qr, wr));
+  else  // the block sums and query tails stay for the block filter
+    MISA_TRY(run_route(cx, p, pl, ws, A, at<int32_t>(ws, pl.heads), nullptr, nullptr, 0, qr, wr, false, false,
+                       true));
   // both HISA stages with the routed heads: their packed rows stand in for q and w
   // (packed fp8 rows carry their scales: scale 1 from here on)
   misa_problem pr = *p;

@@ -58,8 +58,7 @@ inline long long padded_ld(long long n) { return ((n + 127) / 128) * 128; }
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
                              double* tsum, bool tails_only = false, uint16_t* kb16 = nullptr,
-                             int first_block = 0, bool max_pool = false,
-                             unsigned long long* zero = nullptr, int zero_n = 0);
+                             int first_block = 0, bool max_pool = false);
 // MISA head routing with an exact result (route_fast.hip): bf16 block scores
 // with proven error bounds, then float64 settling of every head's maximum.
 // part: T * route_fast_parts(L, B, T) * 64 records of route_part_bytes();
@@ -74,16 +73,18 @@ hipError_t launch_route_heads(const LaunchCtx& cx, const uint16_t* q, const floa
                               float* r_out, uint16_t* qr, float* wr);
 // Router tiles of 16 blocks.
 int route_chunks(int L, int B);
-// Partial per-head maxima of the router per query (tiles spread over them).
-constexpr int kRouteSlots = 8;
-// Router: per-head maxima of the complete blocks into rmax[T,kRouteSlots,64]
-// (float64 bit patterns, zero on entry: launch_block_sums clears them) and the
-// last block's ReLU(rho) into the T*64 doubles after them, when rmax is set
-// (required for the head ranking);
-// then, when heads or r_out is set, heads[T,A] (ascending), optional r[T,H]
-// and optionally the routed q rows qr[T,A,128] and weights wr[T,A] packed in
-// slot order (so scoring needs no head indirection). Optional HISA block
-// scores beta. max_pool: ksum and tsum hold max-pooled representatives
+// Router, one of two forms.
+// Head ranking (beta null, heads or r_out set): the router tiles write the
+// per-head maxima of the complete blocks before each query's last block into
+// part[T, route_chunks(L, B), 64] (float64; every slot read is written, no
+// clearing) and, with tsum, the last block's value into the T * 64 doubles
+// after them; then one workgroup per query takes that value or, when tsum is
+// null, pools the last block from K / kscale itself, ranks the heads
+// and writes heads[T,A] (ascending), optional r[T,H] and optionally the routed
+// q rows qr[T,A,128] and weights wr[T,A] packed in slot order (so scoring
+// needs no head indirection). ksum (or kbar) must hold the complete blocks.
+// Block scores (beta set): HISA's beta from ksum / kbar and the query tails
+// tsum; max_pool: ksum and tsum hold max-pooled representatives
 // (launch_block_sums with max_pool), used as given.
 // q_fp8: q holds E4M3FN codes with one scale per (query, head) in qscale (null:
 // scale 1, for rows that already carry their scales; the head selection needs
@@ -91,8 +92,9 @@ constexpr int kRouteSlots = 8;
 // folded in, and their weights w * |scale|.
 hipError_t launch_route(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,
                         const int32_t* pos, int T, int H, int L, int B, int A, const double* ksum,
-                        const float* kbar, const double* tsum, unsigned long long* rmax, int32_t* heads,
-                        float* r_out, float* beta, int beta_ld, void* qr, float* wr, bool max_pool = false);
+                        const float* kbar, const double* tsum, const void* K, const float* kscale, bool k_fp8,
+                        double* part, int32_t* heads, float* r_out, float* beta, int beta_ld, void* qr, float* wr,
+                        bool max_pool = false);
 // Pack q rows and weights of given heads [T,A] in slot order (ids outside [0,H)
 // give zero rows and weights).
 hipError_t launch_gather_heads(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,

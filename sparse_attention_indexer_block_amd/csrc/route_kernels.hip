@@ -46,7 +46,7 @@ struct KeySlice {
   }
 };
 
-// Sum of key rows [s0, s1) in float64, one workgroup of kSumThreads threads;
+// Sum of key rows [s0, s1) in float64, one workgroup of NTH threads;
 // thread (rl, dg) takes rows rl, rl + RL, ... and one 16-byte slice of dims. A
 // whole 128-key block's rows of a thread (8 fp8 or 16 bf16 slices) are loaded
 // before any is added, so the loads overlap. Column sums
@@ -64,12 +64,12 @@ constexpr int kRedStride = kHeadDim + 8;  // doubles per row group of the reduct
 // the first to finish.
 constexpr int kSumThreads = 128;
 
-template <bool FP8, bool MAX = false>
+template <bool FP8, bool MAX = false, int NTH = kSumThreads>
 struct RowSum {
   static constexpr int DPT = KeySlice<FP8>::DPT;
   static constexpr int NG = kHeadDim / DPT;  // slices per key
-  static constexpr int RL = kSumThreads / NG;  // row groups
-  static constexpr int U = kHeadDim / RL;        // rows per thread per pass (one 128-key block)
+  static constexpr int RL = NTH / NG;        // row groups
+  static constexpr int U = 128 / RL;         // rows per thread per pass (128 keys per pass)
   static __device__ __forceinline__ int dim_of(int c) { return (c % NG) * DPT + c / NG; }
   static __device__ __forceinline__ void run(const void* K, const float* kscale, int s0, int s1, double* red) {
     const int tid = threadIdx.x, dg = tid % NG, rl = tid / NG;
@@ -77,24 +77,26 @@ struct RowSum {
 #pragma unroll
     for (int e = 0; e < DPT; ++e) acc[e] = MAX ? -__builtin_huge_val() : 0.0;
     for (int sb = s0 + rl; sb < s1; sb += RL * U) {
+      // every row's loads are issued before any is used, from clamped rows (a
+      // load inside a condition would be waited for inside it); rows past s1
+      // are masked afterwards
       u32x4 v[U];
-      double sc[U];
+      float scr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int s = sb + RL * u;
-        v[u] = u32x4{0u, 0u, 0u, 0u};
-        sc[u] = 0.0;
-        if (s < s1) {
-          v[u] = KeySlice<FP8>::load(K, s, dg);
-          if constexpr (FP8) sc[u] = (double)kscale[s];
-        }
+        const int s = min(sb + RL * u, s1 - 1);
+        v[u] = KeySlice<FP8>::load(K, s, dg);
+        scr[u] = FP8 ? kscale[s] : 1.f;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
+        const bool ok = sb + RL * u < s1;
+        if (!ok) v[u] = u32x4{0u, 0u, 0u, 0u};
+        const double sc = ok ? (double)scr[u] : 0.0;
         double x[DPT];
-        KeySlice<FP8>::widen(v[u], sc[u], x);
+        KeySlice<FP8>::widen(v[u], sc, x);
         if constexpr (MAX) {
-          if (sb + RL * u < s1) {
+          if (ok) {
 #pragma unroll
             for (int e = 0; e < DPT; ++e) acc[e] = x[e] > acc[e] ? x[e] : acc[e];
           }
@@ -119,20 +121,14 @@ struct RowSum {
 // rounded once to float32. MAX: the
 // per-dimension maxima of the same keys instead of their sums (max-pooled
 // block representatives; no kbar or kb16), zero for a query with no key.
-// The workgroups also clear zero[0, zero_n) (the router's per-head maxima,
-// which the router kernel raises with atomic maxima), each a share.
 template <bool FP8, bool MAX>
 __global__ __launch_bounds__(kSumThreads) void k_block_sums(const void* K, const float* kscale, int L,
                                                     int B, int M, double* ksum, float* kbar,
                                                     uint16_t* kb16, const int32_t* pos, double* tsum,
-                                                    int ntail, int b_base, unsigned long long* zero,
-                                                    int zero_n) {
+                                                    int ntail, int b_base) {
   using RS = RowSum<FP8, MAX>;
   constexpr int RL = RS::RL;
   __shared__ double red[RL * kRedStride];
-  if (zero)
-    for (int i = (int)(blockIdx.x * kSumThreads + threadIdx.x); i < zero_n; i += (int)gridDim.x * kSumThreads)
-      zero[i] = 0ull;
   const int wg = (int)blockIdx.x;
   const bool is_tail = wg < ntail;
   const int b = is_tail ? -1 : wg - ntail + b_base;
@@ -184,19 +180,18 @@ __global__ __launch_bounds__(kSumThreads) void k_block_sums(const void* K, const
 // takes four head dims; lane l feeds head (A) and block (B) l % 16 with dims
 // [32(l/16), 32(l/16) + 32), one per step, so its operands are contiguous.
 // The result D[row][col] sits at lane col + 16 * (row % 4), element row / 4.
-// Raises rmax[t, tile % kRouteSlots, h] (float64 bit patterns, zero on entry)
-// to the maximum of ReLU(q . Ksum_b) over the tile's complete blocks: the raw
-// product with the block's sum (or its cached mean, or its maxima), which the
-// ranking kernel divides by the block size once; dividing the maximum gives the
-// same value as dividing every block's product, division by a positive
-// constant being monotone. Every value is >= +0.0, where the order of the bit
-// patterns as unsigned integers is the order of the values, so 64-bit atomic
-// maxima leave the maximum; spreading the tiles over kRouteSlots partial
-// maxima keeps the atomics on any one address few (the ranking kernel takes
-// the largest slot). The tile holding the query's last (possibly partial)
-// block stores that block's ReLU(rho) into rtail[t, h] with plain stores (one
-// tile per query). rmax may be null (not needed). With WITH_BETA it writes the
-// HISA block score beta(t,b) = sum_h w[t,h] ReLU(rho) of every visible block.
+// Without WITH_BETA (head ranking) it writes part[t, tile, h], the maximum
+// of ReLU(q . Ksum_b) over the tile's complete blocks before the query's last
+// block, with plain stores (every tile that holds such a block writes; the
+// ranking kernel reads exactly those tiles). The value is the raw product with
+// the block's sum (or its cached mean), which the ranking kernel divides by the
+// block size once: dividing the maximum gives the same value as dividing every
+// block's product, division by a positive constant being monotone. When tsum
+// is given, the tile holding the query's last (possibly partial) block also
+// writes that block's ReLU(rho) to part[T * ntiles + t, h]; otherwise the
+// last block is left to the ranking kernel. With
+// WITH_BETA it writes the HISA block score beta(t,b) = sum_h w[t,h] ReLU(rho)
+// of every visible block, the last one from the query's tail sum tsum.
 constexpr int kRouteTile = 16;  // blocks per workgroup
 
 // max over the 16 lanes of each row of the wave (every lane gets its row's max)
@@ -219,15 +214,18 @@ __device__ __forceinline__ double row_max16(double v) {
 // QF8: q holds E4M3FN codes with one scale per (query, head) in qscale (null:
 // scale 1, rows that already carry their scales); the value code * scale is
 // formed exactly in float64.
-template <bool WITH_BETA, int kRouteQG, bool QF8>
+// MEANS: the complete blocks come as cached float means (kbar), else as float64
+// sums (ksum).
+template <bool WITH_BETA, int kRouteQG, bool QF8, bool MEANS>
 __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* qscale, const float* w,
                                                     const int32_t* pos, int T, int H, int L, int B,
                                                     int ntiles, const double* ksum,
                                                     const float* kbar, const double* tsum,
-                                                    unsigned long long* rmax, double* rtail,
-                                                    float* beta, int beta_ld, int max_pool) {
+                                                    double* part, float* beta, int beta_ld,
+                                                    int max_pool) {
   __shared__ f64x2 kt[kRouteTile][kHeadDim / 2 + 1];  // padded rows
   __shared__ double bsum[4][kRouteTile];
+  __shared__ f64x2 tls[kRouteQG][kHeadDim / 2];  // the group's query tail sums
   const int tile = blockIdx.x, tq0 = blockIdx.y * kRouteQG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -236,18 +234,33 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
   const int b0 = tile * kRouteTile;
   const int blk = b0 + col;
   const int h_a = kRouteTile * wv + col;  // head fed by this lane's A operand
-  // per query of the group: visible blocks, and the A operand (32 bf16 dims)
-  // in a two-slot ring so the next query's rows load during this one's products
-  int n_q[kRouteQG];
+  // Every global read below is issued from an address that is always valid and
+  // masked once it has arrived (a load inside a condition is waited for inside
+  // it): the tile's block statistics first, then the q rows, then the lengths.
+  int pos_q[kRouteQG];  // lengths first (raw positions; masked below)
 #pragma unroll
-  for (int i = 0; i < kRouteQG; ++i) {
-    const int t = tq0 + i;
-    n_q[i] = t < T ? visible_len(pos[t], L) : 0;
+  for (int i = 0; i < kRouteQG; ++i) pos_q[i] = pos[min(tq0 + i, T - 1)];
+  f32x4 xm[2];  // cached means (8 KB per tile): two 16-byte loads per thread
+  f64x2 xs[4];  // or block sums (16 KB per tile): four
+  if constexpr (MEANS) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = tid + 256 * u, r = i >> 5, c4 = i & 31;
+      xm[u] = reinterpret_cast<const f32x4*>(kbar + (size_t)min(b0 + r, M - 1) * kHeadDim)[c4];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = tid + 256 * u, r = i >> 6, c2 = i & 63;
+      xs[u] = reinterpret_cast<const f64x2*>(ksum + (size_t)min(b0 + r, M - 1) * kHeadDim)[c2];
+    }
   }
-  // 32 dims per lane: 64 bytes of bf16, or 32 fp8 codes and the row's scale
+  // per query of the group: the A operand (32 bf16 dims, or 32 fp8 codes and
+  // the row's scale) in a two-slot ring so the next query's rows load during
+  // this one's products, and the visible blocks
   constexpr int QW16 = QF8 ? 2 : 4;
   u32x4 qv[2][4];
-  double qsc[2] = {1.0, 1.0};
+  float qsc[2] = {1.f, 1.f};  // widened to float64 where used (exact)
 #define MISA_LOAD_Q(i, slot)                                                                     \
   do {                                                                                           \
     const int t_ = tq0 + (i);                                                                    \
@@ -255,41 +268,40 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
     const size_t row_ = (size_t)(ok_ ? t_ : 0) * H + (ok_ ? h_a : 0);                            \
     const u32x4* src_ = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) +     \
                                                        row_ * kHeadDim * (QF8 ? 1 : 2) + 32 * g * (QF8 ? 1 : 2)); \
-    _Pragma("unroll") for (int v_ = 0; v_ < QW16; ++v_) qv[slot][v_] = ok_ ? src_[v_] : u32x4{0u, 0u, 0u, 0u}; \
-    if (QF8) qsc[slot] = ok_ ? (qscale ? (double)qscale[row_] : 1.0) : 0.0;                      \
+    _Pragma("unroll") for (int v_ = 0; v_ < QW16; ++v_) qv[slot][v_] = src_[v_];                 \
+    /* (w stands in as a valid address when the rows carry their scales) */                      \
+    const float sc_ = QF8 ? (qscale ? qscale : w)[row_] : 1.f;                                   \
+    if (!ok_) {                                                                                  \
+      _Pragma("unroll") for (int v_ = 0; v_ < QW16; ++v_) qv[slot][v_] = u32x4{0u, 0u, 0u, 0u}; \
+    }                                                                                            \
+    if (QF8) qsc[slot] = ok_ ? (qscale ? sc_ : 1.f) : 0.f;                                       \
   } while (0)
   MISA_LOAD_Q(0, 0);
-  if (kbar) {
-    // stage the tile's cached block means (8 KB): two 16-byte loads per thread
-    f32x4 x[2];
+  // the group's tail sums into LDS (read by the lanes of each query's last block)
+  if (tsum && tid < kRouteQG * (kHeadDim / 2)) {
+    const int i = tid / (kHeadDim / 2), c2 = tid % (kHeadDim / 2);
+    tls[i][c2] = reinterpret_cast<const f64x2*>(tsum + (size_t)min(tq0 + i, T - 1) * kHeadDim)[c2];
+  }
+  int n_q[kRouteQG];
+#pragma unroll
+  for (int i = 0; i < kRouteQG; ++i) n_q[i] = tq0 + i < T ? visible_len(pos_q[i], L) : 0;
+  if constexpr (MEANS) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = tid + 256 * u, r = i >> 5, c4 = i & 31;
-      x[u] = b0 + r < M ? reinterpret_cast<const f32x4*>(kbar + (size_t)(b0 + r) * kHeadDim)[c4]
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = tid + 256 * u, r = i >> 5, c4 = i & 31;
-      kt[r][2 * c4] = f64x2{(double)x[u][0], (double)x[u][1]};
-      kt[r][2 * c4 + 1] = f64x2{(double)x[u][2], (double)x[u][3]};
+      const f32x4 x = b0 + r < M ? xm[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+      kt[r][2 * c4] = f64x2{(double)x[0], (double)x[1]};
+      kt[r][2 * c4 + 1] = f64x2{(double)x[2], (double)x[3]};
     }
   } else {
-    // stage the tile's block sums (16 KB): four 16-byte loads per thread
-    f64x2 x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int i = tid + 256 * u, r = i >> 6, c2 = i & 63;
-      x[u] = b0 + r < M ? reinterpret_cast<const f64x2*>(ksum + (size_t)(b0 + r) * kHeadDim)[c2] : f64x2{0.0, 0.0};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = tid + 256 * u;
-      kt[i >> 6][i & 63] = x[u];
+      const int i = tid + 256 * u, r = i >> 6;
+      kt[i >> 6][i & 63] = b0 + r < M ? xs[u] : f64x2{0.0, 0.0};
     }
   }
   // full blocks hold sums (divide by B), cached means or maxima (divide by 1)
-  const double div_full = kbar || max_pool ? 1.0 : (double)B;
+  const double div_full = MEANS || max_pool ? 1.0 : (double)B;
   __syncthreads();
   f64x2 kv[16];
 #pragma unroll
@@ -302,17 +314,21 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
     if (i + 1 < kRouteQG) MISA_LOAD_Q(i + 1, (i + 1) & 1);
     const int n = n_q[i];
     const int Mt = (int)(((long long)n + B - 1) / B);
-    if (b0 >= Mt) continue;  // uniform: no block of this tile is visible
-    const bool valid = blk < Mt;
-    const bool tail = blk == Mt - 1;
+    // every visible block, the last one from the query's tail sum when the
+    // block-sum pass pooled it (tsum); otherwise (cached means, head ranking)
+    // the complete blocks only: the ranking kernel pools the last block itself
+    const bool with_tail = WITH_BETA || tsum != nullptr;  // uniform
+    const int Mc = with_tail ? Mt : Mt - 1;
+    if (b0 >= Mc) continue;  // uniform: no block of this tile is taken
+    const bool valid = blk < Mc;
+    const bool tail = with_tail && blk == Mt - 1;
     // B operand: the block sums, or this query's own sum for its last block
     f64x2 kb[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) kb[v] = valid ? kv[v] : f64x2{0.0, 0.0};
     if (tail) {
-      const f64x2* src = reinterpret_cast<const f64x2*>(tsum + (size_t)t * kHeadDim + 32 * g);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) kb[v] = src[v];
+      for (int v = 0; v < 16; ++v) kb[v] = tls[i][16 * g + v];
     }
     // two accumulation chains (even and odd dims) keep the matrix unit busy
     f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
@@ -324,8 +340,8 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
         const uint32_t word = qv[i & 1][s >> 4][(s >> 2) & 3];
         float f0, f1;
         fp8x2_to_f32<false>((s & 2) ? (word >> 16) : word, f0, f1);
-        a0 = (double)f0 * qsc[i & 1];
-        a1 = (double)f1 * qsc[i & 1];
+        a0 = (double)f0 * (double)qsc[i & 1];
+        a1 = (double)f1 * (double)qsc[i & 1];
       } else {
         const uint32_t word = qv[i & 1][s >> 3][(s >> 1) & 3];
         a0 = (double)bf16_bits_to_f32(word & 0xffffu);
@@ -336,34 +352,40 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
     }
     const f64x4 acc = acc0 + acc1;
     // this lane holds heads 16 wv + 4 e + g (e = 0..3) against block blk
-    const double cnt = tail ? (max_pool ? 1.0 : (double)(n - (Mt - 1) * B)) : div_full;
-    if (rmax) {
-      unsigned long long* rm = rmax + ((size_t)t * kRouteSlots + tile % kRouteSlots) * kWave + kRouteTile * wv + g;
+    if constexpr (!WITH_BETA) {
+      // this tile's maximum of ReLU(q . Ksum_b) per head over its complete
+      // blocks, raw (see above); the last block's ReLU(rho) to rtail
+      double* pp = part + ((size_t)t * ntiles + tile) * kWave + kRouteTile * wv + g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const double m = row_max16((valid && !tail && acc[e] > 0.0) ? acc[e] : 0.0);
-        if (col == 0 && m > 0.0) atomicMax(rm + 4 * e, (unsigned long long)__double_as_longlong(m));
+        // device-scope stores: written through to memory, where the ranking
+        // kernel's workgroups (on other XCDs) read them without a probe of
+        // this XCD's L2
+        if (col == 0) __hip_atomic_store(pp + 4 * e, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (Mt - 1 < b0 + kRouteTile && tail) {  // the query's last block: its own count of keys
-        double* rt = rtail + (size_t)t * kWave + kRouteTile * wv + g;
+      if (tail) {
+        double* rt = part + ((size_t)T * ntiles + t) * kWave + kRouteTile * wv + g;
+        const double cnt = (double)(n - (Mt - 1) * B);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const double v = acc[e] / cnt;
-          rt[4 * e] = v > 0.0 ? v : 0.0;
+          __hip_atomic_store(rt + 4 * e, v > 0.0 ? v : 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
     if constexpr (WITH_BETA) {
-      double part = 0.0;
+      const double cnt = tail ? (max_pool ? 1.0 : (double)(n - (Mt - 1) * B)) : div_full;
+      double bs = 0.0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int hh = kRouteTile * wv + 4 * e + g;
         const double rho = acc[e] / cnt;
-        part += (hh < H && rho > 0.0) ? (double)w[(size_t)t * H + hh] * rho : 0.0;
+        bs += (hh < H && rho > 0.0) ? (double)w[(size_t)t * H + hh] * rho : 0.0;
       }
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
-      if (lane < kRouteTile) bsum[wv][lane] = part;
+      bs += __shfl_xor(bs, 16, kWave);
+      bs += __shfl_xor(bs, 32, kWave);
+      if (lane < kRouteTile) bsum[wv][lane] = bs;
       __syncthreads();
       if (tid < kRouteTile && b0 + tid < Mt) {
         const double s = bsum[0][tid] + bsum[1][tid] + bsum[2][tid] + bsum[3][tid];
@@ -376,49 +398,136 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
 
 #undef MISA_LOAD_Q
 
-// Final router step, 256 threads per query: r(t,h) = w[t,h] * max_b ReLU(rho)
-// from the complete blocks' maximum rmax (divided here by div_full, the block
-// size, or 1 for means and maxima) and the last block's rtail, then the first
-// A heads under (-r, h).
-// heads[t,:] is written in ascending head order; with qr the routed q rows and
-// weights are packed in the same order for the scoring kernel. Every global
-// read is issued up front (none depends on another). QF8: the rows are fp8
-// codes; a packed row is the head's codes with the sign of its scale folded in
-// (bit 7 flipped when the scale is negative) and its weight is w * |scale|, so
-// that w * ReLU(q . k) of the packed row equals the head's term.
-template <bool QF8>
+// Final router step, one workgroup of 256 threads per query:
+// r(t,h) = w[t,h] * max(the complete blocks' maximum, ReLU(rho of the last
+// block)), then the first A heads under (-r, h). The complete blocks' maxima
+// come from the router tiles (part: raw products, divided here once by
+// div_full, the block size, or 1 for cached means). The query's last block
+// [(M_t - 1) B, n_t), possibly partial, comes from the block-sum pass (tsum)
+// or, when tsum is null (cached means: no block-sum pass), is pooled here from
+// the keys in float64; its rho = q . sum / count is formed for every head
+// (thread (h, j) takes head h over dims [32 j, 32 j + 32)). heads[t,:] is written in
+// ascending head order; with qr the routed q rows and weights are packed in the
+// same order for the scoring kernel. QF8: the rows are fp8 codes; a packed row
+// is the head's codes with the sign of its scale folded in (bit 7 flipped when
+// the scale is negative) and its weight is w * |scale|, so that
+// w * ReLU(q . k) of the packed row equals the head's term.
+template <bool QF8, bool KF8>
 __global__ __launch_bounds__(256) void k_route_select(const void* q, const float* qscale, const float* w, int H,
-                                                     int A, const int32_t* pos, int L, double div_full,
-                                                     const unsigned long long* rmax, const double* rtail,
-                                                     int32_t* heads, float* r_out, void* qr, float* wr) {
+                                                     int A, const int32_t* pos, int L, int B, int ntiles,
+                                                     double div_full, const double* part, const double* tsum,
+                                                     const void* K, const float* kscale, int32_t* heads,
+                                                     float* r_out, void* qr, float* wr) {
+  using RS = RowSum<KF8, false, 256>;
   constexpr int RB = QF8 ? kHeadDim : 2 * kHeadDim;  // bytes per q row
   constexpr int RW = RB / 16;                          // 16-byte words per q row
+  constexpr int QW = RW / 4;                           // words of a thread's 32 dims
+  __shared__ double red[RS::RL * kRedStride];
+  __shared__ double tl[kHeadDim];  // the last block's key sum
+  __shared__ double pm[4][kWave];  // complete blocks' maxima, per thread group
+  __shared__ double pd[4][kWave];  // last-block products over 32 dims
   __shared__ double rs[kWave];
   __shared__ int rank_part[4][kWave];
   __shared__ u32x4 qs[kWave * RW];  // q[t] as 16-byte words
   const int t = blockIdx.x, tid = threadIdx.x, h = tid & 63, j = tid >> 6;
   const bool active = h < H;
-  const float wt = active ? w[(size_t)t * H + h] : 0.f;
-  const float sc = (QF8 && active) ? qscale[(size_t)t * H + h] : 1.f;
-  const bool any_key = visible_len(pos[t], L) > 0;
-  unsigned long long mraw = 0ull;  // float64 bits of values >= +0.0: integer order is value order
+  const int n = visible_len(pos[t], L);
+  const int Mt = (int)(((long long)n + B - 1) / B);
+  const int s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
+  const int nc = Mt > 1 ? (Mt - 1 + kRouteTile - 1) / kRouteTile : 0;  // tiles with complete blocks
+  // every global read is issued up front from an address that is always valid
+  // (a load inside a condition is waited for inside it); values are masked after
+  const int hc = active ? h : 0;
+  const float wt_raw = w[(size_t)t * H + hc];
+  const float sc_raw = QF8 ? qscale[(size_t)t * H + hc] : 1.f;
+  u32x4 qd[QW];  // this thread's 32 dims of q[t,h]
+  {
+    const u32x4* row = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) +
+                                                      ((size_t)t * H + hc) * RB) + QW * j;
 #pragma unroll
-  for (int i = 0; i < kRouteSlots; ++i) {
-    const unsigned long long x = rmax[((size_t)t * kRouteSlots + i) * kWave + h];
-    mraw = x > mraw ? x : mraw;
+    for (int v = 0; v < QW; ++v) qd[v] = row[v];
   }
-  const double mfull = __longlong_as_double((long long)mraw) / div_full;
-  const double mtail = any_key ? rtail[(size_t)t * kWave + h] : 0.0;
-  const double m = mtail > mfull ? mtail : mfull;
-  if (qr) {
+  const int nw = H * RW;  // 16-byte words of q[t]
+  u32x4 qst[4];  // q[t] for the packed rows (read even when not packed: no branch to wait in)
+  {
     const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) + (size_t)t * H * RB);
-    const int nw = H * RW;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qst[u] = src[min(tid + 256 * u, nw - 1)];
+  }
+  // every tile's slot is requested before the query's length arrives (slots
+  // past its complete blocks hold stale values and are masked afterwards)
+  const double mt_raw = tsum ? part[((size_t)gridDim.x * ntiles + t) * kWave + h] : 0.0;  // gridDim.x = T
+  double m = 0.0;  // values >= +0.0
+  for (int c0 = 0; c0 < ntiles; c0 += 64) {  // 16 loads in flight per thread
+    double x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) x[u] = part[((size_t)t * ntiles + min(c0 + j + 4 * u, ntiles - 1)) * kWave + h];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) m = (c0 + j + 4 * u < nc && x[u] > m) ? x[u] : m;
+  }
+  pm[j][h] = m;
+  const float wt = active ? wt_raw : 0.f;
+  const float sc = active ? sc_raw : 1.f;
+  if (qr) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (tid + 256 * u < nw) qs[tid + 256 * u] = src[tid + 256 * u];
+      if (tid + 256 * u < nw) qs[tid + 256 * u] = qst[u];
   }
+  // the last block's ReLU(rho): from the router tiles when the block-sum pass
+  // pooled the tails, else pooled and scored here
+  double mtail = 0.0;
+  if (tsum) {
+    mtail = Mt > 0 ? mt_raw : 0.0;
+  } else {
+    RS::run(K, kscale, s0, n, red);  // synchronises
+    if (tid < kHeadDim) {
+      double sum = 0.0;
+#pragma unroll
+      for (int r = 0; r < RS::RL; ++r) sum += red[r * kRedStride + tid];
+      tl[RS::dim_of(tid)] = sum;
+    }
+    __syncthreads();
+    double dp = 0.0;
+    if constexpr (QF8) {
+      const double qsc = (double)sc;  // code * scale is exact in float64
+#pragma unroll
+      for (int v = 0; v < QW; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float a0, a1, a2, a3;
+          fp8x2_to_f32<false>(qd[v][c], a0, a1);
+          fp8x2_to_f32<true>(qd[v][c], a2, a3);
+          const int d = 32 * j + 16 * v + 4 * c;
+          dp += ((double)a0 * qsc) * tl[d];
+          dp += ((double)a1 * qsc) * tl[d + 1];
+          dp += ((double)a2 * qsc) * tl[d + 2];
+          dp += ((double)a3 * qsc) * tl[d + 3];
+        }
+    } else {
+#pragma unroll
+      for (int v = 0; v < QW; ++v)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d = 32 * j + 8 * v + 2 * c;
+          dp += (double)bf16_bits_to_f32(qd[v][c] & 0xffffu) * tl[d];
+          dp += (double)bf16_bits_to_f32(qd[v][c] >> 16) * tl[d + 1];
+        }
+    }
+    pd[j][h] = dp;
+    __syncthreads();
+    if (j == 0 && Mt > 0) {
+      const double dt = ((pd[0][h] + pd[1][h]) + pd[2][h]) + pd[3][h];
+      mtail = dt / (double)(n - s0);  // the last block: its own count of keys
+    }
+  }
+  __syncthreads();  // pm complete
   if (j == 0) {
-    const double r = active ? (double)wt * m + 0.0 : -__builtin_huge_val();
+    double mfull = pm[0][h];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) mfull = pm[i][h] > mfull ? pm[i][h] : mfull;
+    mfull /= div_full;
+    const double mm = mtail > mfull ? mtail : mfull;  // ReLU: mfull >= +0.0
+    const double r = active ? (double)wt * mm + 0.0 : -__builtin_huge_val();
     if (r_out && active) r_out[(size_t)t * H + h] = (float)r;
     rs[h] = r;
   }
@@ -484,8 +593,7 @@ __global__ __launch_bounds__(64) void k_gather_heads(const void* q, const float*
 
 hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* kscale, bool fp8,
                              int L, int B, double* ksum, float* kbar, int T, const int32_t* pos,
-                             double* tsum, bool tails_only, uint16_t* kb16, int first_block, bool max_pool,
-                             unsigned long long* zero, int zero_n) {
+                             double* tsum, bool tails_only, uint16_t* kb16, int first_block, bool max_pool) {
   const int M = (int)(((long long)L + B - 1) / B);
   const int base = tails_only ? M : (first_block < M ? first_block : M);
   const int ntail = tsum ? T : 0;
@@ -494,7 +602,7 @@ hipError_t launch_block_sums(const LaunchCtx& cx, const void* K, const float* ks
   const char* nm = tails_only ? "tail_sums" : "block_sums";
 #define MISA_SUMS_LAUNCH(F8, MX)                                                                    \
   cx.launch(nm, k_block_sums<F8, MX>, dim3(grid), dim3(kSumThreads), 0, K, kscale, L, B, M, ksum,            \
-            MX ? nullptr : kbar, MX ? nullptr : kb16, pos, tsum, ntail, base, zero, zero_n)
+            MX ? nullptr : kbar, MX ? nullptr : kb16, pos, tsum, ntail, base)
   if (max_pool) return fp8 ? MISA_SUMS_LAUNCH(true, true) : MISA_SUMS_LAUNCH(false, true);
   return fp8 ? MISA_SUMS_LAUNCH(true, false) : MISA_SUMS_LAUNCH(false, false);
 #undef MISA_SUMS_LAUNCH
@@ -508,38 +616,42 @@ int route_chunks(int L, int B) {
 
 hipError_t launch_route(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,
                         const int32_t* pos, int T, int H, int L, int B, int A, const double* ksum,
-                        const float* kbar, const double* tsum, unsigned long long* rmax, int32_t* heads,
-                        float* r_out, float* beta, int beta_ld, void* qr, float* wr, bool max_pool) {
+                        const float* kbar, const double* tsum, const void* K, const float* kscale, bool k_fp8,
+                        double* part, int32_t* heads, float* r_out, float* beta, int beta_ld, void* qr, float* wr,
+                        bool max_pool) {
   if (T == 0) return hipSuccess;
   const int nt = route_chunks(L, B);
   const bool f8 = q_fp8;
   if (f8 && (heads || r_out) && !qscale) return hipErrorInvalidValue;  // selection needs the scales
+  if (!beta && (!part || max_pool)) return hipErrorInvalidValue;  // ranking: maxima of mean-pooled blocks
   hipError_t e;
   // one query per workgroup while that leaves few workgroups per CU; past
   // that, groups of queries share each staged tile
   const long long work = (long long)nt * T;
   const int qg = work > 16384 ? 8 : (work > 2048 ? 2 : 1);
   const dim3 grid(nt, (T + qg - 1) / qg);
-  double* rtail = rmax ? reinterpret_cast<double*>(rmax + (size_t)T * kRouteSlots * kWave) : nullptr;
-#define MISA_ROUTE_LAUNCH(BETA, QG)                                                                     \
-  (f8 ? cx.launch("route_mfma", k_route_mfma<BETA, QG, true>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, B, \
-                  nt, ksum, kbar, tsum, rmax, rtail, beta, beta_ld, max_pool ? 1 : 0)                     \
-      : cx.launch("route_mfma", k_route_mfma<BETA, QG, false>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, \
-                  B, nt, ksum, kbar, tsum, rmax, rtail, beta, beta_ld, max_pool ? 1 : 0))
+#define MISA_ROUTE_LAUNCH1(BETA, QG, QF, MN)                                                              \
+  cx.launch("route_mfma", k_route_mfma<BETA, QG, QF, MN>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, B, nt, \
+            ksum, kbar, tsum, part, beta, beta_ld, max_pool ? 1 : 0)
+#define MISA_ROUTE_LAUNCH(BETA, QG)                                                                  \
+  (f8 ? (kbar ? MISA_ROUTE_LAUNCH1(BETA, QG, true, true) : MISA_ROUTE_LAUNCH1(BETA, QG, true, false)) \
+      : (kbar ? MISA_ROUTE_LAUNCH1(BETA, QG, false, true) : MISA_ROUTE_LAUNCH1(BETA, QG, false, false)))
   if (beta)
     e = qg == 8 ? MISA_ROUTE_LAUNCH(true, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(true, 2) : MISA_ROUTE_LAUNCH(true, 1));
   else
     e = qg == 8 ? MISA_ROUTE_LAUNCH(false, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(false, 2) : MISA_ROUTE_LAUNCH(false, 1));
 #undef MISA_ROUTE_LAUNCH
+#undef MISA_ROUTE_LAUNCH1
   if (e != hipSuccess) return e;
   if (!heads && !r_out) return hipSuccess;  // block scores only
-  if (!rmax) return hipErrorInvalidValue;  // the ranking needs the maxima
-  const double div_full = kbar || max_pool ? 1.0 : (double)B;
-  if (f8)
-    return cx.launch("route_select", k_route_select<true>, dim3(T), dim3(256), 0, q, qscale, w, H, A, pos, L,
-                     div_full, (const unsigned long long*)rmax, (const double*)rtail, heads, r_out, qr, wr);
-  return cx.launch("route_select", k_route_select<false>, dim3(T), dim3(256), 0, q, qscale, w, H, A, pos, L,
-                   div_full, (const unsigned long long*)rmax, (const double*)rtail, heads, r_out, qr, wr);
+  if (beta) return hipErrorInvalidValue;     // the ranking reads the maxima pass
+  const double div_full = kbar ? 1.0 : (double)B;
+#define MISA_SELECT_LAUNCH(QF, KF)                                                                        \
+  cx.launch("route_select", k_route_select<QF, KF>, dim3(T), dim3(256), 0, q, qscale, w, H, A, pos, L, B, nt, \
+            div_full, (const double*)part, tsum, K, kscale, heads, r_out, qr, wr)
+  if (f8) return k_fp8 ? MISA_SELECT_LAUNCH(true, true) : MISA_SELECT_LAUNCH(true, false);
+  return k_fp8 ? MISA_SELECT_LAUNCH(false, true) : MISA_SELECT_LAUNCH(false, false);
+#undef MISA_SELECT_LAUNCH
 }
 
 hipError_t launch_gather_heads(const LaunchCtx& cx, const void* q, bool q_fp8, const float* qscale, const float* w,

@@ -128,12 +128,12 @@ __device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, TopkShare
 // inside it. Each thread reads its (at most 16) bins with vector loads, one
 // block scan orders the thread sums, and the owning thread finishes from
 // registers.
+// This thread's bins of hist[0, nb) for find_bin_in (h[i], i < nb / NT).
 template <int NT>
-__device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int rem, TopkShared<NT>& sm) {
+__device__ __forceinline__ void load_bins(const uint32_t* hist, int nb, uint32_t (&h)[16]) {
   const int tid = threadIdx.x;
   const int per = nb >= NT ? nb / NT : 1;
   const bool act = tid < (nb >= NT ? NT : nb);
-  uint32_t h[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) h[i] = 0u;
   if (act) {
@@ -155,6 +155,14 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int rem, 
       h[0] = hist[tid];
     }
   }
+}
+
+// find_bin over bins already loaded by load_bins.
+template <int NT>
+__device__ __forceinline__ void find_bin_in(const uint32_t (&h)[16], int nb, int rem, TopkShared<NT>& sm) {
+  const int tid = threadIdx.x;
+  const int per = nb >= NT ? nb / NT : 1;
+  const bool act = tid < (nb >= NT ? NT : nb);
   int local = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) local += (int)h[i];
@@ -174,6 +182,13 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int rem, 
     }
   }
   __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void find_bin(const uint32_t* hist, int nb, int rem, TopkShared<NT>& sm) {
+  uint32_t h[16];
+  load_bins<NT>(hist, nb, h);
+  find_bin_in<NT>(h, nb, rem, sm);
 }
 
 // tau = the rem-th largest of the c keys in sm.list (all-pairs count; c <=
@@ -644,9 +659,11 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* r
   uint32_t u[kGroups][4];
   bool in[kGroups][4];
   load_groups4<kGroups>(src, ws0, s1, lane, kWave, u, in);
+  uint32_t hb[16];  // the finished histogram, loaded beside the keys
+  load_bins<NT>(ghist + (size_t)row * kCoarseBins, kCoarseBins, hb);
   row_range<NT>(rmm, nmm, a.rows, row, sm);
   const float xlo = key_score(sm.umin), scale = lin_scale(xlo, key_score(sm.umax), kCoarseBins);
-  find_bin<NT>(ghist + (size_t)row * kCoarseBins, kCoarseBins, a.k, sm);
+  find_bin_in<NT>(hb, kCoarseBins, a.k, sm);
   const uint32_t bstar = (uint32_t)sm.digit;
   if (chunk == 0 && tid == 0) {
     LongRec r{};
@@ -749,22 +766,35 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
         }
     return;
   }
-  // ---- per-chunk counts (all issued together), then the region offsets
+  // ---- per-chunk counts and the first kPre keys of every region of the
+  // boundary list (all issued together), then the region offsets
   const int nc = (n + kChunk - 1) / kChunk;
   const int rem = (int)rec[row].rem;
+  const uint32_t* gk = bkeys + (size_t)row * rld;
+  constexpr int kPre = 32;                        // keys prefetched per region
+  constexpr int kPreRegions = 2 * NT * 4 / kPre;  // two 16-byte words per thread
+  u32x4 pf[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int wi = tid + NT * v, r = wi / (kPre / 4);
+    pf[v] = r < nc ? *reinterpret_cast<const u32x4*>(gk + (size_t)r * kChunk + 4 * (wi % (kPre / 4)))
+                   : u32x4{0u, 0u, 0u, 0u};
+  }
   int gt_before = 0;
+  bool spill = false;  // a region holds more keys than were prefetched
   for (int c0 = 0; c0 < nc; c0 += NT) {
     const int c = c0 + tid;
     const int bc = c < nc ? bcnt[(size_t)row * nch + c] : 0;
     if (c < chunk) gt_before += gcnt[(size_t)row * nch + c];
+    spill |= bc > (c < kPreRegions ? kPre : 0);
     int tot_c;
     const int inc = block_scan<NT>(bc, sm, &tot_c);
     if (c < nc) boff[c + 1] = (c0 > 0 ? boff[c0] : 0) + inc;
     if (c0 == 0 && tid == 0) boff[0] = 0;
     __syncthreads();
   }
+  spill = __syncthreads_or(spill);
   const int cb = boff[nc];
-  const uint32_t* gk = bkeys + (size_t)row * rld;
   // list item i lives in region c = the last with boff[c] <= i
   auto item = [=](int i) -> uint32_t {
     int lo = 0, hi = nc - 1;
@@ -777,11 +807,38 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
   const bool in_lds = cb <= kBoundaryCap;
   uint32_t lo = 0xffffffffu, hi = 0u;
   if (in_lds) {
-    for (int i = tid; i < cb; i += NT) {
-      const uint32_t x = item(i);
-      blist[i] = x;
-      lo = min(lo, x);
-      hi = max(hi, x);
+    // prefetched keys to their places; keys past a region's first kPre (or
+    // in regions past the prefetched ones) are read now
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int wi = tid + NT * v, r = wi / (kPre / 4), o = 4 * (wi % (kPre / 4));
+      if (r < nc) {
+        const int b0 = boff[r], bc = boff[r + 1] - b0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (o + e < bc) {
+            const uint32_t x = pf[v][e];
+            blist[b0 + o + e] = x;
+            lo = min(lo, x);
+            hi = max(hi, x);
+          }
+      }
+    }
+    if (spill) {
+      for (int i = tid; i < cb; i += NT) {
+        int r = 0, top = nc - 1;
+        while (r < top) {
+          const int mid = (r + top + 1) >> 1;
+          if (boff[mid] <= i) r = mid; else top = mid - 1;
+        }
+        const int k = i - boff[r];
+        if (k >= kPre || r >= kPreRegions) {
+          const uint32_t x = gk[(size_t)r * kChunk + k];
+          blist[i] = x;
+          lo = min(lo, x);
+          hi = max(hi, x);
+        }
+      }
     }
   } else {
     for (int i = tid; i < cb; i += NT) {
