@@ -577,19 +577,18 @@ __device__ __forceinline__ uint32_t coarse_bin(uint32_t u, float xlo, float scal
 // so the aligned group holding item s1 - 1 lies inside the row's storage: each
 // group is one 16-byte load from a clamped address, with no branch per group
 // (all G loads are in flight together).
+// The loads alone (load_raw4) and the conversion (keys4) are separate so that
+// a caller can issue its other reads in between: a use of a load's value makes
+// the compiler wait for every read issued before it.
 template <int G>
-__device__ __forceinline__ void load_groups4(const float* row, int s0, int s1, int j0, int dj,
-                                             uint32_t (&u)[G][4], bool (&in)[G][4]) {
-  f32x4 v[G];
-  if (s1 > s0) {
-    const int last = (s1 - 1) & ~3;
+__device__ __forceinline__ void load_raw4(const float* row, int s0, int s1, int j0, int dj, f32x4 (&v)[G]) {
+  const int last = s1 > s0 ? (s1 - 1) & ~3 : 0;  // an empty range reads item 0 (ignored)
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      v[g] = *reinterpret_cast<const f32x4*>(row + min(s0 + 4 * (j0 + dj * g), last));
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g) v[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int g = 0; g < G; ++g) v[g] = *reinterpret_cast<const f32x4*>(row + min(s0 + 4 * (j0 + dj * g), last));
+}
+template <int G>
+__device__ __forceinline__ void keys4(const f32x4 (&v)[G], int s0, int s1, int j0, int dj, uint32_t (&u)[G][4],
+                                      bool (&in)[G][4]) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int s = s0 + 4 * (j0 + dj * g);
@@ -599,6 +598,13 @@ __device__ __forceinline__ void load_groups4(const float* row, int s0, int s1, i
       u[g][e] = in[g][e] ? score_key(v[g][e]) : 0u;
     }
   }
+}
+template <int G>
+__device__ __forceinline__ void load_groups4(const float* row, int s0, int s1, int j0, int dj,
+                                             uint32_t (&u)[G][4], bool (&in)[G][4]) {
+  f32x4 v[G];
+  load_raw4<G>(row, s0, s1, j0, dj, v);
+  keys4<G>(v, s0, s1, j0, dj, u, in);
 }
 
 // Workgroup layout of a chunk in the count and emit passes: wave w owns the
@@ -751,41 +757,52 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
   const float* src = a.S + (size_t)row * a.S_ld;
   const int32_t* ri = a.row_idx ? a.row_idx + (size_t)row * a.idx_ld : nullptr;
   const int ws0 = s0 + w * (kChunk / NW);
-  uint32_t u[kGroups][4];
-  bool in[kGroups][4];
-  load_groups4<kGroups>(src, ws0, s1, lane, kWave, u, in);
-  if (take_all) {
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (in[g][e]) {
-          const int s = ws0 + 4 * (lane + kWave * g) + e;
-          oi[s] = ri ? ri[s] : s;
-          if (os) os[s] = key_score(u[g][e]);
-        }
-    return;
-  }
-  // ---- per-chunk counts and the first kPre keys of every region of the
-  // boundary list (all issued together), then the region offsets
+  // every read that does not depend on another is issued here, before any is
+  // used: the chunk's scores, the row record, the first NT chunks' counts and
+  // the first kPre keys of every region of the boundary list (with take_all
+  // the count pass did not run and these are ignored)
+  f32x4 sv[kGroups];
+  load_raw4<kGroups>(src, ws0, s1, lane, kWave, sv);
   const int nc = (n + kChunk - 1) / kChunk;
-  const int rem = (int)rec[row].rem;
+  const int rem_raw = (int)rec[row].rem;
   const uint32_t* gk = bkeys + (size_t)row * rld;
   constexpr int kPre = 32;                        // keys prefetched per region
   constexpr int kPreRegions = 2 * NT * 4 / kPre;  // two 16-byte words per thread
   u32x4 pf[2];
 #pragma unroll
   for (int v = 0; v < 2; ++v) {
-    const int wi = tid + NT * v, r = wi / (kPre / 4);
-    pf[v] = r < nc ? *reinterpret_cast<const u32x4*>(gk + (size_t)r * kChunk + 4 * (wi % (kPre / 4)))
-                   : u32x4{0u, 0u, 0u, 0u};
+    const int wi = tid + NT * v, r = min(wi / (kPre / 4), nch - 1);
+    pf[v] = *reinterpret_cast<const u32x4*>(gk + (size_t)r * kChunk + 4 * (wi % (kPre / 4)));
   }
+  const int bc0 = bcnt[(size_t)row * nch + min(tid, nch - 1)];
+  const int gc0 = gcnt[(size_t)row * nch + min(tid, nch - 1)];
+  if (take_all) {  // every item, scores as stored (-0 folded to +0)
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = ws0 + 4 * (lane + kWave * g) + e;
+        if (s < s1) {
+          oi[s] = ri ? ri[s] : s;
+          if (os) os[s] = sv[g][e] == 0.f ? 0.f : sv[g][e];
+        }
+      }
+    return;
+  }
+  uint32_t u[kGroups][4];
+  bool in[kGroups][4];
+  keys4<kGroups>(sv, ws0, s1, lane, kWave, u, in);
+  // ---- the region offsets of the concatenated boundary list
+  const int rem = rem_raw;
   int gt_before = 0;
   bool spill = false;  // a region holds more keys than were prefetched
   for (int c0 = 0; c0 < nc; c0 += NT) {
     const int c = c0 + tid;
-    const int bc = c < nc ? bcnt[(size_t)row * nch + c] : 0;
-    if (c < chunk) gt_before += gcnt[(size_t)row * nch + c];
+    const int cc = min(c, nch - 1);
+    const int bc_raw = c0 == 0 ? bc0 : bcnt[(size_t)row * nch + cc];
+    const int gc_raw = c0 == 0 ? gc0 : gcnt[(size_t)row * nch + cc];
+    const int bc = c < nc ? bc_raw : 0;
+    if (c < chunk) gt_before += gc_raw;
     spill |= bc > (c < kPreRegions ? kPre : 0);
     int tot_c;
     const int inc = block_scan<NT>(bc, sm, &tot_c);
