@@ -405,6 +405,67 @@ def stream_floor(byte_counts, grid=1024, min_rotation=600 << 20):
     return res
 
 
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """Summarise four rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of the
+    headline benchmark; then of the copy calibration) into
+    profiles/score_keys_c4_pmc.json and .md: the routed scoring kernel's
+    counters per launch (median over launches), each scaled by what the same
+    counter reads for a plain device copy of known size."""
+    import csv
+    import glob
+    import hashlib
+    import re
+
+    def per_dispatch(d, counter, name_re):
+        vals = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(path)):
+                if r.get("Counter_Name") == counter and re.search(name_re, r.get("Kernel_Name", "")):
+                    key = (path, r.get("Dispatch_Id"))
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return sorted(vals.values())
+
+    score_re = r"k_score_direct<\d+, \d+, \d+, (true|false), false"
+    f = per_dispatch(fetch_dir, "FETCH_SIZE", score_re)
+    w = per_dispatch(write_dir, "WRITE_SIZE", score_re)
+    cf = per_dispatch(copy_fetch_dir, "FETCH_SIZE", r"copyBuffer|copy_kernel|CopyKernel")
+    cw = per_dispatch(copy_write_dir, "WRITE_SIZE", r"copyBuffer|copy_kernel|CopyKernel")
+    if not (f and w and cf and cw):
+        raise SystemExit(f"pmc summary: missing counters (fetch {len(f)}, write {len(w)}, copy {len(cf)}, {len(cw)})")
+    copy_bytes = 256 << 20
+    cfk, cwk = float(np.median(cf[-3:])), float(np.median(cw[-3:]))  # the 256 MiB copies (largest)
+    fs, ws = copy_bytes / 1024 / cfk, copy_bytes / 1024 / cwk
+    fk, wk = float(np.median(f)), float(np.median(w))
+    src = os.path.join(ROOT, "sparse_attention_indexer_block_amd", "csrc", "score_kernels.hip")
+    rec = {"kernel": "k_score_direct (routed scoring, keys in position order)",
+           "workload": "c4_hier_decode_128k (T=8, L=131072, fp8 keys, A=8)",
+           "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "fetch_kib_per_launch_median": fk, "write_kib_per_launch_median": wk,
+           "launches_counted": [len(f), len(w)], "fetch_scale": fs, "write_scale": ws,
+           "calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": cfk, "copy_write_kib": cwk},
+           "hbm_bytes_per_launch": (fk * fs + wk * ws) * 1024, "commands": commands}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "score_keys_c4_pmc.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    import synth
+    algo = score_kernel_bytes(synth.CONFIGS["c4_hier_decode_128k"], 8)
+    md = ["# HBM traffic of the routed scoring kernel at c4_hier_decode_128k", "",
+          "Kernel: `k_score_direct` (key ranges, one launch per call).", "",
+          "Commands (repository root, each pass a run of its own), then the summary:", "", "```"]
+    md += commands + ["python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write "
+                      "gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write", "```", "",
+                      f"- FETCH_SIZE per launch (median of {len(f)}): {fk:.1f} KiB",
+                      f"- WRITE_SIZE per launch (median of {len(w)}): {wk:.1f} KiB",
+                      f"- copy calibration, 256 MiB device copy: FETCH_SIZE {cfk:.0f} KiB (scale {fs:.3f}), "
+                      f"WRITE_SIZE {cwk:.0f} KiB (scale {ws:.3f})",
+                      f"- HBM bytes per launch = FETCH*scale + WRITE*scale = {rec['hbm_bytes_per_launch'] / 1e6:.2f} MB",
+                      f"- algorithmic bytes per launch (keys + scales + routed q rows + w + pos): {algo / 1e6:.2f} MB; "
+                      "the score rows written are intermediate", ""]
+    with open(os.path.join(ROOT, "profiles", "score_keys_c4_pmc.md"), "w") as fh:
+        fh.write("\n".join(md))
+    print(json.dumps(rec))
+
+
 def traffic_from_profiles(kernel_tag):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 PMC
     summaries, or None when they are missing or the kernel source changed."""
@@ -434,7 +495,20 @@ def main():
     ap.add_argument("--only", default=None, metavar="PATH:WORKLOAD",
                     help="time one secondary line only (e.g. misa:c3_causal_prefill) and print it; "
                          "for profiling")
+    ap.add_argument("--pmc-summary", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="summarise four rocprofv3 --pmc runs into profiles/score_keys_c4_pmc.* (no GPU)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        B = "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra"
+        C = "python3 bench.py --copy-calibration 256"
+        d = args.pmc_summary
+        cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- {B}",
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- {B}",
+                f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[2]} -o run -- {C}",
+                f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[3]} -o run -- {C}"]
+        pmc_summary(*d, cmds)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         _fail_multi_gpu(max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))))
 

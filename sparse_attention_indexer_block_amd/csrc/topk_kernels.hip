@@ -28,7 +28,8 @@ constexpr int kCoarseBits = 10;
 constexpr int kCoarseBins = 1 << kCoarseBits;  // long rows: bins of the first pass
 constexpr int kFineBins = 2048;                  // rows in one workgroup
 constexpr int kListCap = 4096;     // survivors of the first radix digit kept in LDS
-constexpr int kRankCap = 512;      // lists this short are ranked pairwise instead of by digits
+constexpr int kRankCap = 128;      // lists this short are ranked pairwise instead of by digits
+constexpr int kPairCap = 64;       // threshold bins this short are ranked pairwise directly
 
 template <int NT>
 struct RegShared {
@@ -336,7 +337,6 @@ __device__ __forceinline__ void radix_threshold(KeyAt key_at, int n, int k, uint
 template <int NT, typename KeyAt>
 __device__ __forceinline__ void list_threshold(KeyAt key_at, int c, int rem, uint32_t umin, uint32_t umax,
                                                TopkShared<NT>& sm, uint32_t& tau, int& need_eq) {
-  constexpr int kPairCap = 64;
   constexpr int kSubBins = 1024;
   const int tid = threadIdx.x;
   if (c <= kPairCap) {
@@ -603,7 +603,15 @@ template <int G>
 __device__ __forceinline__ void load_groups4(const float* row, int s0, int s1, int j0, int dj,
                                              uint32_t (&u)[G][4], bool (&in)[G][4]) {
   f32x4 v[G];
-  load_raw4<G>(row, s0, s1, j0, dj, v);
+  if (s1 > s0) {
+    const int last = (s1 - 1) & ~3;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      v[g] = *reinterpret_cast<const f32x4*>(row + min(s0 + 4 * (j0 + dj * g), last));
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) v[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   keys4<G>(v, s0, s1, j0, dj, u, in);
 }
 
