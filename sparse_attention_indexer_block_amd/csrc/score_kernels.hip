@@ -335,6 +335,13 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   const int wr = wave / WC, wc = wave % WC;  // row group and key group of this wave
   const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
   const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
+  // The query lengths' inputs are the first reads (from always-valid
+  // addresses): the later wait for them then waits for nothing else.
+  const int tqc = min(g * QW + (tid < QW ? tid : 0), p.T - 1);
+  const int pos_raw = p.pos[tqc];
+  const int* ncnt = GATHER ? (p.blocks ? p.nblocks : p.ncand) : p.pos;
+  const int n_raw = ncnt[tqc];  // listed blocks or candidates (gather modes)
+  int last_raw = 0;             // block lists: the last listed block (requested below)
 
   // With several key waves per row group (WC > 1) the workgroup's q rows and
   // weights are loaded once into LDS (one pad word per row keeps the 16-byte
@@ -443,6 +450,33 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
 #pragma unroll
     for (int d = 0; d < D; ++d) load_group(d, d);
   }
+  // Gather modes: the first D groups' candidate indices, and then their key
+  // rows, are requested before the query's candidate count arrives, from
+  // positions clamped to the row's capacity and keys clamped to [0, L) (always
+  // valid rows); columns past the count are masked once it is known.
+  if constexpr (GATHER) {
+    const int bsz = p.blocks ? p.B : 1;
+    const long long cap = p.blocks ? p.blocks_ld * (long long)p.B : p.cand_ld;
+    const int* src = p.blocks ? p.blocks + (size_t)qt0 * p.blocks_ld : p.cand + (size_t)qt0 * p.cand_ld;
+    int iraw[D], off[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int col = (tile0 + d) * KT + 16 * wc + kcol;
+      const int cc = (int)min((long long)col, cap - 1);
+      const int blk = cc / bsz;
+      iraw[d] = src[blk];
+      off[d] = cc - blk * bsz;
+    }
+    // block lists: the query's last listed block (for its candidate count),
+    // requested here so that the count does not wait for the key rows
+    const int* lsrc = p.blocks ? p.blocks + (size_t)qt0 * p.blocks_ld : p.pos;
+    last_raw = lsrc[p.blocks ? min(max(n_raw - 1, 0), (int)p.blocks_ld - 1) : 0];
+    int kraw[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) kraw[d] = min(max(iraw[d] * bsz + off[d], 0), p.L - 1);
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_key(kraw[d], d);
+  }
 
   if (p.zero) {  // every workgroup clears its share
     const long long nthreads = 256ll * gridDim.x * gridDim.y;
@@ -456,15 +490,15 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
       if (GATHER && p.blocks) {
         // candidates = the visible keys of the listed blocks (ascending); only
         // the last listed block can be the query's partial last block
-        const int nb = p.nblocks[t];
+        const int nb = n_raw;
         if (nb > 0) {
-          const int last = p.blocks[(size_t)t * p.blocks_ld + nb - 1];
-          const long long tail = (long long)visible_len(p.pos[t], p.L) - (long long)last * p.B;
+          const int last = last_raw;
+          const long long tail = (long long)visible_len(pos_raw, p.L) - (long long)last * p.B;
           nn = (nb - 1) * p.B + (int)(tail < p.B ? tail : p.B);
         }
         if (split == 0) p.ncand_out[t] = nn;
       } else {
-        nn = GATHER ? p.ncand[t] : visible_len(p.pos[t], p.L);
+        nn = GATHER ? n_raw : visible_len(pos_raw, p.L);
       }
     }
     qn[tid] = nn;
@@ -557,12 +591,10 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   }
 
   if constexpr (GATHER) {
-    // key indices of the first D groups, all requested before any key row
-    int k0[D];
+    // the first D groups were requested before the count: mask their columns
 #pragma unroll
-    for (int d = 0; d < D; ++d) k0[d] = key_of(d);  // in bounds for any d (clamped)
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_key(k0[d], d);
+    for (int d = 0; d < D; ++d)
+      if ((tile0 + d) * KT + 16 * wc + kcol >= qn[0]) keyv[d] = -1;
   }
 
   // stores need no mask: a key past the query's candidates or visible length
