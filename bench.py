@@ -560,6 +560,7 @@ def main():
     traffic = traffic_from_profiles("score_keys")
     floor = stream_floor([algo_bytes])
     fr = floor["reads"][0]
+    floors_us = {algo_bytes: fr["stamped_us"]}  # streaming floor (kernel-stamped) by byte count
     # per-step milliseconds of each kernel family (launch averages times launches per step)
     per_step = {k: (v[0] * v[1] / args.steps if v[0] else 0.0) for k, v in kms.items()}
     sel_ms = sum(per_step[k] for k in ("topk_rows", "topk_hist", "topk_count", "topk_emit"))
@@ -654,9 +655,15 @@ def main():
                  "score_keys_avg_ms": k2["score_keys"][0], "score_gather_avg_ms": k2["score_gather"][0]}
             if k2["score_keys"][0]:
                 flops = 2.0 * (A or w2.A) * 128 * p2
+                sb = score_kernel_bytes(w2, A or w2.A, fp8q)
                 e["score_keys_tflops"] = flops / (k2["score_keys"][0] * 1e-3) / 1e12
-                e["score_keys_hbm_gbs"] = score_kernel_bytes(w2, A or w2.A, fp8q) / (k2["score_keys"][0] * 1e-3) / 1e9
+                e["score_keys_hbm_gbs"] = sb / (k2["score_keys"][0] * 1e-3) / 1e9
                 e["score_keys_hbm_frac"] = e["score_keys_hbm_gbs"] / HBM_PEAK_GBS
+                if "c3" not in nm:  # decode: the kernel against one plain read of its bytes
+                    if sb not in floors_us:
+                        floors_us[sb] = stream_floor([sb])["reads"][0]["stamped_us"]
+                    e["score_keys_stream_floor_ms"] = floors_us[sb] * 1e-3
+                    e["score_keys_vs_stream_floor"] = k2["score_keys"][0] / (floors_us[sb] * 1e-3)
                 if fp8q:  # fp8 x fp8 matrix cores: their own peak
                     e["score_keys_mfma_frac"] = e["score_keys_tflops"] / MFMA_FP8_PEAK_TFLOPS
                     e["compute"] = "fp8 e4m3 q and K, v_mfma_scale_f32_16x16x128_f8f6f4 (fp32 accumulate)"

@@ -171,3 +171,48 @@ def test_fp8q_unsupported_requests():
     # HISA takes any batch
     idx, sc = S.hisa_topk(q2, w2, K2, pos2, 128, 4, 50, ks2, q_scale=qs2)
     check_hisa(big, 128, 4, 50, _np(idx), _np(sc), label="fp8q hisa, many queries")
+
+
+@pytest.mark.parametrize("source", ["pooled", "arbitrary"])
+@pytest.mark.parametrize("L", [3000, 20000])
+def test_fp8q_cached_block_means(source, L):
+    """fp8 queries with cached block means: the head ranking launches no block-sum
+    pass and pools each query's last block itself (float64, code * scale exact)."""
+    inp = _case(71, 9, L, 64, positions="random" if L < 10000 else "decode")
+    q, w, K, ks, pos, qs = _gpu(inp)
+    B, A = 128, 8
+    M = -(-L // B)
+    if source == "pooled":
+        kbar = S.block_means(K, B, ks)
+    else:
+        rows = np.random.default_rng(L).standard_normal((M, 128)).astype(np.float32) * 0.2
+        kbar = torch.from_numpy(rows).cuda()
+    inp = dict(inp, kbar=_np(kbar))
+    P = oracle_problem(inp, B)
+    heads, r = S.route(q, w, K, pos, B, A, ks, with_r=True, kbar=kbar, q_scale=qs)
+    heads_o, ill = check_heads(P, A, _np(heads), _np(r))
+    assert ill == 0
+    idx, sc = S.score_topk(q, w, K, pos, B, A, 100, ks, kbar=kbar, q_scale=qs)
+    _check_misa(inp, B, A, 100, _np(idx), _np(sc), heads_o, label="fp8q cached misa")
+    idx, sc = S.hier_topk(q, w, K, pos, B, A, 600, 100, ks, kbar=kbar, q_scale=qs)
+    check_hier(inp, B, A, 600, 100, _np(idx), _np(sc), label="fp8q cached hier")
+    idx, sc = S.misa_hisa_topk(q, w, K, pos, B, A, 6, 100, ks, kbar=kbar, q_scale=qs)
+    check_misa_hisa(inp, B, A, 6, 100, _np(idx), _np(sc), heads_o, label="fp8q cached misa-hisa")
+
+
+def test_fp8q_cached_block_means_full_c4():
+    """The cached-means MISA-dagger step at the full 128K decode shape with fp8
+    queries: heads bit-exact, selections within the fp8 tolerance, and the same
+    call without a workspace (static scratch) bit for bit."""
+    wl = synth.CONFIGS["c4_hier_decode_128k"]
+    inp = synth.make_inputs(wl, seed=1, q_fp8=True)
+    q, w, K, ks, pos, qs = _gpu(inp)
+    kbar = S.block_means(K, wl.B, ks)
+    inp = dict(inp, kbar=_np(kbar))
+    heads = S.route(q, w, K, pos, wl.B, wl.A, ks, kbar=kbar, q_scale=qs)
+    heads_o, ill = check_heads(oracle_problem(inp, wl.B), wl.A, _np(heads))
+    assert ill == 0
+    idx, sc = S.hier_topk(q, w, K, pos, wl.B, wl.A, wl.kprime, wl.k, ks, kbar=kbar, q_scale=qs)
+    check_hier(inp, wl.B, wl.A, wl.kprime, wl.k, _np(idx), _np(sc), label="c4 fp8q cached hier")
+    i2, s2 = S.hier_topk_noalloc(q, w, K, pos, wl.B, wl.A, wl.kprime, wl.k, ks, kbar=kbar, q_scale=qs)
+    assert torch.equal(idx, i2) and torch.equal(sc, s2)
