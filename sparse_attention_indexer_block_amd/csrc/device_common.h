@@ -12,6 +12,7 @@ constexpr int kWave = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -39,12 +40,12 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t packed) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Two E4M3FN bytes -> two fp32 values (exact).
+// Two E4M3FN bytes -> two fp32 values (exact, one conversion instruction).
 template <bool HIGH_WORD>
 __device__ __forceinline__ void fp8x2_to_f32(uint32_t packed, float& a, float& b) {
-  uint32_t bb = fp8x2_to_bf16x2<HIGH_WORD>(packed);
-  a = __uint_as_float(bb << 16);
-  b = __uint_as_float(bb & 0xffff0000u);
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)packed, 1.0f, HIGH_WORD);
+  a = v.x;
+  b = v.y;
 }
 
 // Order-preserving map float -> uint32 (larger float -> larger key); -0.0 is

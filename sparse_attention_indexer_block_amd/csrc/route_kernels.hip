@@ -48,8 +48,9 @@ struct KeySlice {
 
 // Sum of key rows [s0, s1) in float64, one workgroup of NTH threads;
 // thread (rl, dg) takes rows rl, rl + RL, ... and one 16-byte slice of dims. A
-// whole 128-key block's rows of a thread (8 fp8 or 16 bf16 slices) are loaded
-// before any is added, so the loads overlap. Column sums
+// whole 128-key block's rows of a thread (U slices) are loaded
+// before any is added, so the loads overlap. Column sums of RR row groups
+// (FOLD: the upper half of the RL row groups first added into the lower half)
 // are left in red for the caller to add up: value e of slice dg of row group rl
 // sits at red[rl * kRedStride + e * NG + dg] (so one store instruction of a wave
 // covers contiguous doubles, and the padded row stride puts alternate row
@@ -58,17 +59,18 @@ struct KeySlice {
 // MAX: per-dimension maximum instead of the sum (max-pooled representatives;
 // exact, the widened values being exact in float64).
 constexpr int kRedStride = kHeadDim + 8;  // doubles per row group of the reduction buffer
-// 128 threads keep the reduction buffer at 17 KiB (fp8) so that every
-// workgroup of a 128K-key problem (1024 blocks plus the query tails) is
-// resident at once; with 256 threads a second round of workgroups waited for
-// the first to finish.
-constexpr int kSumThreads = 128;
+// Four waves per block, so that a workgroup whose rows arrive last adds them
+// up on all four SIMDs of its CU; the reduction buffer is folded once (FOLD)
+// to stay at 17 KiB, so that every workgroup of a 128K-key problem (1024
+// blocks plus the query tails) is resident at once.
+constexpr int kSumThreads = 256;
 
-template <bool FP8, bool MAX = false, int NTH = kSumThreads>
+template <bool FP8, bool MAX = false, int NTH = kSumThreads, bool FOLD = false>
 struct RowSum {
   static constexpr int DPT = KeySlice<FP8>::DPT;
   static constexpr int NG = kHeadDim / DPT;  // slices per key
   static constexpr int RL = NTH / NG;        // row groups
+  static constexpr int RR = FOLD ? RL / 2 : RL;  // row groups left in the reduction buffer
   static constexpr int U = 128 / RL;         // rows per thread per pass (128 keys per pass)
   static __device__ __forceinline__ int dim_of(int c) { return (c % NG) * DPT + c / NG; }
   static __device__ __forceinline__ void run(const void* K, const float* kscale, int s0, int s1, double* red) {
@@ -106,8 +108,30 @@ struct RowSum {
         }
       }
     }
+    if constexpr (FOLD) {
+      // the upper half of the row groups hands its partials to the lower half
+      if (rl >= RR) {
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) red[rl * kRedStride + e * NG + dg] = acc[e];
+        for (int e = 0; e < DPT; ++e) red[(rl - RR) * kRedStride + e * NG + dg] = acc[e];
+      }
+      __syncthreads();
+      if (rl < RR) {
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) {
+          const double y = red[rl * kRedStride + e * NG + dg];
+          if constexpr (MAX) acc[e] = y > acc[e] ? y : acc[e];
+          else acc[e] += y;
+        }
+      }
+      __syncthreads();
+      if (rl < RR) {
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) red[rl * kRedStride + e * NG + dg] = acc[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) red[rl * kRedStride + e * NG + dg] = acc[e];
+    }
     __syncthreads();
   }
 };
@@ -126,8 +150,8 @@ __global__ __launch_bounds__(kSumThreads) void k_block_sums(const void* K, const
                                                     int B, int M, double* ksum, float* kbar,
                                                     uint16_t* kb16, const int32_t* pos, double* tsum,
                                                     int ntail, int b_base) {
-  using RS = RowSum<FP8, MAX>;
-  constexpr int RL = RS::RL;
+  using RS = RowSum<FP8, MAX, kSumThreads, true>;
+  constexpr int RL = RS::RR;
   __shared__ double red[RL * kRedStride];
   const int wg = (int)blockIdx.x;
   const bool is_tail = wg < ntail;
