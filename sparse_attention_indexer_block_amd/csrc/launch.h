@@ -78,8 +78,9 @@ int route_chunks(int L, int B);
 // per-head maxima of the complete blocks before each query's last block into
 // part[T, route_chunks(L, B), 64] (float64; every slot read is written, no
 // clearing) and, with tsum, the last block's value into the T * 64 doubles
-// after them; then one workgroup per query takes that value or, when tsum is
-// null, pools the last block from K / kscale itself, ranks the heads
+// after them (when tsum is null, which needs cached means kbar, an extra
+// workgroup column of the router launch pools each query's last block from
+// K / kscale into those slots instead); then one workgroup per query ranks the heads
 // and writes heads[T,A] (ascending), optional r[T,H] and optionally the routed
 // q rows qr[T,A,128] and weights wr[T,A] packed in slot order (so scoring
 // needs no head indirection). ksum (or kbar) must hold the complete blocks.

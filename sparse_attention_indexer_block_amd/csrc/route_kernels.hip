@@ -235,22 +235,106 @@ __device__ __forceinline__ double row_max16(double v) {
   return dpp_max<0x128>(v);  // row_ror:8
 }
 
+// The last, possibly partial block [(M_t - 1) B, n_t) of query t, pooled from
+// the keys in float64 by one workgroup of 256 threads, and ReLU(q . sum /
+// count) of every head into slot[0, 64) (heads past H get unused values).
+// Thread (h, j) forms head h over dims [32 j, 32 j + 32); the four partial
+// products are added in the order j = 0, 1, 2, 3.
+template <bool KF8, bool QF8>
+__device__ __forceinline__ void route_tail(const void* q, const float* qscale, int H, int t, int n, int B,
+                                           const void* K, const float* kscale, double* slot) {
+  using RS = RowSum<KF8, false, 256, true>;
+  constexpr int RB = QF8 ? kHeadDim : 2 * kHeadDim;  // bytes per q row
+  constexpr int QW = RB / 64;                          // 16-byte words of a thread's 32 dims
+  __shared__ double red[RS::RR * kRedStride];
+  __shared__ double tl[kHeadDim];  // the last block's key sum
+  __shared__ double pd[4][kWave];  // products over 32 dims
+  const int tid = threadIdx.x, h = tid & 63, j = tid >> 6;
+  const int hc = h < H ? h : 0;
+  const int Mt = (int)(((long long)n + B - 1) / B);
+  const int s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
+  // the q row and its scale are requested before the keys (used after them)
+  u32x4 qd[QW];
+  {
+    const u32x4* row = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) +
+                                                      ((size_t)t * H + hc) * RB) + QW * j;
+#pragma unroll
+    for (int v = 0; v < QW; ++v) qd[v] = row[v];
+  }
+  const float sc = QF8 ? qscale[(size_t)t * H + hc] : 1.f;
+  RS::run(K, kscale, s0, n, red);  // synchronises
+  if (tid < kHeadDim) {
+    double sum = 0.0;
+#pragma unroll
+    for (int r = 0; r < RS::RR; ++r) sum += red[r * kRedStride + tid];
+    tl[RS::dim_of(tid)] = sum;
+  }
+  __syncthreads();
+  double dp = 0.0;
+  if constexpr (QF8) {
+    const double qsc = (double)sc;  // code * scale is exact in float64
+#pragma unroll
+    for (int v = 0; v < QW; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float a0, a1, a2, a3;
+        fp8x2_to_f32<false>(qd[v][c], a0, a1);
+        fp8x2_to_f32<true>(qd[v][c], a2, a3);
+        const int d = 32 * j + 16 * v + 4 * c;
+        dp += ((double)a0 * qsc) * tl[d];
+        dp += ((double)a1 * qsc) * tl[d + 1];
+        dp += ((double)a2 * qsc) * tl[d + 2];
+        dp += ((double)a3 * qsc) * tl[d + 3];
+      }
+  } else {
+#pragma unroll
+    for (int v = 0; v < QW; ++v)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d = 32 * j + 8 * v + 2 * c;
+        dp += (double)bf16_bits_to_f32(qd[v][c] & 0xffffu) * tl[d];
+        dp += (double)bf16_bits_to_f32(qd[v][c] >> 16) * tl[d + 1];
+      }
+  }
+  pd[j][h] = dp;
+  __syncthreads();
+  if (j == 0) {
+    const double dt = ((pd[0][h] + pd[1][h]) + pd[2][h]) + pd[3][h];
+    const double v = Mt > 0 ? dt / (double)(n - s0) : 0.0;  // the block's own count of keys
+    slot[h] = v > 0.0 ? v : 0.0;
+  }
+  __syncthreads();  // the buffers are reused by the group's next query
+}
+
 // QF8: q holds E4M3FN codes with one scale per (query, head) in qscale (null:
 // scale 1, rows that already carry their scales); the value code * scale is
 // formed exactly in float64.
 // MEANS: the complete blocks come as cached float means (kbar), else as float64
 // sums (ksum).
-template <bool WITH_BETA, int kRouteQG, bool QF8, bool MEANS>
+// TK (head ranking with cached means, no pooled tails): workgroup column 0
+// pools every query's last block from K (TK = 1: bf16 keys, 2: fp8 keys with
+// kscale) into the slot after the tile maxima; the tiles are columns 1 .. ntiles.
+template <bool WITH_BETA, int kRouteQG, bool QF8, bool MEANS, int TK>
 __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* qscale, const float* w,
                                                     const int32_t* pos, int T, int H, int L, int B,
                                                     int ntiles, const double* ksum,
                                                     const float* kbar, const double* tsum,
+                                                    const void* K, const float* kscale,
                                                     double* part, float* beta, int beta_ld,
                                                     int max_pool) {
   __shared__ f64x2 kt[kRouteTile][kHeadDim / 2 + 1];  // padded rows
   __shared__ double bsum[4][kRouteTile];
   __shared__ f64x2 tls[kRouteQG][kHeadDim / 2];  // the group's query tail sums
-  const int tile = blockIdx.x, tq0 = blockIdx.y * kRouteQG;
+  if constexpr (TK != 0) {
+    if (blockIdx.x == 0) {  // uniform: the query group's last blocks
+      const int tq = blockIdx.y * kRouteQG;
+      for (int i = 0; i < kRouteQG && tq + i < T; ++i)
+        route_tail<TK == 2, QF8>(q, qscale, H, tq + i, visible_len(pos[tq + i], L), B, K, kscale,
+                                 part + ((size_t)T * ntiles + tq + i) * kWave);
+      return;
+    }
+  }
+  const int tile = (int)blockIdx.x - (TK != 0 ? 1 : 0), tq0 = blockIdx.y * kRouteQG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
@@ -340,7 +424,7 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
     const int Mt = (int)(((long long)n + B - 1) / B);
     // every visible block, the last one from the query's tail sum when the
     // block-sum pass pooled it (tsum); otherwise (cached means, head ranking)
-    // the complete blocks only: the ranking kernel pools the last block itself
+    // the complete blocks only: column 0 pools the last block
     const bool with_tail = WITH_BETA || tsum != nullptr;  // uniform
     const int Mc = with_tail ? Mt : Mt - 1;
     if (b0 >= Mc) continue;  // uniform: no block of this tile is taken
@@ -426,30 +510,23 @@ __global__ __launch_bounds__(256) void k_route_mfma(const void* q, const float* 
 // r(t,h) = w[t,h] * max(the complete blocks' maximum, ReLU(rho of the last
 // block)), then the first A heads under (-r, h). The complete blocks' maxima
 // come from the router tiles (part: raw products, divided here once by
-// div_full, the block size, or 1 for cached means). The query's last block
-// [(M_t - 1) B, n_t), possibly partial, comes from the block-sum pass (tsum)
-// or, when tsum is null (cached means: no block-sum pass), is pooled here from
-// the keys in float64; its rho = q . sum / count is formed for every head
-// (thread (h, j) takes head h over dims [32 j, 32 j + 32)). heads[t,:] is written in
+// div_full, the block size, or 1 for cached means), and the last block's
+// ReLU(rho) from the slot after them (written by the tile holding that block
+// from the block-sum pass's tail sum, or by the router's tail workgroups with
+// cached means). heads[t,:] is written in
 // ascending head order; with qr the routed q rows and weights are packed in the
 // same order for the scoring kernel. QF8: the rows are fp8 codes; a packed row
 // is the head's codes with the sign of its scale folded in (bit 7 flipped when
 // the scale is negative) and its weight is w * |scale|, so that
 // w * ReLU(q . k) of the packed row equals the head's term.
-template <bool QF8, bool KF8>
+template <bool QF8>
 __global__ __launch_bounds__(256) void k_route_select(const void* q, const float* qscale, const float* w, int H,
                                                      int A, const int32_t* pos, int L, int B, int ntiles,
-                                                     double div_full, const double* part, const double* tsum,
-                                                     const void* K, const float* kscale, int32_t* heads,
+                                                     double div_full, const double* part, int32_t* heads,
                                                      float* r_out, void* qr, float* wr) {
-  using RS = RowSum<KF8, false, 256>;
   constexpr int RB = QF8 ? kHeadDim : 2 * kHeadDim;  // bytes per q row
   constexpr int RW = RB / 16;                          // 16-byte words per q row
-  constexpr int QW = RW / 4;                           // words of a thread's 32 dims
-  __shared__ double red[RS::RL * kRedStride];
-  __shared__ double tl[kHeadDim];  // the last block's key sum
   __shared__ double pm[4][kWave];  // complete blocks' maxima, per thread group
-  __shared__ double pd[4][kWave];  // last-block products over 32 dims
   __shared__ double rs[kWave];
   __shared__ int rank_part[4][kWave];
   __shared__ u32x4 qs[kWave * RW];  // q[t] as 16-byte words
@@ -457,20 +534,12 @@ __global__ __launch_bounds__(256) void k_route_select(const void* q, const float
   const bool active = h < H;
   const int n = visible_len(pos[t], L);
   const int Mt = (int)(((long long)n + B - 1) / B);
-  const int s0 = Mt > 0 ? (int)((long long)(Mt - 1) * B) : 0;
   const int nc = Mt > 1 ? (Mt - 1 + kRouteTile - 1) / kRouteTile : 0;  // tiles with complete blocks
   // every global read is issued up front from an address that is always valid
   // (a load inside a condition is waited for inside it); values are masked after
   const int hc = active ? h : 0;
   const float wt_raw = w[(size_t)t * H + hc];
   const float sc_raw = QF8 ? qscale[(size_t)t * H + hc] : 1.f;
-  u32x4 qd[QW];  // this thread's 32 dims of q[t,h]
-  {
-    const u32x4* row = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(q) +
-                                                      ((size_t)t * H + hc) * RB) + QW * j;
-#pragma unroll
-    for (int v = 0; v < QW; ++v) qd[v] = row[v];
-  }
   const int nw = H * RW;  // 16-byte words of q[t]
   u32x4 qst[4];  // q[t] for the packed rows (read even when not packed: no branch to wait in)
   {
@@ -480,7 +549,7 @@ __global__ __launch_bounds__(256) void k_route_select(const void* q, const float
   }
   // every tile's slot is requested before the query's length arrives (slots
   // past its complete blocks hold stale values and are masked afterwards)
-  const double mt_raw = tsum ? part[((size_t)gridDim.x * ntiles + t) * kWave + h] : 0.0;  // gridDim.x = T
+  const double mt_raw = part[((size_t)gridDim.x * ntiles + t) * kWave + h];  // gridDim.x = T
   double m = 0.0;  // values >= +0.0
   for (int c0 = 0; c0 < ntiles; c0 += 64) {  // 16 loads in flight per thread
     double x[16];
@@ -497,53 +566,7 @@ __global__ __launch_bounds__(256) void k_route_select(const void* q, const float
     for (int u = 0; u < 4; ++u)
       if (tid + 256 * u < nw) qs[tid + 256 * u] = qst[u];
   }
-  // the last block's ReLU(rho): from the router tiles when the block-sum pass
-  // pooled the tails, else pooled and scored here
-  double mtail = 0.0;
-  if (tsum) {
-    mtail = Mt > 0 ? mt_raw : 0.0;
-  } else {
-    RS::run(K, kscale, s0, n, red);  // synchronises
-    if (tid < kHeadDim) {
-      double sum = 0.0;
-#pragma unroll
-      for (int r = 0; r < RS::RL; ++r) sum += red[r * kRedStride + tid];
-      tl[RS::dim_of(tid)] = sum;
-    }
-    __syncthreads();
-    double dp = 0.0;
-    if constexpr (QF8) {
-      const double qsc = (double)sc;  // code * scale is exact in float64
-#pragma unroll
-      for (int v = 0; v < QW; ++v)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float a0, a1, a2, a3;
-          fp8x2_to_f32<false>(qd[v][c], a0, a1);
-          fp8x2_to_f32<true>(qd[v][c], a2, a3);
-          const int d = 32 * j + 16 * v + 4 * c;
-          dp += ((double)a0 * qsc) * tl[d];
-          dp += ((double)a1 * qsc) * tl[d + 1];
-          dp += ((double)a2 * qsc) * tl[d + 2];
-          dp += ((double)a3 * qsc) * tl[d + 3];
-        }
-    } else {
-#pragma unroll
-      for (int v = 0; v < QW; ++v)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int d = 32 * j + 8 * v + 2 * c;
-          dp += (double)bf16_bits_to_f32(qd[v][c] & 0xffffu) * tl[d];
-          dp += (double)bf16_bits_to_f32(qd[v][c] >> 16) * tl[d + 1];
-        }
-    }
-    pd[j][h] = dp;
-    __syncthreads();
-    if (j == 0 && Mt > 0) {
-      const double dt = ((pd[0][h] + pd[1][h]) + pd[2][h]) + pd[3][h];
-      mtail = dt / (double)(n - s0);  // the last block: its own count of keys
-    }
-  }
+  const double mtail = Mt > 0 ? mt_raw : 0.0;  // the last block's ReLU(rho)
   __syncthreads();  // pm complete
   if (j == 0) {
     double mfull = pm[0][h];
@@ -653,28 +676,35 @@ hipError_t launch_route(const LaunchCtx& cx, const void* q, bool q_fp8, const fl
   // that, groups of queries share each staged tile
   const long long work = (long long)nt * T;
   const int qg = work > 16384 ? 8 : (work > 2048 ? 2 : 1);
-  const dim3 grid(nt, (T + qg - 1) / qg);
-#define MISA_ROUTE_LAUNCH1(BETA, QG, QF, MN)                                                              \
-  cx.launch("route_mfma", k_route_mfma<BETA, QG, QF, MN>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, B, nt, \
-            ksum, kbar, tsum, part, beta, beta_ld, max_pool ? 1 : 0)
-#define MISA_ROUTE_LAUNCH(BETA, QG)                                                                  \
-  (f8 ? (kbar ? MISA_ROUTE_LAUNCH1(BETA, QG, true, true) : MISA_ROUTE_LAUNCH1(BETA, QG, true, false)) \
-      : (kbar ? MISA_ROUTE_LAUNCH1(BETA, QG, false, true) : MISA_ROUTE_LAUNCH1(BETA, QG, false, false)))
+  // head ranking without pooled tails (cached means): the launch's column 0
+  // pools the queries' last blocks from the keys
+  const bool pool_tails = !beta && tsum == nullptr;
+  if (pool_tails && (kbar == nullptr || K == nullptr)) return hipErrorInvalidValue;
+  const dim3 grid(nt + (pool_tails ? 1 : 0), (T + qg - 1) / qg);
+#define MISA_ROUTE_LAUNCH1(BETA, QG, QF, MN, TKV)                                                         \
+  cx.launch("route_mfma", k_route_mfma<BETA, QG, QF, MN, TKV>, grid, dim3(256), 0, q, qscale, w, pos, T, H, L, B, \
+            nt, ksum, kbar, tsum, K, kscale, part, beta, beta_ld, max_pool ? 1 : 0)
+#define MISA_ROUTE_POOL(QG, QF) \
+  (k_fp8 ? MISA_ROUTE_LAUNCH1(false, QG, QF, true, 2) : MISA_ROUTE_LAUNCH1(false, QG, QF, true, 1))
+#define MISA_ROUTE_LAUNCH(BETA, QG)                                                                        \
+  (pool_tails ? (f8 ? MISA_ROUTE_POOL(QG, true) : MISA_ROUTE_POOL(QG, false))                              \
+   : f8 ? (kbar ? MISA_ROUTE_LAUNCH1(BETA, QG, true, true, 0) : MISA_ROUTE_LAUNCH1(BETA, QG, true, false, 0)) \
+        : (kbar ? MISA_ROUTE_LAUNCH1(BETA, QG, false, true, 0) : MISA_ROUTE_LAUNCH1(BETA, QG, false, false, 0)))
   if (beta)
     e = qg == 8 ? MISA_ROUTE_LAUNCH(true, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(true, 2) : MISA_ROUTE_LAUNCH(true, 1));
   else
     e = qg == 8 ? MISA_ROUTE_LAUNCH(false, 8) : (qg == 2 ? MISA_ROUTE_LAUNCH(false, 2) : MISA_ROUTE_LAUNCH(false, 1));
 #undef MISA_ROUTE_LAUNCH
+#undef MISA_ROUTE_POOL
 #undef MISA_ROUTE_LAUNCH1
   if (e != hipSuccess) return e;
   if (!heads && !r_out) return hipSuccess;  // block scores only
   if (beta) return hipErrorInvalidValue;     // the ranking reads the maxima pass
   const double div_full = kbar ? 1.0 : (double)B;
-#define MISA_SELECT_LAUNCH(QF, KF)                                                                        \
-  cx.launch("route_select", k_route_select<QF, KF>, dim3(T), dim3(256), 0, q, qscale, w, H, A, pos, L, B, nt, \
-            div_full, (const double*)part, tsum, K, kscale, heads, r_out, qr, wr)
-  if (f8) return k_fp8 ? MISA_SELECT_LAUNCH(true, true) : MISA_SELECT_LAUNCH(true, false);
-  return k_fp8 ? MISA_SELECT_LAUNCH(false, true) : MISA_SELECT_LAUNCH(false, false);
+#define MISA_SELECT_LAUNCH(QF)                                                                          \
+  cx.launch("route_select", k_route_select<QF>, dim3(T), dim3(256), 0, q, qscale, w, H, A, pos, L, B, nt, \
+            div_full, (const double*)part, heads, r_out, qr, wr)
+  return f8 ? MISA_SELECT_LAUNCH(true) : MISA_SELECT_LAUNCH(false);
 #undef MISA_SELECT_LAUNCH
 }
 
