@@ -1044,9 +1044,9 @@ __device__ __forceinline__ void reg_threshold(const uint32_t (&u)[G][4], In in, 
 
 // Emit the selection in item order: items with key > tau, plus the first
 // need_eq items equal to tau (all items when take_all). Writes positions below
-// k only.
+// k only. Only the wave's first gl groups hold items (gl uniform over the wave).
 template <int NT, int G, bool WITH_SCORE, typename In, typename IdxOf>
-__device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], In in, int seg0,
+__device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], In in, int seg0, int gl,
                                          bool take_all, uint32_t tau, int need_eq, int k,
                                          RegShared<NT>& sm, IdxOf idx_of, int32_t* out_idx,
                                          float* out_score) {
@@ -1057,6 +1057,8 @@ __device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], In in, int s
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     int c = 0;
+    cnt[g] = 0;
+    if (g >= gl) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool gt = in(g, e) && (take_all || u[g][e] > tau);
@@ -1072,6 +1074,7 @@ __device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], In in, int s
     sm.weq[w] = tot >> 16;
   }
   __syncthreads();
+  if (gl == 0) return;  // uniform: no item in this wave
   int gt_run = 0, eq_run = 0;
   for (int i = 0; i < w; ++i) {
     gt_run += sm.wgt[i];
@@ -1079,6 +1082,7 @@ __device__ __forceinline__ void reg_emit(const uint32_t (&u)[G][4], In in, int s
   }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    if (g >= gl) break;  // uniform
     const int inc = wave_inclusive_scan(cnt[g]);
     const int exc = inc - cnt[g];
     int gt_b = gt_run + (exc & 0xffff), eq_b = eq_run + (exc >> 16);
@@ -1122,12 +1126,39 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
   const int n = min(row_length(a, row), NT * 4 * G);
   const int seg0 = w * 256 * G;
   const float* src = a.S + (size_t)row * a.S_ld;
+  const int nrel = n - seg0;  // items of this wave's segment that exist (may be <= 0)
+  // Rows of up to 16,384 items (G = 4), mostly shorter: gl counts the wave's
+  // groups that hold items (uniform), and every per-item loop stops at the
+  // first group past the row's end, so waves and groups beyond a short row
+  // issue no per-item work (C3's causal rows: 0.46 ms against 0.58 ms). The
+  // smaller forms, whose rows are mostly full, keep every group (gl = G).
+  constexpr bool kSkip = G >= 4;
+  const int gl = kSkip ? __builtin_amdgcn_readfirstlane(nrel <= 0 ? 0 : min(G, (nrel + 4 * kWave - 1) / (4 * kWave)))
+                       : G;
   uint32_t u[G][4];
-  {
+  if constexpr (kSkip) {
+    f32x4 v[G];
+    if (nrel > 0) {
+      const int last = (n - 1) & ~3;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        v[g] = *reinterpret_cast<const f32x4*>(src + min(seg0 + 4 * (lane + kWave * g), last));
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[g][e] = 0u;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g >= gl) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        u[g][e] = 4 * (lane + kWave * g) + e < nrel ? score_key(v[g][e]) : 0u;
+    }
+  } else {
     bool unused[G][4];
     load_groups4<G>(src, seg0, n, lane, kWave, u, unused);
   }
-  const int nrel = n - seg0;  // items of this wave's segment that exist (may be <= 0)
   auto in = [=](int g, int e) { return 4 * (lane + kWave * g) + e < nrel; };
   i32x4 ix[IDX ? G : 1];
   if constexpr (IDX) {
@@ -1149,13 +1180,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
   if (!take_all) {
     uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      if (g >= gl) break;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (in(g, e)) {
           lo = min(lo, u[g][e]);
           hi = max(hi, u[g][e]);
         }
+    }
     for (int b = tid; b < kFineBins; b += NT) sm.hist[b] = 0u;
     if (tid == 0) {
       sm.ncand = 0;
@@ -1166,10 +1199,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
     const float xlo = key_score(sm.umin);
     const float scale = lin_scale(xlo, key_score(sm.umax), kFineBins);
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      if (g >= gl) break;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (in(g, e)) atomicAdd(&sm.hist[lin_bin(u[g][e], xlo, scale, kFineBins)], 1u);
+    }
     __syncthreads();
     find_bin<NT>(sm.hist, kFineBins, k, sm);
     const uint32_t bstar = (uint32_t)sm.digit;
@@ -1184,7 +1219,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
       uint32_t kbits = 0u, clo = 0xffffffffu, chi = 0u;
       int wcnt = 0;
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
+        if (g >= gl) break;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool kp = in(g, e) && lin_bin(u[g][e], xlo, scale, kFineBins) == bstar;
@@ -1195,12 +1231,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
             chi = max(chi, u[g][e]);
           }
         }
+      }
       if (wcnt) {  // uniform: one slot range per wave, taken with one atomic
         int at = 0;
         if (lane == 0) at = atomicAdd(&sm.ncand, wcnt);
         at = __shfl(at, 0, kWave);
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+          if (g >= gl) break;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool kp = (kbits >> (4 * g + e)) & 1u;
@@ -1208,6 +1246,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
             if (kp) dst[at + lanes_below(m)] = u[g][e];
             at += __popcll(m);
           }
+        }
         if (need_ext) {
           clo = wave_min_u32(clo);
           chi = wave_max_u32(chi);
@@ -1236,8 +1275,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 1024 &
     if constexpr (IDX) return ix[g][e];
     else return s;
   };
-  if (os) reg_emit<NT, G, true>(u, in, seg0, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
-  else reg_emit<NT, G, false>(u, in, seg0, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
+  if (os) reg_emit<NT, G, true>(u, in, seg0, gl, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
+  else reg_emit<NT, G, false>(u, in, seg0, gl, take_all, tau, need_eq, k, sm.reg, idx_of, oi, os);
   const int nsel = take_all ? n : k;
   for (int p = nsel + tid; p < k; p += NT) {
     oi[p] = -1;
