@@ -313,8 +313,9 @@ static TopkLongWs long_ws(const Plan& pl, void* ws, int nmm) {
 // `nmm` > 0 means the scoring kernel already wrote it (and cleared the
 // selection counters); otherwise a range pass runs first.
 static misa_status run_topk(const LaunchCtx& cx, const TopkArgs& a, const Plan& pl, void* ws,
-                            int max_n, int nmm = 0) {
+                            int max_n, int nmm = 0, const RerankArgs* rr = nullptr) {
   if (max_n <= topk_lds_cap()) {
+    if (rr) return fail(MISA_ERR_HIP, "internal: the rerank form needs long rows");
     HIP_TRY(launch_topk_rows(cx, a, max_n), "top-k");
     return MISA_OK;
   }
@@ -324,7 +325,7 @@ static misa_status run_topk(const LaunchCtx& cx, const TopkArgs& a, const Plan& 
             "top-k range");
     nmm = topk_long_chunks(max_n);
   }
-  HIP_TRY(launch_topk_long(cx, a, long_ws(pl, ws, nmm), max_n), "top-k (long rows)");
+  HIP_TRY(launch_topk_long(cx, a, long_ws(pl, ws, nmm), max_n, rr), "top-k (long rows)");
   return MISA_OK;
 }
 
@@ -470,16 +471,32 @@ static misa_status run_hier(const LaunchCtx& cx, const misa_problem* p, const Pl
   ta.out_idx = cand;
   ta.out_ld = pl.cand_ld;
   ta.out_count = ncand;
-  MISA_TRY(run_topk(cx, ta, pl, ws, p->L, nmm));
-  // fine stage: all H heads rescore the candidates, then top-k
-  ScoreArgs sa = score_args(p);
-  sa.cand = cand;
-  sa.cand_ld = pl.cand_ld;
-  sa.cand_max = kc;
-  sa.ncand = ncand;
-  sa.S = at<float>(ws, pl.S2);
-  sa.S_ld = pl.S2_ld;
-  HIP_TRY(launch_score_gather(cx, sa, p->k_dtype == MISA_K_FP8_E4M3FN), "rerank scoring");
+  // fine stage: all H heads rescore the candidates, then top-k. Long rows with
+  // bf16 queries rescore each chunk's kept candidates inside the emission
+  // pass; otherwise the gather form of the scoring kernel rescores the list.
+  const bool fp8k = p->k_dtype == MISA_K_FP8_E4M3FN;
+  if (p->L > topk_lds_cap() && p->q_dtype != MISA_Q_FP8_E4M3FN) {
+    RerankArgs rr;
+    rr.q = static_cast<const uint16_t*>(p->q);
+    rr.w = p->w;
+    rr.H = p->H;
+    rr.K = p->K;
+    rr.kscale = p->k_scale;
+    rr.fp8 = fp8k;
+    rr.S = at<float>(ws, pl.S2);
+    rr.S_ld = pl.S2_ld;
+    MISA_TRY(run_topk(cx, ta, pl, ws, p->L, nmm, &rr));
+  } else {
+    MISA_TRY(run_topk(cx, ta, pl, ws, p->L, nmm));
+    ScoreArgs sa = score_args(p);
+    sa.cand = cand;
+    sa.cand_ld = pl.cand_ld;
+    sa.cand_max = kc;
+    sa.ncand = ncand;
+    sa.S = at<float>(ws, pl.S2);
+    sa.S_ld = pl.S2_ld;
+    HIP_TRY(launch_score_gather(cx, sa, fp8k), "rerank scoring");
+  }
   TopkArgs tb = topk_args(p);
   tb.S = at<float>(ws, pl.S2);
   tb.S_ld = pl.S2_ld;

@@ -48,6 +48,9 @@ __device__ __forceinline__ void fp8x2_to_f32(uint32_t packed, float& a, float& b
   b = v.y;
 }
 
+// ReLU on the bits: negative values (and -0.0) give +0.0.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Order-preserving map float -> uint32 (larger float -> larger key); -0.0 is
 // folded onto +0.0 so the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float x) {

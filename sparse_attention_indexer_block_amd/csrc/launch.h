@@ -192,8 +192,22 @@ int topk_long_chunk();
 int topk_long_max_chunks();
 size_t topk_long_rec_bytes();
 int topk_coarse_bins();
+// Rescoring of the kept items with every head, fused into the emission (rows
+// whose item index is the key index, i.e. row_idx null): S[row, p] for each
+// output position p < out_count[row] gets sum_h w[row,h] ReLU(q[row,h] . k_s)
+// (times the key's scale for fp8 keys) of the key s emitted at p.
+struct RerankArgs {
+  const uint16_t* q;     // [rows, H, 128] bf16
+  const float* w;        // [rows, H]
+  int H;                 // 1 <= H <= 64
+  const void* K;         // [L, 128] bf16 or e4m3fn
+  const float* kscale;   // [L] (fp8)
+  bool fp8;
+  float* S;              // [rows, S_ld]
+  long long S_ld;        // multiple of 4
+};
 hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLongWs& ws,
-                            int max_n);
+                            int max_n, const RerankArgs* rr = nullptr);
 // Rows whose key range is not known yet: per-chunk ranges into rmm_out
 // [topk_long_chunks(max_n), rows, 2] (and `zero` cleared).
 hipError_t launch_topk_range(const LaunchCtx& cx, const TopkArgs& a, uint32_t* rmm_out,

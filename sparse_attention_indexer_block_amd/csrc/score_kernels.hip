@@ -23,7 +23,6 @@ constexpr int kLdsStride = kHeadDim + 8;  // bf16 per key row in LDS (16 B pad)
 // ReLU of an MFMA result as one integer max on its bits: negative values (and
 // -0.0) have the sign bit set and become +0.0. fmaxf would add a quieting step
 // for signalling NaNs, which MFMA results on finite inputs never are.
-__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Row layout of the A operand. With AP <= 16 head slots and RPW a multiple of
 // G = AP / 4, G row tiles form a "quad" of four queries: row r of tile k in the

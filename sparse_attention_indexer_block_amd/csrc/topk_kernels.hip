@@ -738,10 +738,107 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* r
 // need_eq (items equal to tau that are kept, lowest positions first) from the
 // boundary list, counts the kept items of the chunks before its own, and
 // writes its chunk's kept items in position order.
-template <int NT>
-__global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
-                                                  const int32_t* bcnt, int nch, const uint32_t* bkeys,
-                                                  long long rld) {
+// Rescoring of a chunk's kept candidates with every head (MISA technical
+// summary, "Variante Jerarquica": the routed top-k' candidates are rescored by
+// all H indexer heads before the final top-k), for the rerank form of the
+// emission: candidate c of the chunk (key cl[c], output position pj + c) gets
+// S[row, pj + c] = sum_h w[row,h] ReLU(q[row,h] . k) * scale, the sum the
+// gather form of the scoring kernel forms, in the same order and with the same
+// operand layout: rows (heads) and columns (keys) of v_mfma_f32_16x16x32_bf16,
+// lane l covering head / key l mod 16 with dims [32 (l / 16), 32 (l / 16) + 32).
+// qsh / wsh: the query's 64 head rows (kRerankQStride 16-byte words apart;
+// rows past H zero) and weights (zero past H), staged in LDS.
+constexpr int kRerankQStride = kHeadDim / 8 + 1;  // one pad word per row: conflict-free row reads
+template <int NT, bool FP8>
+__device__ __forceinline__ void rerank_kept(const RerankArgs& rr, int row, const int32_t* cl, int pj, int kj,
+                                            const u32x4* qsh, const float* wsh) {
+  constexpr int NW = NT / kWave;
+  constexpr int NV = FP8 ? 2 : 4;  // 16-byte words of a lane's 32 dims of a key
+  constexpr int D = 2;             // key groups in flight per wave
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
+  const int kcol = lane & 15, slice = lane >> 4;
+  const int ng = (kj + 15) >> 4;  // groups of 16 candidates
+  if (w >= ng) return;  // uniform: no group for this wave
+  bf16x8 af[4][4];
+  float wv[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      af[r][ks] = __builtin_bit_cast(bf16x8, qsh[(16 * r + kcol) * kRerankQStride + 4 * slice + ks]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[r][i] = wsh[16 * r + 4 * slice + i];
+  }
+  float* out = rr.S + (size_t)row * rr.S_ld + pj;
+  for (int g0 = w; g0 < ng; g0 += NW * D) {
+    // every group's key rows are requested before any is used (a column past
+    // the list reads its last candidate and is not written)
+    u32x4 kv[D][NV];
+    float ksc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int key = cl[min(16 * (g0 + NW * d) + kcol, kj - 1)];
+      const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(rr.K) +
+                                                        (size_t)key * (FP8 ? kHeadDim : 2 * kHeadDim) +
+                                                        slice * NV * 16);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) kv[d][v] = src[v];
+      ksc[d] = FP8 ? rr.kscale[key] : 1.f;
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int gi = g0 + NW * d;
+      if (gi >= ng) break;  // uniform
+      bf16x8 bf[4];
+      if constexpr (FP8) {
+        // 32 E4M3 codes -> 32 bf16 (exact), in dimension order
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            u32x4 x;
+            x[0] = fp8x2_to_bf16x2<false>(kv[d][v][2 * e]);
+            x[1] = fp8x2_to_bf16x2<true>(kv[d][v][2 * e]);
+            x[2] = fp8x2_to_bf16x2<false>(kv[d][v][2 * e + 1]);
+            x[3] = fp8x2_to_bf16x2<true>(kv[d][v][2 * e + 1]);
+            bf[2 * v + e] = __builtin_bit_cast(bf16x8, x);
+          }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bf[v] = __builtin_bit_cast(bf16x8, kv[d][v]);
+      }
+      f32x4 acc[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r][ks], bf[ks], a4, 0, 0, 0);
+        acc[r] = a4;
+      }
+      // ReLU, times w, the head sum, times |scale| (a negative scale flips the
+      // key's sign inside the ReLU)
+      const float sc = ksc[d];
+      const float sgn = sc < 0.f ? -1.f : 1.f;
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wv[r][i] * relu(sgn * acc[r][i]);
+      part += __shfl_xor(part, 16, kWave);
+      part += __shfl_xor(part, 32, kWave);
+      const int c = 16 * gi + kcol;
+      if (slice == 0 && c < kj) out[c] = part * fabsf(sc);
+    }
+  }
+}
+
+// RR: the rerank form (rr: the query rows, weights and keys; FP8: fp8 keys),
+// which also rescores the chunk's kept candidates into rr.S at their output
+// positions; otherwise rr is unused.
+template <int NT, bool RR, bool FP8>
+__device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec, const int32_t* gcnt,
+                                          const int32_t* bcnt, int nch, const uint32_t* bkeys, long long rld,
+                                          const RerankArgs& rr) {
   constexpr int NW = NT / kWave;
   __shared__ TopkShared<NT> sm;
   __shared__ __attribute__((aligned(16))) uint32_t blist[kBoundaryCap];
@@ -784,6 +881,36 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
   }
   const int bc0 = bcnt[(size_t)row * nch + min(tid, nch - 1)];
   const int gc0 = gcnt[(size_t)row * nch + min(tid, nch - 1)];
+  // rerank form: the query's head rows and weights (16 KiB and 256 B), one
+  // 16-byte word per thread and round, requested after the reads above so that
+  // their first use does not wait for these; staged in LDS below
+  __shared__ u32x4 qsh[RR ? kMaxHeads * kRerankQStride : 1];
+  __shared__ float wsh[RR ? kMaxHeads : 1];
+  constexpr int kQRounds = kMaxHeads * (kHeadDim / 8) / NT;  // 16-byte words per thread
+  u32x4 qst[RR ? kQRounds : 1];
+  float wst = 0.f;
+  if constexpr (RR) {
+#pragma unroll
+    for (int u = 0; u < kQRounds; ++u) {
+      const int i = tid + NT * u, h = i / (kHeadDim / 8);
+      qst[u] = reinterpret_cast<const u32x4*>(rr.q + ((size_t)row * rr.H + min(h, rr.H - 1)) * kHeadDim)
+          [i % (kHeadDim / 8)];
+    }
+    wst = rr.w[(size_t)row * rr.H + min(tid & (kMaxHeads - 1), rr.H - 1)];
+  }
+  auto stage_q = [&]() {  // rows past H and their weights are zero
+    if constexpr (RR) {
+#pragma unroll
+      for (int u = 0; u < kQRounds; ++u) {
+        const int i = tid + NT * u, h = i / (kHeadDim / 8);
+        qsh[h * kRerankQStride + i % (kHeadDim / 8)] = h < rr.H ? qst[u] : u32x4{0u, 0u, 0u, 0u};
+      }
+      if (tid < kMaxHeads) wsh[tid] = tid < rr.H ? wst : 0.f;
+    }
+  };
+  // kept candidates of the chunk, in output order (rerank form: the boundary
+  // list's buffer, free once the threshold is known)
+  int32_t* cl = reinterpret_cast<int32_t*>(blist);
   if (take_all) {  // every item, scores as stored (-0 folded to +0)
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
@@ -793,13 +920,20 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
         if (s < s1) {
           oi[s] = ri ? ri[s] : s;
           if (os) os[s] = sv[g][e] == 0.f ? 0.f : sv[g][e];
+          if (RR) cl[s - s0] = ri ? ri[s] : s;
         }
       }
+    if constexpr (RR) {
+      stage_q();
+      __syncthreads();
+      rerank_kept<NT, FP8>(rr, row, cl, s0, s1 - s0, qsh, wsh);
+    }
     return;
   }
   uint32_t u[kGroups][4];
   bool in[kGroups][4];
   keys4<kGroups>(sv, ws0, s1, lane, kWave, u, in);
+  stage_q();  // read after the barriers below
   // ---- the region offsets of the concatenated boundary list
   const int rem = rem_raw;
   int gt_before = 0;
@@ -932,6 +1066,18 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
     gt_run += sm.wgt[i];
     eq_run += sm.weq[i];
   }
+  // the chunk's kept items take output positions [pj, pend)
+  const int pj = min(gt_all + min(eq_all, need_eq), a.k);
+  int pend = 0;
+  if constexpr (RR) {
+    int gt_end = gt_all, eq_end = eq_all;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      gt_end += sm.wgt[i];
+      eq_end += sm.weq[i];
+    }
+    pend = min(gt_end + min(eq_end, need_eq), a.k);
+  }
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
     const int inc = wave_inclusive_scan(cnt[g]);
@@ -952,12 +1098,31 @@ __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec
       if (p >= 0 && p < a.k) {
         oi[p] = ri ? ri[s] : s;
         if (os) os[p] = key_score(u[g][e]);
+        if (RR) cl[p - pj] = ri ? ri[s] : s;
       }
     }
     const int wt = __builtin_amdgcn_readlane(inc, kWave - 1);
     gt_run += wt & 0xffff;
     eq_run += wt >> 16;
   }
+  if constexpr (RR) {
+    __syncthreads();  // the kept list is complete
+    rerank_kept<NT, FP8>(rr, row, cl, pj, pend - pj, qsh, wsh);
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
+                                                  const int32_t* bcnt, int nch, const uint32_t* bkeys,
+                                                  long long rld) {
+  long_emit<NT, false, false>(a, rec, gcnt, bcnt, nch, bkeys, rld, RerankArgs{});
+}
+
+template <int NT, bool FP8>
+__global__ __launch_bounds__(NT) void k_long_emit_rerank(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
+                                                         const int32_t* bcnt, int nch, const uint32_t* bkeys,
+                                                         long long rld, RerankArgs rr) {
+  long_emit<NT, true, FP8>(a, rec, gcnt, bcnt, nch, bkeys, rld, rr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1343,7 +1508,8 @@ hipError_t launch_topk_rows(const LaunchCtx& cx, const TopkArgs& a, int max_n) {
 #undef MISA_ROWS
 }
 
-hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLongWs& ws, int max_n) {
+hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLongWs& ws, int max_n,
+                            const RerankArgs* rr) {
   if (a.rows == 0) return hipSuccess;
   const int nch = topk_long_chunks(max_n);
   if (nch > kMaxChunks) return hipErrorInvalidValue;
@@ -1356,6 +1522,15 @@ hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLo
   e = cx.launch("topk_count", k_long_count<kLongNT>, grid, dim3(kLongNT), 0, a, ws.rmm, ws.nmm,
                 (const uint32_t*)ws.ghist, rec, ws.gcnt, ws.bcnt, nch, ws.bkeys, rld);
   if (e != hipSuccess) return e;
+  if (rr) {
+    if (a.row_idx || rr->H < 1 || rr->H > kMaxHeads || rr->S_ld % 4 != 0) return hipErrorInvalidValue;
+    return rr->fp8 ? cx.launch("topk_emit_rerank", k_long_emit_rerank<kLongNT, true>, grid, dim3(kLongNT), 0, a,
+                               (const LongRec*)rec, (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch,
+                               (const uint32_t*)ws.bkeys, rld, *rr)
+                   : cx.launch("topk_emit_rerank", k_long_emit_rerank<kLongNT, false>, grid, dim3(kLongNT), 0, a,
+                               (const LongRec*)rec, (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch,
+                               (const uint32_t*)ws.bkeys, rld, *rr);
+  }
   return cx.launch("topk_emit", k_long_emit<kLongNT>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,
                    (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch, (const uint32_t*)ws.bkeys, rld);
 }
