@@ -563,9 +563,14 @@ def main():
     floors_us = {algo_bytes: fr["stamped_us"]}  # streaming floor (kernel-stamped) by byte count
     # per-step milliseconds of each kernel family (launch averages times launches per step)
     per_step = {k: (v[0] * v[1] / args.steps if v[0] else 0.0) for k, v in kms.items()}
+    # "topk_emit" also matches the rerank form of the emission ("topk_emit_rerank"), which
+    # rescores the candidates itself: then no gather kernel runs and its bytes are the selection's
     sel_ms = sum(per_step[k] for k in ("topk_rows", "topk_hist", "topk_count", "topk_emit"))
+    fused_rerank = not kms["score_gather"][0]
     sel_bytes = selection_bytes(wl, pairs)
     gat_bytes = gather_bytes(wl)
+    if fused_rerank:
+        sel_bytes += gat_bytes
     step_bytes = step_bytes_compulsory(wl)
 
     def line(bytes_, ms_, **kw):
@@ -611,9 +616,15 @@ def main():
         "rooflines": {
             "block_sums": line(block_sums_bytes(wl), per_step["block_sums"], kernel="block pooling, K once"),
             "score_keys": line(algo_bytes, per_step["score_keys"], kernel="routed scoring, K once"),
-            "selection": line(sel_bytes, sel_ms, kernel="top-k' of the score rows + top-k of the candidates",
-                              bytes_rule="4*sum(n_t) + 4*T*k' read-write of the k' stage; 8*T*k' + 8*T*k of the final"),
-            "rerank_gather": line(gat_bytes, per_step["score_gather"], kernel="all-head rescoring of the candidates"),
+            "selection": line(sel_bytes, sel_ms,
+                              kernel="top-k' of the score rows" +
+                                     (" with the candidates' all-head rescoring inside its emission pass"
+                                      if fused_rerank else "") + " + top-k of the candidates",
+                              bytes_rule="4*sum(n_t) + 4*T*k' read-write of the k' stage; 8*T*k' + 8*T*k of the final" +
+                                         ("; + the rescoring's gathered key rows and q rows" if fused_rerank else "")),
+            "rerank_gather": ({"fused": "inside the k' emission pass (topk_emit_rerank), counted in selection"}
+                              if fused_rerank else
+                              line(gat_bytes, per_step["score_gather"], kernel="all-head rescoring of the candidates")),
             "step": line(step_bytes, ms, kernel="whole step (graph replay)",
                          bytes_rule="K once + q + w + pos + outputs"),
         },
