@@ -151,6 +151,13 @@ def test_hier_selections_exact_random():
     _hier_exact(inp, 128, 8, 3000, 700)
 
 
+def test_hier_selections_exact_random_bf16():
+    # long rows with bf16 keys and 40 heads (rows short of k' are taken whole)
+    inp = synth.random_small(72, T=7, L=21000, H=40, k_dtype=synth.KDT_BF16, positions="random")
+    inp["pos"][0] = 0
+    _hier_exact(inp, 64, 5, 2500, 300)
+
+
 def _hisa_exact(inp, B, m, k, maxpool=False):
     q, w, K, ks, pos = to_gpu(inp)
     L = K.shape[0]

@@ -259,6 +259,8 @@ HIER_CASES = [
     (32, 9, 3000, 32, 8, 128, 1024, 256, O.KDT_FP8),
     (33, 5, 400, 64, 4, 64, 400, 30, O.KDT_BF16),      # k' >= n: dense
     (34, 8, 20000, 64, 8, 128, 4096, 512, O.KDT_FP8),  # long rows
+    (35, 6, 18000, 32, 8, 128, 3000, 400, O.KDT_BF16),  # long rows, bf16 keys, fewer heads than 64
+    (36, 5, 17000, 48, 6, 128, 20000, 600, O.KDT_FP8),  # long rows, k' >= n: every key a candidate
 ]
 
 
@@ -286,6 +288,15 @@ def test_misa_hier_topk(case):
     q, w, K, ks, pos = to_gpu(inp)
     idx, sc = S.hier_topk(q, w, K, pos, B, A, kprime, k, ks)
     check_hier(inp, B, A, kprime, k, _np(idx), _np(sc))
+
+
+def test_misa_hier_topk_long_rows_negative_scales():
+    # the candidates' rescoring inside the long-row emission with keys whose
+    # scale is negative (the sign flips inside the ReLU)
+    inp = _case(38, 5, 19000, 64, O.KDT_FP8, positions="decode", neg_scales=True)
+    q, w, K, ks, pos = to_gpu(inp)
+    idx, sc = S.hier_topk(q, w, K, pos, 128, 8, 2500, 300, ks)
+    check_hier(inp, 128, 8, 2500, 300, _np(idx), _np(sc))
 
 
 # ----------------------------------------------------------------- HISA
