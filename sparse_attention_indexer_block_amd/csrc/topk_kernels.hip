@@ -834,8 +834,11 @@ __device__ __forceinline__ void rerank_kept(const RerankArgs& rr, int row, const
 
 // RR: the rerank form (rr: the query rows, weights and keys; FP8: fp8 keys),
 // which also rescores the chunk's kept candidates into rr.S at their output
-// positions; otherwise rr is unused.
-template <int NT, bool RR, bool FP8>
+// positions; otherwise rr is unused. IDX: the row has explicit item indices
+// (row_idx), read beside the scores; without them the index is the position
+// (no read in the emission loop, whose stores would otherwise each wait for
+// every earlier memory operation behind that conditional read).
+template <int NT, bool RR, bool FP8, bool IDX>
 __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec, const int32_t* gcnt,
                                           const int32_t* bcnt, int nch, const uint32_t* bkeys, long long rld,
                                           const RerankArgs& rr) {
@@ -860,7 +863,7 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
   const int s0 = chunk * kChunk, s1 = min(n, s0 + kChunk);
   if (s0 >= s1) return;  // uniform
   const float* src = a.S + (size_t)row * a.S_ld;
-  const int32_t* ri = a.row_idx ? a.row_idx + (size_t)row * a.idx_ld : nullptr;
+  const int32_t* ri = IDX ? a.row_idx + (size_t)row * a.idx_ld : nullptr;
   const int ws0 = s0 + w * (kChunk / NW);
   // every read that does not depend on another is issued here, before any is
   // used: the chunk's scores, the row record, the first NT chunks' counts and
@@ -868,6 +871,17 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
   // the count pass did not run and these are ignored)
   f32x4 sv[kGroups];
   load_raw4<kGroups>(src, ws0, s1, lane, kWave, sv);
+  i32x4 ix[IDX ? kGroups : 1];  // explicit indices, same clamped 16-byte groups as the scores
+  if constexpr (IDX) {
+    const int last = s1 > ws0 ? (s1 - 1) & ~3 : 0;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+      ix[g] = *reinterpret_cast<const i32x4*>(ri + min(ws0 + 4 * (lane + kWave * g), last));
+  }
+  auto idx_of = [&](int g, int e, int s) {
+    if constexpr (IDX) return ix[g][e];
+    else return s;
+  };
   const int nc = (n + kChunk - 1) / kChunk;
   const int rem_raw = (int)rec[row].rem;
   const uint32_t* gk = bkeys + (size_t)row * rld;
@@ -918,9 +932,9 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
       for (int e = 0; e < 4; ++e) {
         const int s = ws0 + 4 * (lane + kWave * g) + e;
         if (s < s1) {
-          oi[s] = ri ? ri[s] : s;
+          oi[s] = idx_of(g, e, s);
           if (os) os[s] = sv[g][e] == 0.f ? 0.f : sv[g][e];
-          if (RR) cl[s - s0] = ri ? ri[s] : s;
+          if (RR) cl[s - s0] = idx_of(g, e, s);
         }
       }
     if constexpr (RR) {
@@ -1096,9 +1110,9 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
         ++eq_b;
       }
       if (p >= 0 && p < a.k) {
-        oi[p] = ri ? ri[s] : s;
+        oi[p] = idx_of(g, e, s);
         if (os) os[p] = key_score(u[g][e]);
-        if (RR) cl[p - pj] = ri ? ri[s] : s;
+        if (RR) cl[p - pj] = idx_of(g, e, s);
       }
     }
     const int wt = __builtin_amdgcn_readlane(inc, kWave - 1);
@@ -1111,18 +1125,18 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
   }
 }
 
-template <int NT>
+template <int NT, bool IDX>
 __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
                                                   const int32_t* bcnt, int nch, const uint32_t* bkeys,
                                                   long long rld) {
-  long_emit<NT, false, false>(a, rec, gcnt, bcnt, nch, bkeys, rld, RerankArgs{});
+  long_emit<NT, false, false, IDX>(a, rec, gcnt, bcnt, nch, bkeys, rld, RerankArgs{});
 }
 
 template <int NT, bool FP8>
 __global__ __launch_bounds__(NT) void k_long_emit_rerank(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
                                                          const int32_t* bcnt, int nch, const uint32_t* bkeys,
                                                          long long rld, RerankArgs rr) {
-  long_emit<NT, true, FP8>(a, rec, gcnt, bcnt, nch, bkeys, rld, rr);
+  long_emit<NT, true, FP8, false>(a, rec, gcnt, bcnt, nch, bkeys, rld, rr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1531,7 +1545,10 @@ hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLo
                                (const LongRec*)rec, (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch,
                                (const uint32_t*)ws.bkeys, rld, *rr);
   }
-  return cx.launch("topk_emit", k_long_emit<kLongNT>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,
+  if (a.row_idx)
+    return cx.launch("topk_emit", k_long_emit<kLongNT, true>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,
+                     (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch, (const uint32_t*)ws.bkeys, rld);
+  return cx.launch("topk_emit", k_long_emit<kLongNT, false>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,
                    (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch, (const uint32_t*)ws.bkeys, rld);
 }
 
