@@ -471,13 +471,15 @@ static misa_status run_hier(const LaunchCtx& cx, const misa_problem* p, const Pl
   ta.out_idx = cand;
   ta.out_ld = pl.cand_ld;
   ta.out_count = ncand;
-  // fine stage: all H heads rescore the candidates, then top-k. Long rows with
-  // bf16 queries rescore each chunk's kept candidates inside the emission
-  // pass; otherwise the gather form of the scoring kernel rescores the list.
+  // fine stage: all H heads rescore the candidates, then top-k. Long rows
+  // rescore each chunk's kept candidates inside the emission pass; otherwise
+  // the gather form of the scoring kernel rescores the list.
   const bool fp8k = p->k_dtype == MISA_K_FP8_E4M3FN;
-  if (p->L > topk_lds_cap() && p->q_dtype != MISA_Q_FP8_E4M3FN) {
+  if (p->L > topk_lds_cap()) {
     RerankArgs rr;
-    rr.q = static_cast<const uint16_t*>(p->q);
+    rr.q = p->q;
+    rr.q_fp8 = p->q_dtype == MISA_Q_FP8_E4M3FN;
+    rr.qscale = p->q_scale;
     rr.w = p->w;
     rr.H = p->H;
     rr.K = p->K;

@@ -197,7 +197,9 @@ int topk_coarse_bins();
 // output position p < out_count[row] gets sum_h w[row,h] ReLU(q[row,h] . k_s)
 // (times the key's scale for fp8 keys) of the key s emitted at p.
 struct RerankArgs {
-  const uint16_t* q;     // [rows, H, 128] bf16
+  const void* q;         // [rows, H, 128] bf16, or E4M3FN codes (q_fp8, fp8 keys only)
+  bool q_fp8;
+  const float* qscale;   // q_fp8: [rows, H] per-row scales
   const float* w;        // [rows, H]
   int H;                 // 1 <= H <= 64
   const void* K;         // [L, 128] bf16 or e4m3fn

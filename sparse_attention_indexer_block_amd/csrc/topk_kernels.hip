@@ -746,12 +746,18 @@ __global__ __launch_bounds__(NT) void k_long_count(TopkArgs a, const uint32_t* r
 // gather form of the scoring kernel forms, in the same order and with the same
 // operand layout: rows (heads) and columns (keys) of v_mfma_f32_16x16x32_bf16,
 // lane l covering head / key l mod 16 with dims [32 (l / 16), 32 (l / 16) + 32).
+// QF8 (fp8 queries, fp8 keys): the staged rows are E4M3 codes with the sign of
+// their scale folded in and the weights are w |scale|, and one
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) per row tile takes all
+// 128 dims of the codes, as in the gather kernel's fp8 form.
 // qsh / wsh: the query's 64 head rows (kRerankQStride 16-byte words apart;
 // rows past H zero) and weights (zero past H), staged in LDS.
 constexpr int kRerankQStride = kHeadDim / 8 + 1;  // one pad word per row: conflict-free row reads
-template <int NT, bool FP8>
+                                                  // (a bf16 row fills 16 words, an fp8 row 8)
+template <int NT, bool FP8, bool QF8>
 __device__ __forceinline__ void rerank_kept(const RerankArgs& rr, int row, const int32_t* cl, int pj, int kj,
                                             const u32x4* qsh, const float* wsh) {
+  static_assert(!QF8 || FP8, "fp8 queries are scored against fp8 keys");
   constexpr int NW = NT / kWave;
   constexpr int NV = FP8 ? 2 : 4;  // 16-byte words of a lane's 32 dims of a key
   constexpr int D = 2;             // key groups in flight per wave
@@ -759,13 +765,19 @@ __device__ __forceinline__ void rerank_kept(const RerankArgs& rr, int row, const
   const int kcol = lane & 15, slice = lane >> 4;
   const int ng = (kj + 15) >> 4;  // groups of 16 candidates
   if (w >= ng) return;  // uniform: no group for this wave
-  bf16x8 af[4][4];
+  bf16x8 af[QF8 ? 1 : 4][4];
+  i32x8 af8[QF8 ? 4 : 1];
   float wv[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    const u32x4* qrow = qsh + (16 * r + kcol) * kRerankQStride;
+    if constexpr (QF8) {
+      const u32x4 lo = qrow[2 * slice], hi = qrow[2 * slice + 1];
+      af8[r] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      af[r][ks] = __builtin_bit_cast(bf16x8, qsh[(16 * r + kcol) * kRerankQStride + 4 * slice + ks]);
+      for (int ks = 0; ks < 4; ++ks) af[r][ks] = __builtin_bit_cast(bf16x8, qrow[4 * slice + ks]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[r][i] = wsh[16 * r + 4 * slice + i];
   }
@@ -790,7 +802,9 @@ __device__ __forceinline__ void rerank_kept(const RerankArgs& rr, int row, const
       const int gi = g0 + NW * d;
       if (gi >= ng) break;  // uniform
       bf16x8 bf[4];
-      if constexpr (FP8) {
+      if constexpr (QF8) {
+        // the key's 32 codes are used as they are
+      } else if constexpr (FP8) {
         // 32 E4M3 codes -> 32 bf16 (exact), in dimension order
 #pragma unroll
         for (int v = 0; v < 2; ++v)
@@ -811,8 +825,14 @@ __device__ __forceinline__ void rerank_kept(const RerankArgs& rr, int row, const
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (QF8) {
+          const i32x8 b8 = i32x8{(int)kv[d][0][0], (int)kv[d][0][1], (int)kv[d][0][2], (int)kv[d][0][3],
+                                 (int)kv[d][1][0], (int)kv[d][1][1], (int)kv[d][1][2], (int)kv[d][1][3]};
+          a4 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af8[r], b8, a4, 0, 0, 0, 127, 0, 127);
+        } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r][ks], bf[ks], a4, 0, 0, 0);
+          for (int ks = 0; ks < 4; ++ks) a4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r][ks], bf[ks], a4, 0, 0, 0);
+        }
         acc[r] = a4;
       }
       // ReLU, times w, the head sum, times |scale| (a negative scale flips the
@@ -832,13 +852,13 @@ __device__ __forceinline__ void rerank_kept(const RerankArgs& rr, int row, const
   }
 }
 
-// RR: the rerank form (rr: the query rows, weights and keys; FP8: fp8 keys),
-// which also rescores the chunk's kept candidates into rr.S at their output
-// positions; otherwise rr is unused. IDX: the row has explicit item indices
+// RR: the rerank form (rr: the query rows, weights and keys; FP8: fp8 keys;
+// QF8: fp8 queries), which also rescores the chunk's kept candidates into rr.S
+// at their output positions; otherwise rr is unused. IDX: the row has explicit item indices
 // (row_idx), read beside the scores; without them the index is the position
 // (no read in the emission loop, whose stores would otherwise each wait for
 // every earlier memory operation behind that conditional read).
-template <int NT, bool RR, bool FP8, bool IDX>
+template <int NT, bool RR, bool FP8, bool QF8, bool IDX>
 __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec, const int32_t* gcnt,
                                           const int32_t* bcnt, int nch, const uint32_t* bkeys, long long rld,
                                           const RerankArgs& rr) {
@@ -895,31 +915,46 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
   }
   const int bc0 = bcnt[(size_t)row * nch + min(tid, nch - 1)];
   const int gc0 = gcnt[(size_t)row * nch + min(tid, nch - 1)];
-  // rerank form: the query's head rows and weights (16 KiB and 256 B), one
-  // 16-byte word per thread and round, requested after the reads above so that
-  // their first use does not wait for these; staged in LDS below
+  // rerank form: the query's head rows and weights (16 KiB of bf16 or 8 KiB of
+  // fp8 codes, and 256 B), one 16-byte word per thread and round, requested
+  // after the reads above so that their first use does not wait for these;
+  // staged in LDS below. fp8 rows: the scale's sign goes into the codes (bit 7
+  // of each), its magnitude into the weight.
   __shared__ u32x4 qsh[RR ? kMaxHeads * kRerankQStride : 1];
   __shared__ float wsh[RR ? kMaxHeads : 1];
-  constexpr int kQRounds = kMaxHeads * (kHeadDim / 8) / NT;  // 16-byte words per thread
+  constexpr int kRowWords = QF8 ? kHeadDim / 16 : kHeadDim / 8;  // 16-byte words per q row
+  constexpr int kQRounds = kMaxHeads * kRowWords / NT;             // words per thread
   u32x4 qst[RR ? kQRounds : 1];
-  float wst = 0.f;
+  float qss[QF8 ? kQRounds : 1];  // fp8 rows: the scale of each word's row
+  float wst = 0.f, wsc = 1.f;
   if constexpr (RR) {
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(rr.q);
 #pragma unroll
     for (int u = 0; u < kQRounds; ++u) {
-      const int i = tid + NT * u, h = i / (kHeadDim / 8);
-      qst[u] = reinterpret_cast<const u32x4*>(rr.q + ((size_t)row * rr.H + min(h, rr.H - 1)) * kHeadDim)
-          [i % (kHeadDim / 8)];
+      const int i = tid + NT * u, h = min(i / kRowWords, rr.H - 1);
+      qst[u] = reinterpret_cast<const u32x4*>(qb + ((size_t)row * rr.H + h) * kRowWords * 16)[i % kRowWords];
+      if constexpr (QF8) qss[u] = rr.qscale[(size_t)row * rr.H + h];
     }
-    wst = rr.w[(size_t)row * rr.H + min(tid & (kMaxHeads - 1), rr.H - 1)];
+    const int hw = min(tid & (kMaxHeads - 1), rr.H - 1);
+    wst = rr.w[(size_t)row * rr.H + hw];
+    if constexpr (QF8) wsc = rr.qscale[(size_t)row * rr.H + hw];
   }
   auto stage_q = [&]() {  // rows past H and their weights are zero
     if constexpr (RR) {
 #pragma unroll
       for (int u = 0; u < kQRounds; ++u) {
-        const int i = tid + NT * u, h = i / (kHeadDim / 8);
-        qsh[h * kRerankQStride + i % (kHeadDim / 8)] = h < rr.H ? qst[u] : u32x4{0u, 0u, 0u, 0u};
+        const int i = tid + NT * u, h = i / kRowWords;
+        u32x4 x = h < rr.H ? qst[u] : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (QF8) {
+          const uint32_t f = (h < rr.H && qss[u] < 0.f) ? 0x80808080u : 0u;  // the row's scale sign
+          x[0] ^= f;
+          x[1] ^= f;
+          x[2] ^= f;
+          x[3] ^= f;
+        }
+        qsh[h * kRerankQStride + i % kRowWords] = x;
       }
-      if (tid < kMaxHeads) wsh[tid] = tid < rr.H ? wst : 0.f;
+      if (tid < kMaxHeads) wsh[tid] = tid < rr.H ? (QF8 ? wst * fabsf(wsc) : wst) : 0.f;
     }
   };
   // kept candidates of the chunk, in output order (rerank form: the boundary
@@ -940,7 +975,7 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
     if constexpr (RR) {
       stage_q();
       __syncthreads();
-      rerank_kept<NT, FP8>(rr, row, cl, s0, s1 - s0, qsh, wsh);
+      rerank_kept<NT, FP8, QF8>(rr, row, cl, s0, s1 - s0, qsh, wsh);
     }
     return;
   }
@@ -1121,7 +1156,7 @@ __device__ __forceinline__ void long_emit(const TopkArgs& a, const LongRec* rec,
   }
   if constexpr (RR) {
     __syncthreads();  // the kept list is complete
-    rerank_kept<NT, FP8>(rr, row, cl, pj, pend - pj, qsh, wsh);
+    rerank_kept<NT, FP8, QF8>(rr, row, cl, pj, pend - pj, qsh, wsh);
   }
 }
 
@@ -1129,14 +1164,14 @@ template <int NT, bool IDX>
 __global__ __launch_bounds__(NT) void k_long_emit(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
                                                   const int32_t* bcnt, int nch, const uint32_t* bkeys,
                                                   long long rld) {
-  long_emit<NT, false, false, IDX>(a, rec, gcnt, bcnt, nch, bkeys, rld, RerankArgs{});
+  long_emit<NT, false, false, false, IDX>(a, rec, gcnt, bcnt, nch, bkeys, rld, RerankArgs{});
 }
 
-template <int NT, bool FP8>
+template <int NT, bool FP8, bool QF8>
 __global__ __launch_bounds__(NT) void k_long_emit_rerank(TopkArgs a, const LongRec* rec, const int32_t* gcnt,
                                                          const int32_t* bcnt, int nch, const uint32_t* bkeys,
                                                          long long rld, RerankArgs rr) {
-  long_emit<NT, true, FP8, false>(a, rec, gcnt, bcnt, nch, bkeys, rld, rr);
+  long_emit<NT, true, FP8, QF8, false>(a, rec, gcnt, bcnt, nch, bkeys, rld, rr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1538,12 +1573,14 @@ hipError_t launch_topk_long(const LaunchCtx& cx, const TopkArgs& a, const TopkLo
   if (e != hipSuccess) return e;
   if (rr) {
     if (a.row_idx || rr->H < 1 || rr->H > kMaxHeads || rr->S_ld % 4 != 0) return hipErrorInvalidValue;
-    return rr->fp8 ? cx.launch("topk_emit_rerank", k_long_emit_rerank<kLongNT, true>, grid, dim3(kLongNT), 0, a,
-                               (const LongRec*)rec, (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch,
-                               (const uint32_t*)ws.bkeys, rld, *rr)
-                   : cx.launch("topk_emit_rerank", k_long_emit_rerank<kLongNT, false>, grid, dim3(kLongNT), 0, a,
-                               (const LongRec*)rec, (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch,
-                               (const uint32_t*)ws.bkeys, rld, *rr);
+    if (rr->q_fp8 && (!rr->fp8 || !rr->qscale)) return hipErrorInvalidValue;  // fp8 x fp8, scales needed
+#define MISA_RERANK_LAUNCH(F8, QF)                                                                          \
+  cx.launch("topk_emit_rerank", k_long_emit_rerank<kLongNT, F8, QF>, grid, dim3(kLongNT), 0, a,              \
+            (const LongRec*)rec, (const int32_t*)ws.gcnt, (const int32_t*)ws.bcnt, nch, (const uint32_t*)ws.bkeys, \
+            rld, *rr)
+    if (rr->q_fp8) return MISA_RERANK_LAUNCH(true, true);
+    return rr->fp8 ? MISA_RERANK_LAUNCH(true, false) : MISA_RERANK_LAUNCH(false, false);
+#undef MISA_RERANK_LAUNCH
   }
   if (a.row_idx)
     return cx.launch("topk_emit", k_long_emit<kLongNT, true>, grid, dim3(kLongNT), 0, a, (const LongRec*)rec,

@@ -88,7 +88,8 @@ def test_misa_fp8q_explicit_heads():
     _check_misa(inp, 128, A, 120, _np(idx), _np(sc), hs, label="fp8q explicit heads")
 
 
-HIER_CASES = [(21, 6, 3000, 64, 8, 128, 600, 100), (22, 8, 20000, 64, 8, 128, 4096, 512)]
+HIER_CASES = [(21, 6, 3000, 64, 8, 128, 600, 100), (22, 8, 20000, 64, 8, 128, 4096, 512),
+              (23, 5, 17500, 40, 6, 128, 20000, 500)]  # long rows, 40 heads, k' >= n
 
 
 @pytest.mark.parametrize("case", HIER_CASES, ids=lambda c: f"T{c[1]}L{c[2]}kp{c[6]}k{c[7]}")
