@@ -131,19 +131,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   int nfull[QG];  // complete blocks before each query's last block
   int nvis[QG];   // visible keys of each query
   float wq[QG];   // (single-pass form) head weight of this lane's head
+  float wsel[QG];  // (single-pass form) weight of head tid (tid < 64): the packed weight if chosen
   bf16x8 qa[QG][4];
+  // every input read is issued from an always-valid (clamped) address and
+  // masked once it has arrived: a read under a condition is waited for inside
+  // it, one memory round trip per query
+  int pos_raw[QG];
+  float wq_raw[QG];
+  u32x4 q_raw[QG][4];
+#pragma unroll
+  for (int i = 0; i < QG; ++i) {
+    const int tc = min(tq0 + i, T - 1), hc = min(h_a, H - 1);
+    pos_raw[i] = pos[tc];
+    wq_raw[i] = FUSED ? st.w[(size_t)tc * H + hc] : 0.f;
+    // the packed weight of head tid if it is chosen (read here rather than
+    // beside the final stores, which would then each wait for it)
+    wsel[i] = FUSED ? st.w[(size_t)tc * H + min(tid & (kWave - 1), H - 1)] : 0.f;
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)tc * H + hc) * kHeadDim + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) q_raw[i][s] = src[s];
+  }
 #pragma unroll
   for (int i = 0; i < QG; ++i) {
     const int t = tq0 + i;
-    const int n = t < T ? visible_len(pos[t], L) : 0;
+    const int n = t < T ? visible_len(pos_raw[i], L) : 0;
     const int Mt = (int)(((long long)n + B - 1) / B);
     nfull[i] = Mt > 0 ? Mt - 1 : 0;
     nvis[i] = n;
     const bool ok = t < T && h_a < H;
-    wq[i] = FUSED && ok ? st.w[(size_t)t * H + h_a] : 0.f;
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((size_t)(ok ? t : 0) * H + (ok ? h_a : 0)) * kHeadDim + 32 * g);
+    wq[i] = ok ? wq_raw[i] : 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) qa[i][s] = __builtin_bit_cast(bf16x8, ok ? src[s] : u32x4{0u, 0u, 0u, 0u});
+    for (int s = 0; s < 4; ++s) qa[i][s] = __builtin_bit_cast(bf16x8, ok ? q_raw[i][s] : u32x4{0u, 0u, 0u, 0u});
   }
   // blocks any query of the group can use: only those are staged and scored
   int mneed = 0;
@@ -161,27 +179,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int bstart = tr * NB;
     constexpr int NC = NB * 16 / 256;  // 16-byte chunks (8 dims) per thread
     u32x4 hv[NC], lv[NC];
+    // every row is read from a valid block (clamped to the last one; M >= 1)
+    // before any is used, and rows past bend are stored as zeros below (a read
+    // under a condition would be waited for inside it, one round trip per row)
     if (kb16) {
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
         const int c = tid + 256 * u, r = c >> 4, v = c & 15;
-        const int blk = bstart + r;
-        const bool need = blk < bend;  // rows past it are stored as zeros below
-        hv[u] = need ? reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim)[v] : u32x4{0u, 0u, 0u, 0u};
-        lv[u] = need ? reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + kHeadDim)[v]
-                     : u32x4{0u, 0u, 0u, 0u};
+        const int blk = min(bstart + r, M - 1);
+        hv[u] = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim)[v];
+        lv[u] = reinterpret_cast<const u32x4*>(kb16 + (size_t)blk * 2 * kHeadDim + kHeadDim)[v];
       }
     } else {
+      f32x4 xr[NC][2];
 #pragma unroll
       for (int u = 0; u < NC; ++u) {
         const int c = tid + 256 * u, r = c >> 4, v = c & 15;
-        const int blk = bstart + r;
-        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = x0;
-        if (blk < bend) {
-          const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)blk * kHeadDim + 8 * v);
-          x0 = src[0];
-          x1 = src[1];
-        }
+        const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (size_t)min(bstart + r, M - 1) * kHeadDim + 8 * v);
+        xr[u][0] = src[0];
+        xr[u][1] = src[1];
+      }
+#pragma unroll
+      for (int u = 0; u < NC; ++u) {
+        const f32x4 x0 = xr[u][0], x1 = xr[u][1];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           uint32_t ha, la, hb, lb;
@@ -201,12 +221,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
   }
   // (single-pass form) each query's last-block sum, rounded to float, for the
-  // certified interval of its tail term
+  // certified interval of its tail term; and the weights of heads 0..63 (the
+  // packed weights of the chosen heads, read from LDS at the end)
   __shared__ float tsh[FUSED ? QG : 1][kHeadDim];
+  __shared__ float wsh[FUSED ? QG : 1][kWave];
   if constexpr (FUSED) {
     for (int x = tid; x < QG * kHeadDim; x += 256) {
       const int i = x / kHeadDim, d = x % kHeadDim;
       tsh[i][d] = (float)st.tsum[(size_t)min(tq0 + i, T - 1) * kHeadDim + d];
+    }
+    if (tid < kWave) {
+#pragma unroll
+      for (int i = 0; i < QG; ++i) wsh[i][tid] = wsel[i];
     }
   }
   __syncthreads();
@@ -479,7 +505,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         sh.slot_of[i][h] = slot;
         if (sel) {
           if (st.heads) st.heads[(size_t)t * st.A + slot] = h;
-          if (st.wr) st.wr[(size_t)t * st.A + slot] = st.w[(size_t)t * H + h];
+          if (st.wr) st.wr[(size_t)t * st.A + slot] = wsh[i][h];
         }
       }
     }
