@@ -128,16 +128,20 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs p) {
   u32x4 stage[R][CHUNKS];
   float stage_sc[R];
 
+  // Key tiles through a buffer resource over the key rows (raw buffer, the
+  // third descriptor word of the gfx9 family): a tile's rows are contiguous, so
+  // chunk c of tile t lies at t KT (row bytes) (uniform, the scalar offset) plus
+  // 16 c (fixed per thread), and no per-chunk address arithmetic is needed; the
+  // hardware bounds check returns zeros for rows past the keys (never stored).
+  constexpr int kRowBytes = CH_PER_ROW * 16;
+  const long long kbytes = (long long)p.L * kRowBytes;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.K), (short)0, (int)(uint32_t)(kbytes < 0xffffffffll ? kbytes : 0xffffffffll), 0x00020000);
   auto load_tile = [&](int tile, int rr) {
+    const int toff = (int)((uint32_t)tile * (uint32_t)(KT * kRowBytes));
 #pragma unroll
-    for (int u = 0; u < CHUNKS; ++u) {
-      const int c = tid + 256 * u;
-      const int kr = c / CH_PER_ROW, part = c % CH_PER_ROW;
-      const int s = min(tile * KT + kr, p.L - 1);  // past the end: any valid key (never stored)
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(p.K) + (size_t)s * (FP8 ? kHeadDim : 2 * kHeadDim) +
-                            16 * part;
-      stage[rr][u] = *reinterpret_cast<const u32x4*>(base);
-    }
+    for (int u = 0; u < CHUNKS; ++u)
+      stage[rr][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, 16 * (tid + 256 * u), toff, 0));
     if (FP8 && tid < KT) stage_sc[rr] = p.kscale[min(tile * KT + tid, p.L - 1)];
   };
 
