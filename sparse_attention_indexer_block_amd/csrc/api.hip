@@ -275,8 +275,8 @@ static misa_status run_route(const LaunchCtx& cx, const misa_problem* p, const P
     return fail(MISA_ERR_UNSUPPORTED, "fp8 queries: T = %d queries over %d blocks need the many-query router",
                 p->T, ceil_div(p->L, p->B));
   if (part && max_pool) return fail(MISA_ERR_HIP, "internal: max pooling ranks no heads");
-  // query tails: pooled by the block-sum pass whenever it runs (the ranking
-  // kernel pools them itself only with cached means, where no such pass runs)
+  // query tails: pooled by the block-sum pass whenever it runs (with cached
+  // means, where no such pass runs, the router launch pools them itself)
   const bool tails = !part || keep_sums || p->kbar == nullptr;
   // with cached block means only the query tails are pooled here (nothing is
   // launched when no tails are needed either)
