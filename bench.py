@@ -405,12 +405,13 @@ def stream_floor(byte_counts, grid=1024, min_rotation=600 << 20):
     return res
 
 
-def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands, workload="c4_hier_decode_128k"):
     """Summarise four rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of the
-    headline benchmark; then of the copy calibration) into
-    profiles/score_keys_c4_pmc.json and .md: the routed scoring kernel's
-    counters per launch (median over launches), each scaled by what the same
-    counter reads for a plain device copy of known size."""
+    headline benchmark or of one workload's MISA line; then of the copy
+    calibration) into profiles/score_keys_<c4|c2|...>_pmc.json and .md: the
+    routed scoring kernel's counters per launch (median over launches), each
+    scaled by what the same counter reads for a plain device copy of known
+    size."""
     import csv
     import glob
     import hashlib
@@ -437,23 +438,26 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
     fs, ws = copy_bytes / 1024 / cfk, copy_bytes / 1024 / cwk
     fk, wk = float(np.median(f)), float(np.median(w))
     src = os.path.join(ROOT, "sparse_attention_indexer_block_amd", "csrc", "score_kernels.hip")
+    import synth
+    wl = synth.CONFIGS[workload]
+    tag = workload.split("_")[0]
     rec = {"kernel": "k_score_direct (routed scoring, keys in position order)",
-           "workload": "c4_hier_decode_128k (T=8, L=131072, fp8 keys, A=8)",
+           "workload": f"{workload} (T={wl.T}, L={wl.L}, {'fp8' if wl.k_dtype == 1 else 'bf16'} keys, A={wl.A})",
            "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
            "fetch_kib_per_launch_median": fk, "write_kib_per_launch_median": wk,
            "launches_counted": [len(f), len(w)], "fetch_scale": fs, "write_scale": ws,
            "calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": cfk, "copy_write_kib": cwk},
            "hbm_bytes_per_launch": (fk * fs + wk * ws) * 1024, "commands": commands}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "score_keys_c4_pmc.json"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"score_keys_{tag}_pmc.json"), "w") as fh:
         json.dump(rec, fh, indent=1)
-    import synth
-    algo = score_kernel_bytes(synth.CONFIGS["c4_hier_decode_128k"], 8)
-    md = ["# HBM traffic of the routed scoring kernel at c4_hier_decode_128k", "",
+    algo = score_kernel_bytes(wl, wl.A)
+    md = [f"# HBM traffic of the routed scoring kernel at {workload}", "",
           "Kernel: `k_score_direct` (key ranges, one launch per call).", "",
           "Commands (repository root, each pass a run of its own), then the summary:", "", "```"]
-    md += commands + ["python3 bench.py --pmc-summary gpurun_out/pmc_fetch gpurun_out/pmc_write "
-                      "gpurun_out/pmc_copy_fetch gpurun_out/pmc_copy_write", "```", "",
+    extra = "" if workload == "c4_hier_decode_128k" else f" --pmc-workload {workload}"
+    md += commands + [f"python3 bench.py --pmc-summary {fetch_dir} {write_dir} "
+                      f"{copy_fetch_dir} {copy_write_dir}{extra}", "```", "",
                       f"- FETCH_SIZE per launch (median of {len(f)}): {fk:.1f} KiB",
                       f"- WRITE_SIZE per launch (median of {len(w)}): {wk:.1f} KiB",
                       f"- copy calibration, 256 MiB device copy: FETCH_SIZE {cfk:.0f} KiB (scale {fs:.3f}), "
@@ -461,7 +465,7 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
                       f"- HBM bytes per launch = FETCH*scale + WRITE*scale = {rec['hbm_bytes_per_launch'] / 1e6:.2f} MB",
                       f"- algorithmic bytes per launch (keys + scales + routed q rows + w + pos): {algo / 1e6:.2f} MB; "
                       "the score rows written are intermediate", ""]
-    with open(os.path.join(ROOT, "profiles", "score_keys_c4_pmc.md"), "w") as fh:
+    with open(os.path.join(ROOT, "profiles", f"score_keys_{tag}_pmc.md"), "w") as fh:
         fh.write("\n".join(md))
     print(json.dumps(rec))
 
@@ -497,17 +501,22 @@ def main():
                          "for profiling")
     ap.add_argument("--pmc-summary", nargs=4, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
-                    help="summarise four rocprofv3 --pmc runs into profiles/score_keys_c4_pmc.* (no GPU)")
+                    help="summarise four rocprofv3 --pmc runs into profiles/score_keys_<tag>_pmc.* (no GPU)")
+    ap.add_argument("--pmc-workload", default="c4_hier_decode_128k", metavar="WORKLOAD",
+                    help="workload of the --pmc-summary runs: the headline (default) or the MISA line "
+                         "of another decode workload, profiled with --only misa:WORKLOAD")
     args = ap.parse_args()
     if args.pmc_summary:
-        B = "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra"
+        B = ("python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-extra"
+             if args.pmc_workload == "c4_hier_decode_128k"
+             else f"python3 bench.py --only misa:{args.pmc_workload} --steps 5 --warmup 2")
         C = "python3 bench.py --copy-calibration 256"
         d = args.pmc_summary
         cmds = [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[0]} -o run -- {B}",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[1]} -o run -- {B}",
                 f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d[2]} -o run -- {C}",
                 f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d[3]} -o run -- {C}"]
-        pmc_summary(*d, cmds)
+        pmc_summary(*d, cmds, workload=args.pmc_workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         _fail_multi_gpu(max(args.gpus, int(os.environ.get("WORLD_SIZE", "1"))))

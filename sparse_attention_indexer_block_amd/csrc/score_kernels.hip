@@ -350,8 +350,28 @@ __global__ __launch_bounds__(256) void k_score_direct(ScoreArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave / WC, wc = wave % WC;  // row group and key group of this wave
-  const int g = GATHER ? (int)blockIdx.y : (p.reverse ? p.ngroups - 1 - (int)blockIdx.x : (int)blockIdx.x);
-  const int split = GATHER ? (int)blockIdx.x : (int)blockIdx.y;
+  // Key ranges: a 1-D grid of ngroups x nsplit workgroups. Workgroup i runs on
+  // XCD i mod 8, each XCD with its own L2: when nsplit is a multiple of 8, the
+  // query groups of one key split get consecutive slots of one XCD, so that
+  // the split's keys come from HBM once and the other groups read them from
+  // that L2 (with the groups of a split on different XCDs, the 256-row
+  // batch of 32 queries over 32K keys fetched 4x its keys).
+  int g, split;
+  if constexpr (GATHER) {
+    g = (int)blockIdx.y;
+    split = (int)blockIdx.x;
+  } else {
+    const int lin = (int)blockIdx.x, G = p.ngroups;
+    if (G > 1 && p.nsplit % 8 == 0) {
+      const int slot = lin >> 3;
+      split = (lin & 7) + 8 * (slot / G);
+      g = slot % G;
+    } else {
+      split = lin / G;
+      g = lin % G;
+    }
+    if (p.reverse) g = G - 1 - g;
+  }
   // The query lengths' inputs are the first reads (from always-valid
   // addresses): the later wait for them then waits for nothing else.
   const int tqc = min(g * QW + (tid < QW ? tid : 0), p.T - 1);
@@ -798,7 +818,7 @@ static hipError_t run_direct(const LaunchCtx& cx, ScoreArgs a, bool fp8, const c
   a.ngroups = groups;
   a.nsplit = splits;
   if (nsplit_out) *nsplit_out = splits;
-  const dim3 grid = GATHER ? dim3(splits, groups) : dim3(groups, splits);
+  const dim3 grid = GATHER ? dim3(splits, groups) : dim3(groups * splits);
   if (a.q_fp8) {
     if (!fp8) return hipErrorInvalidValue;  // fp8 queries are scored against fp8 keys
     return cx.launch(name, k_score_direct<AP, RPW, WR, true, GATHER, true>, grid, dim3(256), 0, a);
