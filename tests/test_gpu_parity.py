@@ -205,6 +205,11 @@ MISA_CASES = [
     (23, 40, 17000, 32, 8, 128, 300, O.KDT_FP8, "random"),
     # many rows longer than 8192 keys: the row selection streams through the rows
     (24, 1100, 9000, 16, 4, 128, 300, O.KDT_BF16, "random"),
+    # decode batches of several 64-row query groups: key splits a multiple of 8
+    # (the groups of a split placed on one XCD) and not (plain order)
+    (25, 24, 20000, 64, 8, 128, 500, O.KDT_FP8, "decode"),
+    (26, 32, 16384, 64, 8, 128, 700, O.KDT_BF16, "decode"),
+    (27, 16, 12000, 32, 8, 128, 400, O.KDT_FP8, "random"),
 ]
 
 
