@@ -266,6 +266,9 @@ HIER_CASES = [
     (34, 8, 20000, 64, 8, 128, 4096, 512, O.KDT_FP8),  # long rows
     (35, 6, 18000, 32, 8, 128, 3000, 400, O.KDT_BF16),  # long rows, bf16 keys, fewer heads than 64
     (36, 5, 17000, 48, 6, 128, 20000, 600, O.KDT_FP8),  # long rows, k' >= n: every key a candidate
+    # long rows for batches of three query groups (key splits not / a multiple of 8)
+    (37, 20, 24000, 64, 8, 128, 3000, 700, O.KDT_FP8),
+    (39, 24, 20480, 64, 8, 128, 2048, 256, O.KDT_BF16),
 ]
 
 
@@ -313,6 +316,7 @@ HISA_CASES = [
     (43, 5, 600, 64, 64, 20, 40, O.KDT_BF16),     # m*B >= n: dense
     (44, 6, 300, 16, 1, 50, 30, O.KDT_BF16),      # token blocks
     (45, 4, 40000, 32, 128, 64, 2048, O.KDT_FP8),  # long rows
+    (46, 20, 30000, 64, 128, 32, 1024, O.KDT_FP8),  # long rows, many queries
 ]
 
 
